@@ -1,0 +1,182 @@
+"""Python access to the double-precision CPU oracle (``spectre_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg use this to compute expected values.  The GPU library and
+its binding never import it.
+
+Every function takes host numpy arrays: q, k, v, x as [B, L, H, D] float32
+(dtype 0) or uint16 bfloat16 bit patterns (dtype 1); gate as [H, L//2 + 1]
+float32; gamma, beta as [H*D] float32.  Results are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spectre_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, EINVAL, ENOMEM, EIMAG = 0, -1, -3, -5
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 (IEEE math, no fast-math) of an oracle source file into a shared library."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into liboracle.so next to its source."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _bind(lib):
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_fft.argtypes = [i64, vp, vp, vp, vp, ci]
+    lib.oracle_spectre_y.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp, ci]
+    lib.oracle_layernorm_residual.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp]
+    lib.oracle_spectre_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ci, vp, vp, ci]
+    lib.oracle_spectre_mix_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                              i64, i64, ci, vp, i64, vp, vp, ci]
+    lib.oracle_threads.argtypes = [ci]
+    for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
+              lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads):
+        f.restype = ci
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+class use_library:
+    """Context manager: route this module's calls to another build of the
+    oracle source (the mutation tests plant mistakes in a copy of it)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _bind(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(status: int):
+    if status != OK:
+        raise OracleError("oracle returned status %d" % status)
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _storage(a: np.ndarray, dtype: int) -> np.ndarray:
+    return _c(a, np.float32 if dtype == 0 else np.uint16)
+
+
+def threads(nthreads: int = 0) -> int:
+    """Threads a call with ``nthreads`` uses (0 = every online CPU)."""
+    return _load().oracle_threads(nthreads)
+
+
+def fft(x: np.ndarray, sign: int = -1) -> np.ndarray:
+    """Unnormalised complex DFT of a 1-D array: sum_j x[j] exp(sign 2 pi i f j / n)."""
+    x = np.asarray(x)
+    re = _c(x.real, np.float64)
+    im = _c(x.imag if np.iscomplexobj(x) else np.zeros_like(re), np.float64)
+    n = re.size
+    ore = np.empty(n, np.float64)
+    oim = np.empty(n, np.float64)
+    _check(_load().oracle_fft(n, re.ctypes.data, im.ctypes.data, ore.ctypes.data,
+                              oim.ctypes.data, sign))
+    return ore + 1j * oim
+
+
+def spectre_y(q, k, v, gate, keep_bins: int, dtype: int = 0, nthreads: int = 0) -> np.ndarray:
+    """y = irfft(G Q conj(K) V / L) per column, [B, L, H, D] float64."""
+    B, L, H, D = q.shape
+    q, k, v = (_storage(t, dtype) for t in (q, k, v))
+    gate = _c(gate, np.float32)
+    assert gate.shape == (H, L // 2 + 1)
+    y = np.empty((B, L, H, D), np.float64)
+    _check(_load().oracle_spectre_y(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                    gate.ctypes.data, B, H, L, D, keep_bins, dtype,
+                                    y.ctypes.data, nthreads))
+    return y
+
+
+def layernorm_residual(y, x, gamma, beta, dtype: int = 0) -> np.ndarray:
+    """LayerNorm over the last two axes' H*D channels of (x + y), eps 1e-5."""
+    shape = y.shape
+    C = shape[-1] * shape[-2]
+    ntok = int(np.prod(shape[:-2]))
+    y = _c(y, np.float64)
+    x = _storage(x, dtype)
+    gamma, beta = _c(gamma, np.float32), _c(beta, np.float32)
+    out = np.empty(shape, np.float64)
+    _check(_load().oracle_layernorm_residual(y.ctypes.data, x.ctypes.data, gamma.ctypes.data,
+                                             beta.ctypes.data, ntok, C, dtype, out.ctypes.data))
+    return out
+
+
+def spectre_mix(q, k, v, x, gate, gamma, beta, keep_bins: int, dtype: int = 0,
+                nthreads: int = 0, want_y: bool = False):
+    """The whole mix; returns out [B, L, H, D] float64 (and y if want_y)."""
+    B, L, H, D = q.shape
+    q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
+    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
+    assert gate.shape == (H, L // 2 + 1) and gamma.size == H * D and beta.size == H * D
+    out = np.empty((B, L, H, D), np.float64)
+    y = np.empty((B, L, H, D), np.float64) if want_y else None
+    _check(_load().oracle_spectre_mix(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                      x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
+                                      beta.ctypes.data, B, H, L, D, keep_bins, dtype,
+                                      out.ctypes.data, y.ctypes.data if want_y else None,
+                                      nthreads))
+    return (out, y) if want_y else out
+
+
+def spectre_mix_tokens(q, k, v, x, gate, gamma, beta, keep_bins: int, tokens,
+                       dtype: int = 0, nthreads: int = 0):
+    """The mix at sampled flat token ids b*L + t; returns (out, y), each [ntok, H, D]."""
+    B, L, H, D = q.shape
+    q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
+    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
+    tokens = _c(tokens, np.int64)
+    n = tokens.size
+    out = np.empty((n, H, D), np.float64)
+    y = np.empty((n, H, D), np.float64)
+    _check(_load().oracle_spectre_mix_tokens(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                             x.ctypes.data, gate.ctypes.data,
+                                             gamma.ctypes.data, beta.ctypes.data, B, H, L, D,
+                                             keep_bins, dtype, tokens.ctypes.data, n,
+                                             out.ctypes.data, y.ctypes.data, nthreads))
+    return out, y

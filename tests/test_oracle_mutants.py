@@ -1,0 +1,123 @@
+"""Planted mistakes: each mutant is a copy of the oracle source with one
+plausible error (a dropped conjugate, a wrong sign, index, scale, norm or
+truncation bound), built on the CPU.  The pins must reject every mutant, and
+accept the unmodified source, so they are shown to be able to catch such
+mistakes in the oracle itself."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from test_oracle_pins import closed_form_y, naive_dft
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "spectre_oracle.c")
+
+MUTANTS = {
+    "conj_dropped": ("cmul(cmul(bufq[f], cconj(bufk[f])), bufv[f])",
+                     "cmul(cmul(bufq[f], bufk[f]), bufv[f])"),
+    "conj_on_q": ("cmul(cmul(bufq[f], cconj(bufk[f])), bufv[f])",
+                  "cmul(cmul(cconj(bufq[f]), bufk[f]), bufv[f])"),
+    "gate_scale_dropped": ("double g = (double)J->gate[h * nbins + f] * invL;",
+                           "double g = (double)J->gate[h * nbins + f];"),
+    "inverse_scale_dropped": ("double re = bufq[t].re * invL, im = bufq[t].im * invL;",
+                              "double re = bufq[t].re, im = bufq[t].im * invL;"),
+    "truncation_inclusive": ("if (f < J->keep) {", "if (f <= J->keep) {"),
+    "head_index": ("const int64_t h = c / J->D;", "const int64_t h = c % J->H;"),
+    "hermitian_no_conj": ("tmp[f] = cconj(tmp[L - f]);", "tmp[f] = tmp[L - f];"),
+    "radix4_rotation": ("cpx jb1 = sign > 0 ? (cpx){-b1.im, b1.re} : (cpx){b1.im, -b1.re};",
+                        "cpx jb1 = sign > 0 ? (cpx){b1.im, -b1.re} : (cpx){-b1.im, b1.re};"),
+    "radix3_sign": ("cpx rot = {-(double)sign * s3 * dif.im, (double)sign * s3 * dif.re};",
+                    "cpx rot = {(double)sign * s3 * dif.im, -(double)sign * s3 * dif.re};"),
+    "twiddle_sign": ("t->w[j].im = -sin(a);", "t->w[j].im = sin(a);"),
+    "prime_dft_index": ("acc = cadd(acc, cmul(y[r], twiddle(t, p, r * s, sign)));",
+                        "acc = cadd(acc, cmul(y[r], twiddle(t, p, r + s, sign)));"),
+    "variance_unbiased": ("var /= (double)C;", "var /= (double)(C - 1);"),
+    "eps_outside_sqrt": ("double rstd = 1.0 / sqrt(var + eps);",
+                         "double rstd = 1.0 / (sqrt(var) + eps);"),
+    "gamma_beta_swapped": ("o[c] = (o[c] - mean) * rstd * (double)gamma[c] + (double)beta[c];",
+                           "o[c] = (o[c] - mean) * rstd * (double)beta[c] + (double)gamma[c];"),
+    "residual_dropped": ("o[c] = load_elem(x, dtype, xr * C + c) + yr[c];", "o[c] = yr[c];"),
+    "nyquist_dropped": ("if (f == 0 || (L % 2 == 0 && f == half)) o.im = 0.0;",
+                        "if (f == 0 || (L % 2 == 0 && f == half)) { o.im = 0.0; "
+                        "if (f == half) o.re = 0.0; }"),
+    "bf16_decode_shift": ("uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;",
+                          "uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 15;"),
+}
+
+
+def _pins_pass() -> bool:
+    """A compact run of the pins; False as soon as one fails."""
+    rng = np.random.default_rng(7)
+    try:
+        for n in (5, 7, 12, 16, 18, 30):
+            x = rng.standard_normal(n) + 1j * rng.standard_normal(n)
+            for sign in (-1, 1):
+                ref = naive_dft(x, sign)
+                if np.abs(oracle.fft(x, sign) - ref).max() > 1e-10 * np.abs(ref).max():
+                    return False
+        for L, keep in ((8, 5), (12, 7), (16, 9), (17, 4), (48, 10)):
+            B, H, D = 1, 2, 2
+            q, k, v = (rng.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+            gate = rng.uniform(0.1, 1, (H, L // 2 + 1)).astype(np.float32)
+            ref = closed_form_y(*(a.astype(np.float64) for a in (q, k, v)), gate, keep)
+            if np.abs(oracle.spectre_y(q, k, v, gate, keep) - ref).max() > 1e-10:
+                return False
+        # LayerNorm on a constructed token (mean 3, variance s^2 = 2^-20)
+        H, D = 2, 2
+        C = H * D
+        e = np.array([1.0, -1.0, 1.0, -1.0])
+        s = 2.0 ** -10
+        x = (3.0 + s * e).reshape(1, 1, H, D).astype(np.float32)
+        gamma = np.array([0.5, 1.0, 1.5, 2.0], np.float32)
+        beta = np.array([-0.1, 0.0, 0.1, 0.2], np.float32)
+        # through the full mix with a zero gate (y = 0), bf16 storage of exact values
+        bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+        xb = (bits.astype(np.uint32) << 16).view(np.float32)
+        ref = e * s / np.sqrt(s * s + 1e-5) * gamma + beta
+        for st, dt in ((x, 0), (bits, 1)):
+            if dt == 1 and not np.array_equal(xb, x):
+                continue
+            z = np.zeros((1, 1, H, D), st.dtype)
+            out = oracle.spectre_mix(z, z, z, st, np.zeros((H, 1), np.float32), gamma, beta,
+                                     0, dtype=dt)
+            if np.abs(out.reshape(C) - ref).max() > 1e-9:
+                return False
+        # bf16 decoding: a bf16-stored mix equals the float32 mix of the decoded values
+        L = 16
+        vals = rng.standard_normal((1, L, 1, 2)).astype(np.float32)
+        b16 = (vals.view(np.uint32) >> 16).astype(np.uint16)
+        dec = (b16.astype(np.uint32) << 16).view(np.float32)
+        g = np.ones((1, L // 2 + 1), np.float32)
+        ones, zeros = np.ones(2, np.float32), np.zeros(2, np.float32)
+        a = oracle.spectre_mix(b16, b16, b16, b16, g, ones, zeros, L // 2 + 1, dtype=1)
+        ref_y = closed_form_y(*(dec.astype(np.float64),) * 3, g, L // 2 + 1)
+        ref = oracle.layernorm_residual(ref_y, dec, ones, zeros)
+        if np.abs(a - ref).max() > 1e-9:
+            return False
+    except oracle.OracleError:
+        return False
+    return True
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_unmodified_source_passes(mutant_dir):
+    path = oracle.compile_source(SRC, str(mutant_dir / "lib_clean.so"))
+    with oracle.use_library(path):
+        assert _pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found: %s" % name
+    path_c = mutant_dir / ("%s.c" % name)
+    path_c.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(path_c), str(mutant_dir / ("lib_%s.so" % name)))
+    with oracle.use_library(lib):
+        assert not _pins_pass(), "planted mistake %s went unnoticed" % name

@@ -1,0 +1,356 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* its FFT against the DFT's definition, summed term by term;
+* Hermitian symmetry and Parseval's identity at the workloads' lengths;
+* the whole mix against the closed form the convolution theorem gives
+  (SPECTRE article, section 2.1 and section 2.2): y = (1/L) g (*) (q * k) (*) v,
+  with (q * k) the circular cross-correlation, (*) circular convolution and
+  g the inverse real transform of the gate, brute-forced with plain loops;
+* inputs with closed-form outputs (constants, alternating sign, one cosine,
+  impulses) at the long lengths, with a different gate per head;
+* shift covariance, trilinearity and truncation-as-zeroed-gate;
+* LayerNorm on inputs whose mean and variance are known by construction.
+
+None of these re-types the oracle's steps: each is an independent statement
+that a mistake in it (a dropped term, a wrong sign, a swapped operand, a
+wrong index or scale) would violate.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+RNG = np.random.default_rng(12345)
+
+
+def naive_dft(x, sign=-1):
+    """The DFT by its definition, one output at a time, exponents reduced mod n."""
+    n = len(x)
+    j = np.arange(n)
+    out = np.empty(n, np.complex128)
+    for f in range(n):
+        e = (f * j) % n
+        out[f] = np.sum(x * np.exp(sign * 2j * np.pi * e / n))
+    return out
+
+
+LENGTHS_SMALL = list(range(1, 65))
+
+
+@pytest.mark.parametrize("n", LENGTHS_SMALL + [96, 192, 384, 768])
+def test_fft_equals_dft_definition(n):
+    x = RNG.standard_normal(n) + 1j * RNG.standard_normal(n)
+    for sign in (-1, 1):
+        ref = naive_dft(x, sign)
+        got = oracle.fft(x, sign)
+        scale = max(1.0, np.abs(ref).max())
+        assert np.abs(got - ref).max() <= 1e-12 * scale * max(1, np.log2(n))
+
+
+def test_fft_4096_spot_bins():
+    n = 4096
+    x = RNG.standard_normal(n)
+    got = oracle.fft(x)
+    j = np.arange(n)
+    for f in (0, 1, 2, 3, 5, 1000, 2047, 2048, 2049, 4095):
+        ref = np.sum(x * np.exp(-2j * np.pi * ((f * j) % n) / n))
+        assert abs(got[f] - ref) <= 1e-11 * np.sqrt(n)
+
+
+@pytest.mark.parametrize("n", [65536, 786432, 3 * 1024, 6])
+def test_hermitian_symmetry_and_parseval(n):
+    x = RNG.standard_normal(n)
+    X = oracle.fft(x)
+    norm = np.sqrt(np.sum(np.abs(X) ** 2))
+    f = np.arange(1, n)
+    assert np.abs(X[n - f] - np.conj(X[f])).max() <= 1e-12 * norm
+    assert abs(X[0].imag) <= 1e-12 * norm
+    if n % 2 == 0:
+        assert abs(X[n // 2].imag) <= 1e-12 * norm
+    lhs = np.sum(x * x)
+    rhs = np.sum(np.abs(X) ** 2) / n
+    assert abs(lhs - rhs) <= 1e-12 * lhs
+
+
+def test_fft_linear_and_shift():
+    n = 768
+    a, b = RNG.standard_normal(n), RNG.standard_normal(n)
+    A, Bf = oracle.fft(a), oracle.fft(b)
+    assert np.allclose(oracle.fft(2 * a - 3 * b), 2 * A - 3 * Bf, atol=1e-10)
+    s = 7
+    f = np.arange(n)
+    shifted = oracle.fft(np.roll(a, s))
+    assert np.allclose(shifted, A * np.exp(-2j * np.pi * ((f * s) % n) / n), atol=1e-9)
+
+
+# ---------------------------------------------------------------- closed form
+
+def irfft_gate(G, keep, L):
+    """g[t] = inverse real transform of the gate G[f] * [f < keep], f = 0..L//2,
+    written as its cosine series (a real, even sequence)."""
+    t = np.arange(L)
+    g = np.zeros(L)
+    for f in range(L // 2 + 1):
+        if f >= keep:
+            continue
+        if f == 0:
+            g += G[0]
+        elif L % 2 == 0 and f == L // 2:
+            g += G[f] * np.cos(np.pi * t)
+        else:
+            g += 2 * G[f] * np.cos(2 * np.pi * ((f * t) % L) / L)
+    return g / L
+
+
+def circ_xcorr(q, k):
+    """r[m] = sum_n q[(n + m) mod L] k[n]."""
+    L = len(q)
+    return np.array([sum(q[(n + m) % L] * k[n] for n in range(L)) for m in range(L)])
+
+
+def circ_conv(a, b):
+    """(a (*) b)[t] = sum_s a[s] b[(t - s) mod L]."""
+    L = len(a)
+    return np.array([sum(a[s] * b[(t - s) % L] for s in range(L)) for t in range(L)])
+
+
+def closed_form_y(q, k, v, gate, keep):
+    """y[b, :, h, d] = (1/L) g_h (*) (q * k) (*) v for every column."""
+    B, L, H, D = q.shape
+    y = np.zeros((B, L, H, D))
+    for h in range(H):
+        g = irfft_gate(gate[h].astype(np.float64), keep, L)
+        for b in range(B):
+            for d in range(D):
+                r = circ_xcorr(q[b, :, h, d], k[b, :, h, d])
+                y[b, :, h, d] = circ_conv(g, circ_conv(r, v[b, :, h, d])) / L
+    return y
+
+
+@pytest.mark.parametrize("L,keep", [(1, 1), (2, 2), (3, 2), (4, 3), (5, 3), (6, 4), (8, 5),
+                                    (8, 3), (12, 7), (16, 0), (17, 9), (17, 4), (48, 25),
+                                    (48, 10), (64, 33), (64, 1)])
+def test_mix_equals_closed_form(L, keep):
+    B, H, D = 2, 2, 2
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    y = oracle.spectre_y(q, k, v, gate, keep)
+    ref = closed_form_y(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                        gate, keep)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+# ------------------------------------------------------------ special inputs
+
+def _heads_gate(H, L, seed):
+    return RNG.uniform(0.1, 1.0, (H, L // 2 + 1)).astype(np.float32)
+
+
+@pytest.mark.parametrize("L", [65536, 786432])
+def test_constant_inputs(L):
+    # q = k = v = 1: only bin 0 is non-zero, Q = K = V = L there, so y = G[h, 0] L.
+    H, D = 2, 1
+    one = np.ones((1, L, H, D), np.float32)
+    gate = _heads_gate(H, L, 1)
+    y = oracle.spectre_y(one, one, one, gate, L // 2 + 1)
+    for h in range(H):
+        ref = float(gate[h, 0]) * L
+        assert np.abs(y[0, :, h, 0] - ref).max() <= 1e-9 * ref
+
+
+@pytest.mark.parametrize("L", [65536, 786432])
+def test_alternating_inputs(L):
+    # q = k = v = (-1)^n: only the Nyquist bin is non-zero, y = G[h, L/2] L (-1)^t,
+    # and it vanishes once the Nyquist bin is truncated.
+    H, D = 2, 1
+    alt = np.tile(np.array([1, -1], np.float32), L // 2)
+    a = np.ascontiguousarray(np.broadcast_to(alt[None, :, None, None], (1, L, H, D)))
+    gate = _heads_gate(H, L, 2)
+    y = oracle.spectre_y(a, a, a, gate, L // 2 + 1)
+    for h in range(H):
+        ref = float(gate[h, L // 2]) * L * alt.astype(np.float64)
+        assert np.abs(y[0, :, h, 0] - ref).max() <= 1e-9 * float(gate[h, L // 2]) * L
+    y0 = oracle.spectre_y(a, a, a, gate, L // 2)
+    assert np.abs(y0).max() <= 1e-9 * L
+
+
+@pytest.mark.parametrize("L,bin_", [(65536, 1), (65536, 12345), (786432, 98304),
+                                    (786432, 7)])
+def test_single_cosine(L, bin_):
+    # q = k = v = cos(2 pi a n / L): Q[a] = L/2, so y = G[h, a] (L/4) cos(2 pi a t / L),
+    # and y = 0 when bin a is truncated.
+    H, D = 2, 1
+    t = np.arange(L)
+    c = np.cos(2 * np.pi * ((bin_ * t) % L) / L)
+    a = np.ascontiguousarray(np.broadcast_to(c[None, :, None, None], (1, L, H, D)))
+    a32 = a.astype(np.float32)
+    gate = _heads_gate(H, L, 3)
+    y = oracle.spectre_y(a32, a32, a32, gate, L // 2 + 1)
+    # the float32 rounding of the input perturbs the spectrum slightly
+    for h in range(H):
+        ref = float(gate[h, bin_]) * (L / 4) * c
+        assert np.abs(y[0, :, h, 0] - ref).max() <= 1e-5 * L / 4
+    y0 = oracle.spectre_y(a32, a32, a32, gate, bin_)
+    assert np.abs(y0).max() <= 1e-5 * L / 4
+
+
+@pytest.mark.parametrize("L", [4096, 65536])
+def test_impulses(L):
+    # q = k = delta_0 makes Q = K = 1, so with G = 1 and no truncation y = v / L.
+    B, H, D = 1, 2, 2
+    d = np.zeros((B, L, H, D), np.float32)
+    d[:, 0] = 1
+    v = RNG.standard_normal((B, L, H, D)).astype(np.float32)
+    gate = np.ones((H, L // 2 + 1), np.float32)
+    y = oracle.spectre_y(d, d, v, gate, L // 2 + 1)
+    assert np.abs(y - v / L).max() <= 1e-12 * L
+
+
+# ----------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("L", [96, 4096])
+def test_shift_covariance(L):
+    B, H, D = 1, 2, 2
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    keep = L // 3
+    y = oracle.spectre_y(q, k, v, gate, keep)
+    s = 5
+    tol = 1e-10 * max(1.0, np.abs(y).max())
+    assert np.abs(oracle.spectre_y(np.roll(q, s, 1), k, v, gate, keep)
+                  - np.roll(y, s, 1)).max() <= tol
+    assert np.abs(oracle.spectre_y(q, np.roll(k, s, 1), v, gate, keep)
+                  - np.roll(y, -s, 1)).max() <= tol
+    assert np.abs(oracle.spectre_y(q, k, np.roll(v, s, 1), gate, keep)
+                  - np.roll(y, s, 1)).max() <= tol
+
+
+def test_trilinearity():
+    L, B, H, D = 384, 1, 2, 2
+    q1, q2, k, v = (RNG.standard_normal((B, L, H, D)) for _ in range(4))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    f32 = lambda a: a.astype(np.float32)
+    a, b = 0.75, -1.5
+    lhs = oracle.spectre_y(f32(a * q1 + b * q2), f32(k), f32(v), gate, L // 2 + 1)
+    rhs = (a * oracle.spectre_y(f32(q1), f32(k), f32(v), gate, L // 2 + 1)
+           + b * oracle.spectre_y(f32(q2), f32(k), f32(v), gate, L // 2 + 1))
+    # lhs sees the float32 rounding of the combined input
+    assert np.abs(lhs - rhs).max() <= 1e-5 * np.abs(rhs).max()
+    two_k = oracle.spectre_y(f32(q1), f32(2 * k), f32(v), gate, L // 2 + 1)
+    assert np.allclose(two_k, 2 * oracle.spectre_y(f32(q1), f32(k), f32(v), gate,
+                                                   L // 2 + 1), atol=1e-10)
+
+
+@pytest.mark.parametrize("L,keep", [(4096, 1025), (4096, 1), (4096, 2048), (65536, 8193),
+                                    (98, 13)])
+def test_truncation_equals_zeroed_gate(L, keep):
+    B, H, D = 1, 2, 2
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gz = gate.copy()
+    gz[:, keep:] = 0
+    a = oracle.spectre_y(q, k, v, gate, keep)
+    b = oracle.spectre_y(q, k, v, gz, L // 2 + 1)
+    assert np.abs(a - b).max() <= 1e-13 * max(1.0, np.abs(b).max())
+
+
+def test_keep_zero_and_gate_zero_give_layernorm_of_x():
+    L, B, H, D = 256, 2, 2, 4
+    q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gamma = np.ones(H * D, np.float32)
+    beta = np.zeros(H * D, np.float32)
+    out0, y0 = oracle.spectre_mix(q, k, v, x, gate, gamma, beta, 0, want_y=True)
+    assert np.abs(y0).max() == 0.0
+    out1 = oracle.spectre_mix(q, k, v, x, np.zeros_like(gate), gamma, beta, L // 2 + 1)
+    assert np.array_equal(out0, out1)
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+def test_layernorm_known_statistics():
+    # Per token, x = mu + s * e with e = +1/-1 alternating over channels: the
+    # biased variance is exactly s^2, so out_c = e_c s / sqrt(s^2 + 1e-5) gamma_c + beta_c.
+    # s = 2^-10 makes eps visible (s^2 ~ 9.5e-7 against 1e-5); all values are exact
+    # in binary32, so the construction survives the float32 storage unchanged.
+    H, D = 2, 4
+    C = H * D
+    e = np.array([1.0 if c % 2 == 0 else -1.0 for c in range(C)])
+    mus = [0.0, 3.0, -2.5]
+    ss = [1.0, 2.0 ** -10, 7.0]
+    x = np.array([[mu + s * e for mu, s in zip(mus, ss)]])  # [1, 3, C]
+    x = x.reshape(1, 3, H, D).astype(np.float64)
+    x32 = x.astype(np.float32)
+    gamma = np.linspace(0.5, 2.0, C).astype(np.float32)
+    beta = np.linspace(-1.0, 1.0, C).astype(np.float32)
+    y = np.zeros_like(x)
+    out = oracle.layernorm_residual(y, x32, gamma, beta).reshape(3, C)
+    xs = x32.astype(np.float64).reshape(3, C)
+    for i in range(3):
+        mu = xs[i].mean()
+        s2 = ((xs[i] - mu) ** 2).mean()   # the float32 inputs, exact in double
+        ref = (xs[i] - mu) / np.sqrt(s2 + 1e-5) * gamma + beta
+        assert np.abs(out[i] - ref).max() <= 1e-12
+        assert s2 == ss[i] ** 2
+        assert np.abs(out[i] - (e * ss[i] / np.sqrt(ss[i] ** 2 + 1e-5) * gamma + beta)).max() \
+            <= 1e-12
+
+
+def test_layernorm_invariants_on_mix():
+    w = workloads.WORKLOADS[1]
+    inp = workloads.make_inputs(w)
+    gamma = np.linspace(0.5, 1.5, w.C).astype(np.float32)
+    beta = np.linspace(-0.2, 0.3, w.C).astype(np.float32)
+    out, y = oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], gamma,
+                                beta, w.keep_bins, want_y=True)
+    z = (inp["x"].astype(np.float64) + y).reshape(w.tokens, w.C)
+    n = ((out.reshape(w.tokens, w.C) - beta) / gamma)
+    assert np.abs(n.mean(axis=1)).max() <= 1e-12
+    var_z = z.var(axis=1)
+    assert np.abs(n.var(axis=1) - var_z / (var_z + 1e-5)).max() <= 1e-12
+
+
+# ------------------------------------------------------------ storage and API
+
+def test_bf16_storage_equals_decoded_f32():
+    w = workloads.custom(90, B=1, L=512, H=2, D=4, dtype=workloads.BF16, keep_bins=100)
+    inp = workloads.make_inputs(w)
+    dec = {n: workloads.from_bf16(inp[n]) for n in "qkvx"}
+    a = oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
+                           inp["beta"], w.keep_bins, dtype=1)
+    b = oracle.spectre_mix(dec["q"], dec["k"], dec["v"], dec["x"], inp["gate"], inp["gamma"],
+                           inp["beta"], w.keep_bins, dtype=0)
+    assert np.array_equal(a, b)
+
+
+def test_token_sample_matches_full():
+    w = workloads.custom(91, B=3, L=96, H=2, D=4)
+    inp = workloads.make_inputs(w)
+    out, y = oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
+                                inp["gamma"], inp["beta"], w.keep_bins, want_y=True)
+    toks = workloads.sample_tokens(w, 20)
+    o2, y2 = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
+                                       inp["gamma"], inp["beta"], w.keep_bins, toks)
+    flat_o = out.reshape(w.tokens, w.H, w.D)
+    flat_y = y.reshape(w.tokens, w.H, w.D)
+    assert np.array_equal(o2, flat_o[toks])
+    assert np.array_equal(y2, flat_y[toks])
+
+
+def test_thread_count_does_not_change_result():
+    w = workloads.custom(92, B=2, L=192, H=2, D=4)
+    inp = workloads.make_inputs(w)
+    args = (inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"], inp["beta"],
+            w.keep_bins)
+    assert np.array_equal(oracle.spectre_mix(*args, nthreads=1),
+                          oracle.spectre_mix(*args, nthreads=5))
+
+
+def test_rejects_bad_arguments():
+    q = np.zeros((1, 8, 1, 2), np.float32)
+    gate = np.zeros((1, 5), np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.spectre_y(q, q, q, gate, 6)   # keep_bins > L/2 + 1
+    with pytest.raises(oracle.OracleError):
+        oracle.spectre_y(q, q, q, gate, -1)
