@@ -1,0 +1,558 @@
+// kernels.hpp -- gfx950 kernels of the SPECTRE spectral mix.
+//
+// The operation (SPECTRE FFT-attention article, section 2.2 and its
+// pseudocode; section 2.3 for truncation): per column (b, h, d) of length L,
+// y = irfft( G[h][f] / L * Q[f] conj(K[f]) V[f] * [f < keep] ), then
+// out = LayerNorm_{H*D}(x + y).
+//
+// Data path.  Two real channels (2j, 2j+1) of one token share a complex
+// number z = x[2j] + i x[2j+1] (the article's section 3.1 treats re/im as two
+// real channels; here two neighbouring channels are packed the same way), so
+// one complex transform of length L carries two real columns and every
+// global access is a contiguous 8-byte (f32) or 4-byte (bf16) pair with lanes
+// running along the contiguous H*D axis.
+//
+// The length factors as L = L1 * L2 * L3 (four-step / six-step
+// decomposition).  With n = n1 (L2 L3) + m2 L3 + m3 and
+// f = k1 + L1 (k2 + L2 k3):
+//   A1  L1-point DFT over n1 per (m, pair), times w_L^{m k1}          -> T[k1][m]
+//   A2  L2-point DFT over m2 per (k1, m3, pair), times w_M^{m3 k2}     (in place)
+//   B   L3-point DFT over m3 per column (k1, k2), LDS-resident Stockham; the
+//       spectral product for the column and its mirror column; the inverse
+//       L3-point DFT over k3; times w_M^{-m3 k2} (and w_L^{-m3 k1} when
+//       L2 = 1, standing in for C2's twiddle)                          -> U (in place)
+//   C2  inverse L2-point DFT over k2, times w_L^{-m k1}                (in place)
+//   C1  inverse L1-point DFT over k1, residual, LayerNorm              -> out
+// M = L2 L3.  A pass whose size is 1 is skipped.  For L <= 4096 the whole
+// column fits one workgroup's LDS and only B runs (then a LayerNorm pass).
+//
+// Separating the two packed real spectra needs Z[f] and Z[L-f]; f and L-f
+// always sit in a column pair {(k1, k2), (k1', k2')} (or in one self-paired
+// column), which is why one B workgroup owns a column and its mirror.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dft.hpp"
+
+namespace spectre {
+
+enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_C32 = 2 };
+enum TwKind { TW_NONE = 0, TW_A1 = 1, TW_A2 = 2, TW_C2 = 3 };
+
+// ------------------------------------------------------------- storage I/O
+
+// One channel pair at complex-element offset `off`: (ch 2j, ch 2j+1).
+template <int IN>
+__device__ __forceinline__ float2 load_pair(const void* base, int64_t off) {
+  if constexpr (IN == IN_BF16) {
+    uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base) + off);
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  } else {
+    return reinterpret_cast<const float2*>(base)[off];
+  }
+}
+
+// binary32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_pair(void* base, int64_t off, float2 v) {
+  if constexpr (OUT == IN_BF16) {
+    uint32_t u = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+    __builtin_nontemporal_store(u, reinterpret_cast<uint32_t*>(base) + off);
+  } else {
+    float2* p = reinterpret_cast<float2*>(base) + off;
+    __builtin_nontemporal_store(v.x, &p->x);
+    __builtin_nontemporal_store(v.y, &p->y);
+  }
+}
+
+__device__ __forceinline__ float2 twiddle_lookup(const float2* __restrict__ tw, int e, bool inverse) {
+  float2 w = tw[e];
+  return inverse ? make_float2(w.x, -w.y) : w;
+}
+
+// ------------------------------------------------------ strided DFT passes
+//
+// Data viewed as [outer][R][inner][CP2] complex elements (CP2 = H*D/2 channel
+// pairs).  Each thread owns one (outer, inner, pair) line: R loads along the
+// middle axis, an R-point DFT in registers, a twiddle per output, R stores to
+// the same positions.  Lanes run along the pair axis, so every load/store
+// instruction of a wave touches 64 consecutive pairs.
+//
+// blockIdx.y selects the tensor (q, k, v) for the forward passes.
+
+struct StridedParams {
+  const void* in[3];
+  float2* out[3];
+  const float2* twL;  // twL[e] = exp(-2 pi i e / L)
+  int64_t outer, inner, CP2;
+  int L1;
+};
+
+template <int R, int IN, int TW, int SIGN>
+__global__ __launch_bounds__(256) void k_strided(StridedParams p) {
+  const int64_t line = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t lines = p.outer * p.inner * p.CP2;
+  if (line >= lines) return;
+  const int64_t cp = line % p.CP2;
+  const int64_t t = line / p.CP2;
+  const int i = (int)(t % p.inner);
+  const int64_t o = t / p.inner;
+  const void* in = p.in[blockIdx.y];
+  float2* out = p.out[blockIdx.y];
+  const int64_t step = p.inner * p.CP2;
+  const int64_t base = (o * R * p.inner + i) * p.CP2 + cp;
+
+  float2 a[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) a[r] = load_pair<IN>(in, base + r * step);
+  dft<R, SIGN>(a);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float2 v = a[r];
+    if constexpr (TW == TW_A1) {
+      if (r != 0 && i != 0) v = cmul(v, twiddle_lookup(p.twL, i * r, false));
+    } else if constexpr (TW == TW_A2) {
+      if (r != 0 && i != 0) v = cmul(v, twiddle_lookup(p.twL, i * r * p.L1, false));
+    } else if constexpr (TW == TW_C2) {
+      const int k1 = (int)(o % p.L1);
+      const int e = (r * (int)p.inner + i) * k1;
+      if (e != 0) v = cmul(v, twiddle_lookup(p.twL, e, true));
+    }
+    out[base + r * step] = v;
+  }
+}
+
+// ------------------------------------------- B: LDS Stockham + spectral mix
+
+struct MidParams {
+  const void* in[3];     // q, k, v sources (raw tensors, or the A-pass output)
+  float2* out;           // inverse output (may alias in[0])
+  const float* gate;     // [H][nbins]
+  const float2* twN;     // twN[e] = exp(-2 pi i e / N), e < N
+  const float2* twL;     // twL[e] = exp(-2 pi i e / L)
+  const int2* wgcols;    // per workgroup: its column(s), col = k1 + L1 * k2 (-1 = none)
+  int L, L1, L2, N, M, CP2, D, keep, nbins;
+  int nslot, cpt, Tc;
+  int selfwg;            // workgroup index holding the two self-paired columns, or -1
+  int nrad;
+  int rad[8];            // Stockham radices, product N
+  float scale;           // 1 / (8 L^2): the mix's 1/L, the inverse's 1/L, the (1/2)^3 of the split
+};
+
+// One Stockham autosort pass of radix R over the LDS-resident columns.
+// Thread (tc, col) owns butterflies j = tc + Tc*b, b < P/R; butterfly j reads
+// x[j + r N/R], applies exp(sign 2 pi i r (j mod Ns) / (Ns R)), does an R-point
+// DFT and writes x[(j / Ns) Ns R + (j mod Ns) + r Ns].  The first pass reads
+// and the last pass writes the thread's registers directly: there the data
+// sits at x[tc + Tc i] = v[i].
+template <int P, int R, int SIGN>
+__device__ __forceinline__ void stockham_pass(float2 (&v)[P], float2* lds, int N, int Ns, int Tc,
+                                              int tc, int col, int ncols, const float2* __restrict__ twN,
+                                              bool first, bool last) {
+  if constexpr (P % R != 0) {
+    return;  // never planned: the host only picks radices that divide P
+  } else {
+    constexpr int NB = P / R;
+    float2 u[NB][R];
+    const int NR = N / R;
+    if (first) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < R; ++r) u[b][r] = v[b + r * NB];
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int j = tc + Tc * b;
+#pragma unroll
+        for (int r = 0; r < R; ++r) u[b][r] = lds[(j + r * NR) * ncols + col];
+      }
+      __syncthreads();
+    }
+    const int tstride = N / (Ns * R);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int j = tc + Tc * b;
+      const int k = j % Ns;
+      if (Ns > 1) {
+#pragma unroll
+        for (int r = 1; r < R; ++r) u[b][r] = cmul(u[b][r], twiddle_lookup(twN, r * k * tstride, SIGN > 0));
+      }
+      dft<R, SIGN>(u[b]);
+      if (last) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[b + r * NB] = u[b][r];
+      } else {
+        const int base = (j / Ns) * Ns * R + k;
+#pragma unroll
+        for (int r = 0; r < R; ++r) lds[(base + r * Ns) * ncols + col] = u[b][r];
+      }
+    }
+    if (!last) __syncthreads();
+  }
+}
+
+// Full N-point transform of every column; in and out: v[i] = x[tc + Tc i].
+// The LDS buffer must be free on entry (caller synchronises).
+template <int P, int SIGN>
+__device__ __forceinline__ void fft_columns(float2 (&v)[P], float2* lds, const MidParams& p, int tc, int col,
+                                            int ncols) {
+  int Ns = 1;
+  for (int s = 0; s < p.nrad; ++s) {
+    const int R = p.rad[s];
+    const bool first = s == 0, last = s == p.nrad - 1;
+    switch (R) {
+      case 2: stockham_pass<P, 2, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 3: stockham_pass<P, 3, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 4: stockham_pass<P, 4, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 6: stockham_pass<P, 6, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 8: stockham_pass<P, 8, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 12: stockham_pass<P, 12, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      case 16: stockham_pass<P, 16, SIGN>(v, lds, p.N, Ns, p.Tc, tc, col, ncols, p.twN, first, last); break;
+      default: break;
+    }
+    Ns *= R;
+  }
+}
+
+// The i-th frequency pair a thread owns in the spectral product: element e
+// (slot se, index ie) and its mirror e' (the bin L - f of e's bin f).
+struct PairRef {
+  int se, ie, sm, im;
+};
+
+__device__ __forceinline__ bool pair_at(int i, int P, int s, int tc, int Tc, int N, bool regular,
+                                        PairRef& pr) {
+  if (regular) {
+    // slot 0 holds column c, slot 1 its mirror column: bin (0, idx) <-> (1, N-1-idx)
+    if (i >= P / 2) return false;
+    pr.se = 0;
+    pr.ie = tc + Tc * (2 * i + s);
+    pr.sm = 1;
+    pr.im = N - 1 - pr.ie;
+    return true;
+  }
+  // self-paired column in slot s: index idx <-> (a - idx) mod N with a = 0
+  // for column (0, 0) (slot 0) and a = N - 1 for the other one (slot 1)
+  const bool a_zero = s == 0;
+  pr.se = pr.sm = s;
+  if (i < P / 2) {
+    pr.ie = tc + Tc * i;
+    pr.im = a_zero ? (N - pr.ie) % N : N - 1 - pr.ie;
+    return true;
+  }
+  if (i == P / 2 && a_zero && tc == 0) {
+    pr.ie = pr.im = N / 2;
+    return true;
+  }
+  return false;
+}
+
+template <int P, int IN>
+__global__ __launch_bounds__(512) void k_mid(MidParams p) {
+  extern __shared__ float2 lds[];
+  const int ncols = p.nslot * p.cpt;
+  const int tid = threadIdx.x;
+  const int col = tid % ncols;
+  const int tc = tid / ncols;
+  const int s = col / p.cpt;
+  const int j = col - s * p.cpt;
+  const int cp = blockIdx.y * p.cpt + j;
+  const int b = blockIdx.z;
+  const int2 cols = p.wgcols[blockIdx.x];
+  const int my_col = s == 0 ? cols.x : cols.y;
+  const bool regular = p.nslot == 2 && (int)blockIdx.x != p.selfwg;
+  const bool active = my_col >= 0;
+  const int k1 = active ? my_col % p.L1 : 0;
+  const int k2 = active ? my_col / p.L1 : 0;
+  const int64_t gbase = (((int64_t)b * p.L1 + k1) * p.M + (int64_t)k2 * p.N) * p.CP2 + cp;
+
+  constexpr int NPR = P / 2 + 1;
+  float2 v[P];
+  float2 sa[NPR], sb[NPR];
+
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const void* src = p.in[x];
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) v[i] = load_pair<IN>(src, gbase + (int64_t)(tc + p.Tc * i) * p.CP2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < P; ++i) v[i] = make_float2(0.f, 0.f);
+    }
+    __syncthreads();  // LDS free: the previous tensor's product step is done
+    fft_columns<P, -1>(v, lds, p, tc, col, ncols);
+#pragma unroll
+    for (int i = 0; i < P; ++i) lds[(tc + p.Tc * i) * ncols + col] = v[i];
+    __syncthreads();
+
+    // split the two packed real spectra and accumulate the product:
+    // 2A = Z[f] + conj Z[L-f], 2B = -i (Z[f] - conj Z[L-f])
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      PairRef pr;
+      if (!pair_at(i, P, s, tc, p.Tc, p.N, regular, pr)) continue;
+      const int oe = pr.ie * ncols + pr.se * p.cpt + j;
+      const int om = pr.im * ncols + pr.sm * p.cpt + j;
+      const float2 z = lds[oe], zm = lds[om];
+      const float2 A = make_float2(z.x + zm.x, z.y - zm.y);
+      const float2 Bv = make_float2(z.y + zm.y, zm.x - z.x);
+      if (x == 0) {
+        sa[i] = A;
+        sb[i] = Bv;
+      } else if (x == 1) {
+        sa[i] = cmulc(sa[i], A);
+        sb[i] = cmulc(sb[i], Bv);
+      } else {
+        // bin of element e and the gate of each packed channel's head
+        const int se_col = pr.se == 0 ? cols.x : cols.y;
+        const int f = se_col % p.L1 + p.L1 * (se_col / p.L1 + p.L2 * pr.ie);
+        const int fc = min(f, p.L - f);
+        float ga = 0.f, gb = 0.f;
+        if (fc < p.keep) {
+          ga = p.gate[(2 * cp) / p.D * p.nbins + fc] * p.scale;
+          gb = p.gate[(2 * cp + 1) / p.D * p.nbins + fc] * p.scale;
+        }
+        const float2 oa = cscale(cmul(sa[i], A), ga);
+        const float2 ob = cscale(cmul(sb[i], Bv), gb);
+        // W[f] = Oa + i Ob, W[L-f] = conj(Oa) + i conj(Ob)
+        lds[oe] = make_float2(oa.x - ob.y, oa.y + ob.x);
+        lds[om] = make_float2(oa.x + ob.y, ob.x - oa.y);
+      }
+    }
+  }
+  __syncthreads();
+
+  // inverse transform of W along k3, then the twiddle w_M^{-m3 k2}; when there
+  // is no L2 pass (L2 = 1, m = m3) the twiddle w_L^{-m k1} of the inverse
+  // four-step joins it here
+#pragma unroll
+  for (int i = 0; i < P; ++i) v[i] = lds[(tc + p.Tc * i) * ncols + col];
+  __syncthreads();
+  fft_columns<P, +1>(v, lds, p, tc, col, ncols);
+  if (!active) return;
+  const int tw_mul = p.L1 * k2 + (p.L2 == 1 ? k1 : 0);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int m3 = tc + p.Tc * i;
+    float2 w = v[i];
+    if (tw_mul != 0 && m3 != 0) w = cmul(w, twiddle_lookup(p.twL, m3 * tw_mul, true));
+    p.out[gbase + (int64_t)m3 * p.CP2] = w;
+  }
+}
+
+// ------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// C1 token statistics.  Each lane holds NV per-token values (NV a power of
+// two <= 64); recursive halving over lane bits 32, 16, ... leaves lane l with
+// the wave's total for token l >> (6 - log2 NV), and the remaining lane bits
+// are summed by plain butterflies.  Then the waves' totals meet in LDS.
+template <int NV, int O>
+__device__ __forceinline__ void halve_sums(float* vals, int lane) {
+  if constexpr (O == 0) {
+    return;
+  } else if constexpr (NV > 1) {
+    constexpr int half = NV / 2;
+    const bool up = (lane & O) != 0;
+#pragma unroll
+    for (int q = 0; q < half; ++q) {
+      const float mine = up ? vals[half + q] : vals[q];
+      const float other = up ? vals[q] : vals[half + q];
+      vals[q] = mine + __shfl_xor(other, O, 64);
+    }
+    halve_sums<half, O / 2>(vals, lane);
+  } else {
+    vals[0] += __shfl_xor(vals[0], O, 64);
+    halve_sums<1, O / 2>(vals, lane);
+  }
+}
+
+template <int Rp>
+__device__ __forceinline__ float wave_token_sums(float (&t)[Rp], int lane) {
+  halve_sums<Rp, 32>(t, lane);
+  return t[0];
+}
+
+constexpr int next_pow2(int r) { return r <= 1 ? 1 : 2 * next_pow2((r + 1) / 2); }
+constexpr int ilog2(int r) { return r <= 1 ? 0 : 1 + ilog2(r / 2); }
+
+// ----------------------------------------- C1: inverse L1 DFT (+ LayerNorm)
+//
+// One thread per (b, m, pair): R = L1 loads U[b][k1][m][pair], an inverse
+// R-point DFT gives tokens t = n1 M + m.  With FUSE the workgroup is exactly
+// the CP2 pairs of one (b, m), so every token's H*D channels are in the
+// workgroup: residual add, two-pass mean / variance over the channels, affine,
+// store.  Without FUSE it stores y (binary32) for a separate LayerNorm pass.
+
+struct FinalParams {
+  const float2* U;
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  void* out;  // dtype out, or float y when not fused
+  int64_t M, CP2, L;
+  int64_t lines;  // B * M * CP2
+  float inv_c;
+  float eps;
+};
+
+template <int R, int DT, bool FUSE>
+__global__ __launch_bounds__(256) void k_final(FinalParams p) {
+  constexpr int Rp = next_pow2(R);
+  // fused: one workgroup per (b, m) with exactly CP2 threads; else a flat grid
+  const int64_t line = FUSE ? (int64_t)blockIdx.x * p.CP2 + threadIdx.x
+                            : (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (!FUSE && line >= p.lines) return;
+  const int64_t cp = line % p.CP2;
+  const int64_t bm = line / p.CP2;  // b * M + m
+  const int64_t m = bm % p.M;
+  const int64_t b = bm / p.M;
+
+  float2 z[R];
+  const int64_t ubase = (b * R * p.M + m) * p.CP2 + cp;
+#pragma unroll
+  for (int r = 0; r < R; ++r) z[r] = p.U[ubase + (int64_t)r * p.M * p.CP2];
+  dft<R, +1>(z);
+
+  // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
+  const int64_t obase = (b * p.L + m) * p.CP2 + cp;
+  const int64_t ostep = p.M * p.CP2;
+  if constexpr (!FUSE) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float2* yp = reinterpret_cast<float2*>(p.out) + obase + r * ostep;
+      *yp = z[r];
+    }
+  } else {
+    __shared__ float red[4][Rp];
+    __shared__ float tot[Rp];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[r] = cadd(z[r], load_pair<DT>(p.x, obase + r * ostep));
+
+    float t[Rp];
+    float mean[R], rstd[R];
+    // pass 1: mean
+#pragma unroll
+    for (int r = 0; r < Rp; ++r) t[r] = r < R ? z[r].x + z[r].y : 0.f;
+    {
+      float s = wave_token_sums<Rp>(t, lane);
+      if ((lane & ((64 / Rp) - 1)) == 0) red[wave][lane / (64 / Rp)] = s;
+      __syncthreads();
+      if (threadIdx.x < Rp) {
+        float a = 0.f;
+        for (int w = 0; w < nw; ++w) a += red[w][threadIdx.x];
+        tot[threadIdx.x] = a * p.inv_c;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) mean[r] = tot[r];
+      __syncthreads();
+    }
+    // pass 2: biased variance of the centred values
+#pragma unroll
+    for (int r = 0; r < Rp; ++r) {
+      if (r < R) {
+        const float dx = z[r].x - mean[r], dy = z[r].y - mean[r];
+        t[r] = dx * dx + dy * dy;
+      } else {
+        t[r] = 0.f;
+      }
+    }
+    {
+      float s = wave_token_sums<Rp>(t, lane);
+      if ((lane & ((64 / Rp) - 1)) == 0) red[wave][lane / (64 / Rp)] = s;
+      __syncthreads();
+      if (threadIdx.x < Rp) {
+        float a = 0.f;
+        for (int w = 0; w < nw; ++w) a += red[w][threadIdx.x];
+        tot[threadIdx.x] = 1.0f / sqrtf(a * p.inv_c + p.eps);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) rstd[r] = tot[r];
+    }
+    const float g0 = p.gamma[2 * cp], g1 = p.gamma[2 * cp + 1];
+    const float b0 = p.beta[2 * cp], b1 = p.beta[2 * cp + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float2 o = make_float2((z[r].x - mean[r]) * rstd[r] * g0 + b0,
+                                   (z[r].y - mean[r]) * rstd[r] * g1 + b1);
+      store_pair<DT>(p.out, obase + r * ostep, o);
+    }
+  }
+}
+
+// ------------------------------------------------ standalone LayerNorm
+//
+// One wave per token: lanes stride over the token's channel pairs (up to 32
+// pairs per lane, H*D <= 4096), z = x + y kept in registers, two-pass
+// statistics with wave butterflies, affine, store.
+
+struct NormParams {
+  const float2* y;
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  void* out;
+  int64_t ntok, CP2;
+  float inv_c, eps;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
+  constexpr int MAXIT = 32;
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tok >= p.ntok) return;
+  const int64_t base = tok * p.CP2;
+  float2 z[MAXIT];
+  float s = 0.f;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < p.CP2) {
+      z[it] = cadd(p.y[base + c], load_pair<DT>(p.x, base + c));
+      s += z[it].x + z[it].y;
+    }
+  }
+  const float mean = wave_sum(s) * p.inv_c;
+  float q = 0.f;
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < p.CP2) {
+      const float dx = z[it].x - mean, dy = z[it].y - mean;
+      q += dx * dx + dy * dy;
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * p.inv_c + p.eps);
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < p.CP2) {
+      const float2 o = make_float2((z[it].x - mean) * rstd * p.gamma[2 * c] + p.beta[2 * c],
+                                   (z[it].y - mean) * rstd * p.gamma[2 * c + 1] + p.beta[2 * c + 1]);
+      store_pair<DT>(p.out, base + c, o);
+    }
+  }
+}
+
+}  // namespace spectre

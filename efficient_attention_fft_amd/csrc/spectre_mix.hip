@@ -1,0 +1,705 @@
+// spectre_mix.hip -- host side of the SPECTRE spectral-mix library (C ABI).
+//
+// Validates arguments (before any device call), plans the transform of
+// length L, keeps per-device twiddle tables and a workspace, and enqueues
+// the gfx950 kernels of kernels.hpp on the caller's stream.  The operation is
+// the one the SPECTRE FFT-attention article describes in section 2.2 (with
+// section 2.3's truncation); the C ABI and its conventions are documented in
+// include/spectre_mix.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "../../include/spectre_mix.h"
+#include "kernels.hpp"
+
+namespace spectre {
+namespace {
+
+// ------------------------------------------------------------------ plan
+
+constexpr int64_t kMaxL = 3 * (int64_t(1) << 20);
+constexpr int64_t kMaxSingle = 4096;  // longest column kept whole in one workgroup's LDS
+constexpr int kMaxC = 4096;
+constexpr int kMaxMidThreads = 512;   // launch bound of the B kernel
+constexpr int kMaxFusedPairs = 256; // launch bound of the fused C1 kernel
+constexpr int kLdsBudget = 64 * 1024;  // bytes of LDS per B workgroup
+
+struct Plan {
+  int64_t L = 0, L1 = 1, L2 = 1, L3 = 1;
+  int P = 0;   // points per thread in B
+  int Tc = 0;  // threads per column in B
+  int nrad = 0;
+  int rad[8] = {0};
+};
+
+// 2^a * 3^b decomposition; false if L has another prime factor.
+bool factor23(int64_t L, int& a, int& b) {
+  a = b = 0;
+  while (L > 1 && L % 2 == 0) {
+    L /= 2;
+    ++a;
+  }
+  while (L > 1 && L % 3 == 0) {
+    L /= 3;
+    ++b;
+  }
+  return L == 1;
+}
+
+bool strided_size_ok(int64_t r) {
+  switch (r) {
+    case 2: case 3: case 4: case 6: case 8: case 12: case 16: case 24: case 32: case 48: case 64:
+      return true;
+    default:
+      return false;
+  }
+}
+
+// Radices (each dividing P) whose product is N, largest first.
+bool plan_radices(int64_t N, int P, Plan& pl) {
+  static const int cand[] = {16, 12, 8, 6, 4, 3, 2};
+  pl.nrad = 0;
+  int64_t rem = N;
+  while (rem > 1) {
+    int pick = 0;
+    for (int r : cand)
+      if (P % r == 0 && rem % r == 0) {
+        pick = r;
+        break;
+      }
+    if (!pick || pl.nrad == 8) return false;
+    pl.rad[pl.nrad++] = pick;
+    rem /= pick;
+  }
+  return true;
+}
+
+int make_plan(int64_t L, Plan& pl) {
+  pl = Plan();
+  if (L < 2 || L % 2 != 0) return SPECTRE_EINVAL;
+  int a = 0, b = 0;
+  if (!factor23(L, a, b) || b > 1 || L > kMaxL) return SPECTRE_EUNSUPPORTED;
+  pl.L = L;
+  if (L <= kMaxSingle) {
+    pl.L3 = L;
+  } else {
+    // L3: power of two <= 1024, leaving at least one factor 2 for an even L1
+    int64_t l3 = int64_t(1) << std::min(a - 1, 10);
+    int64_t rest = L / l3;
+    int64_t l1 = rest, l2 = 1;
+    if (rest > 64) {
+      int a_rest = a - (int)std::log2((double)l3);
+      l1 = int64_t(1) << std::min(a_rest, 6);
+      l2 = rest / l1;
+    }
+    if (l1 % 2 != 0 || !strided_size_ok(l1) || (l2 != 1 && !strided_size_ok(l2)))
+      return SPECTRE_EUNSUPPORTED;
+    pl.L1 = l1;
+    pl.L2 = l2;
+    pl.L3 = l3;
+  }
+  const int64_t N = pl.L3;
+  if (N % 3 == 0)
+    pl.P = N >= 12 ? 12 : 6;
+  else
+    pl.P = (int)std::min<int64_t>(16, N);
+  pl.Tc = (int)(N / pl.P);
+  if (!plan_radices(N, pl.P, pl)) return SPECTRE_EUNSUPPORTED;
+  return SPECTRE_OK;
+}
+
+bool is_single(const Plan& pl) { return pl.L1 == 1 && pl.L2 == 1; }
+
+// Channel pairs per workgroup slot in B: a power of two dividing CP2, with
+// the thread count and the LDS tile inside their budgets.
+int choose_cpt(const Plan& pl, int64_t CP2, int nslot) {
+  int cpt = 1;
+  while (true) {
+    int next = cpt * 2;
+    if (CP2 % next != 0) break;
+    if ((int64_t)pl.Tc * nslot * next > kMaxMidThreads) break;
+    if (pl.L3 * nslot * next * 8 > kLdsBudget) break;
+    if (next > 16) break;
+    cpt = next;
+  }
+  return cpt;
+}
+
+// Whether C1 can hold every channel of a token in one workgroup.
+bool fused_norm_ok(int64_t CP2) { return CP2 % 64 == 0 && CP2 <= kMaxFusedPairs; }
+
+// ----------------------------------------------------------- tables cache
+
+struct LenTables {
+  float2* twL = nullptr;   // L entries
+  float2* twN = nullptr;   // L3 entries
+  int2* wgcols = nullptr;  // column workgroups of B
+  int nwg = 0;
+  int selfwg = -1;
+};
+
+struct DeviceState {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::map<int64_t, LenTables> tables;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+// exp(-2 pi i e / n) in double, angle split exactly into a quarter turn and
+// a residual of at most pi/4, then rounded to binary32.
+float2 host_twiddle(int64_t e, int64_t n) {
+  e %= n;
+  int64_t q = (4 * e + n / 2) / n;
+  int64_t r = 4 * e - q * n;
+  double phi = (M_PI / 2) * (double)r / (double)n;
+  double c = std::cos(phi), s = std::sin(phi);
+  double re, im;
+  switch (q & 3) {
+    case 0: re = c; im = s; break;
+    case 1: re = -s; im = c; break;
+    case 2: re = -c; im = -s; break;
+    default: re = s; im = -c; break;
+  }
+  return make_float2((float)re, (float)-im);
+}
+
+// Column workgroups of B: each regular workgroup holds a column and its
+// mirror column; the two self-paired columns share one workgroup, column
+// (0, 0) in slot 0.  Single-level plans have one column per batch.
+void build_wgcols(const Plan& pl, std::vector<int2>& out, int& selfwg) {
+  out.clear();
+  selfwg = -1;
+  if (is_single(pl)) {
+    out.push_back(make_int2(0, -1));
+    return;
+  }
+  const int64_t L1 = pl.L1, L2 = pl.L2;
+  std::vector<int> self;
+  for (int64_t k2 = 0; k2 < L2; ++k2)
+    for (int64_t k1 = 0; k1 < L1; ++k1) {
+      int64_t pk1, pk2;
+      if (k1 != 0) {
+        pk1 = L1 - k1;
+        pk2 = L2 - 1 - k2;
+      } else {
+        pk1 = 0;
+        pk2 = (L2 - k2) % L2;
+      }
+      int64_t c = k1 + L1 * k2, pc = pk1 + L1 * pk2;
+      if (c == pc)
+        self.push_back((int)c);
+      else if (c < pc)
+        out.push_back(make_int2((int)c, (int)pc));
+    }
+  // column (0, 0) first: its mirror map is k3 -> (N - k3) mod N
+  int2 s = make_int2(-1, -1);
+  if (!self.empty()) s.x = self[0];
+  if (self.size() > 1) s.y = self[1];
+  selfwg = (int)out.size();
+  out.push_back(s);
+}
+
+int get_tables(int dev, const Plan& pl, LenTables** res) {
+  DeviceState& ds = g_dev[dev];
+  auto it = ds.tables.find(pl.L);
+  if (it != ds.tables.end()) {
+    *res = &it->second;
+    return SPECTRE_OK;
+  }
+  LenTables t;
+  std::vector<float2> twL(pl.L), twN(pl.L3);
+  for (int64_t e = 0; e < pl.L; ++e) twL[e] = host_twiddle(e, pl.L);
+  for (int64_t e = 0; e < pl.L3; ++e) twN[e] = host_twiddle(e, pl.L3);
+  std::vector<int2> cols;
+  build_wgcols(pl, cols, t.selfwg);
+  t.nwg = (int)cols.size();
+  if (hipMalloc(&t.twL, sizeof(float2) * pl.L) != hipSuccess) return SPECTRE_ENOMEM;
+  if (hipMalloc(&t.twN, sizeof(float2) * pl.L3) != hipSuccess ||
+      hipMalloc(&t.wgcols, sizeof(int2) * cols.size()) != hipSuccess) {
+    (void)hipFree(t.twL);
+    (void)hipFree(t.twN);
+    return SPECTRE_ENOMEM;
+  }
+  if (hipMemcpy(t.twL, twL.data(), sizeof(float2) * pl.L, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(t.twN, twN.data(), sizeof(float2) * pl.L3, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(t.wgcols, cols.data(), sizeof(int2) * cols.size(), hipMemcpyHostToDevice) !=
+          hipSuccess) {
+    (void)hipFree(t.twL);
+    (void)hipFree(t.twN);
+    (void)hipFree(t.wgcols);
+    return SPECTRE_EHIP;
+  }
+  auto ins = ds.tables.emplace(pl.L, t);
+  *res = &ins.first->second;
+  return SPECTRE_OK;
+}
+
+bool fail_alloc_forced() {
+  const char* e = std::getenv("SPECTRE_MIX_FAIL_ALLOC");
+  return e && e[0] == '1';
+}
+
+int get_workspace(int dev, size_t bytes, void** ws) {
+  DeviceState& ds = g_dev[dev];
+  if (fail_alloc_forced()) return SPECTRE_ENOMEM;
+  if (ds.ws_bytes < bytes) {
+    if (ds.ws) {
+      // the previous workspace may still be in use by enqueued work
+      if (hipDeviceSynchronize() != hipSuccess) return SPECTRE_EHIP;
+      (void)hipFree(ds.ws);
+      ds.ws = nullptr;
+      ds.ws_bytes = 0;
+    }
+    if (hipMalloc(&ds.ws, bytes) != hipSuccess) {
+      ds.ws = nullptr;
+      return SPECTRE_ENOMEM;
+    }
+    ds.ws_bytes = bytes;
+  }
+  *ws = ds.ws;
+  return SPECTRE_OK;
+}
+
+// ------------------------------------------------------------ validation
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct Shape {
+  int64_t B, H, L, D, C, CP2, N;
+  int64_t keep;
+  int dtype;
+  size_t esz;
+};
+
+int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, Shape& s,
+                Plan& pl) {
+  if (B < 1 || H < 1 || D < 1 || L < 2) return SPECTRE_EINVAL;
+  if (dtype != SPECTRE_F32 && dtype != SPECTRE_BF16) return SPECTRE_EINVAL;
+  if (L % 2 != 0) return SPECTRE_EINVAL;
+  if (keep < 0 || keep > L / 2 + 1) return SPECTRE_EINVAL;
+  if (H > kMaxC || D > kMaxC || H * D > kMaxC) return SPECTRE_EUNSUPPORTED;
+  const int64_t C = H * D;
+  if (C % 2 != 0) return SPECTRE_EUNSUPPORTED;
+  if (B > (int64_t(1) << 40) / (L * C)) return SPECTRE_EUNSUPPORTED;
+  int st = make_plan(L, pl);
+  if (st != SPECTRE_OK) return st;
+  s.B = B;
+  s.H = H;
+  s.L = L;
+  s.D = D;
+  s.C = C;
+  s.CP2 = C / 2;
+  s.N = B * L * C;
+  s.keep = keep;
+  s.dtype = dtype;
+  s.esz = dtype == SPECTRE_F32 ? 4 : 2;
+  return SPECTRE_OK;
+}
+
+size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
+  const size_t n = (size_t)s.N;
+  if (is_single(pl)) return want_fwd ? 4 * n : 0;  // y for the LayerNorm pass
+  return 12 * n;  // three complex spectra of pairs (q, k, v); U and y reuse them
+}
+
+// ------------------------------------------------------------ launching
+
+#define SPECTRE_LAUNCH_CHECK()                       \
+  do {                                               \
+    if (hipGetLastError() != hipSuccess) return SPECTRE_EHIP; \
+  } while (0)
+
+template <int R, int IN>
+int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+  const int64_t lines = p.outer * p.inner * p.CP2;
+  dim3 grid((unsigned)((lines + 255) / 256), ntensor);
+  if (tw == TW_A1)
+    hipLaunchKernelGGL((k_strided<R, IN, TW_A1, -1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_strided<R, IN, TW_A2, -1>), grid, dim3(256), 0, st, p);
+  SPECTRE_LAUNCH_CHECK();
+  return SPECTRE_OK;
+}
+
+template <int IN>
+int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+  switch (R) {
+    case 2: return launch_strided_fwd<2, IN>(p, tw, ntensor, st);
+    case 3: return launch_strided_fwd<3, IN>(p, tw, ntensor, st);
+    case 4: return launch_strided_fwd<4, IN>(p, tw, ntensor, st);
+    case 6: return launch_strided_fwd<6, IN>(p, tw, ntensor, st);
+    case 8: return launch_strided_fwd<8, IN>(p, tw, ntensor, st);
+    case 12: return launch_strided_fwd<12, IN>(p, tw, ntensor, st);
+    case 16: return launch_strided_fwd<16, IN>(p, tw, ntensor, st);
+    case 24: return launch_strided_fwd<24, IN>(p, tw, ntensor, st);
+    case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st);
+    case 48: return launch_strided_fwd<48, IN>(p, tw, ntensor, st);
+    case 64: return launch_strided_fwd<64, IN>(p, tw, ntensor, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
+template <int R>
+int launch_strided_inv(const StridedParams& p, hipStream_t st) {
+  const int64_t lines = p.outer * p.inner * p.CP2;
+  dim3 grid((unsigned)((lines + 255) / 256), 1);
+  hipLaunchKernelGGL((k_strided<R, IN_C32, TW_C2, +1>), grid, dim3(256), 0, st, p);
+  SPECTRE_LAUNCH_CHECK();
+  return SPECTRE_OK;
+}
+
+int strided_inv(int64_t R, const StridedParams& p, hipStream_t st) {
+  switch (R) {
+    case 2: return launch_strided_inv<2>(p, st);
+    case 3: return launch_strided_inv<3>(p, st);
+    case 4: return launch_strided_inv<4>(p, st);
+    case 6: return launch_strided_inv<6>(p, st);
+    case 8: return launch_strided_inv<8>(p, st);
+    case 12: return launch_strided_inv<12>(p, st);
+    case 16: return launch_strided_inv<16>(p, st);
+    case 24: return launch_strided_inv<24>(p, st);
+    case 32: return launch_strided_inv<32>(p, st);
+    case 48: return launch_strided_inv<48>(p, st);
+    case 64: return launch_strided_inv<64>(p, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
+template <int P, int IN>
+int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
+  const size_t lds = (size_t)p.N * p.nslot * p.cpt * sizeof(float2);
+  hipLaunchKernelGGL((k_mid<P, IN>), grid, dim3(threads), lds, st, p);
+  SPECTRE_LAUNCH_CHECK();
+  return SPECTRE_OK;
+}
+
+template <int IN>
+int launch_mid(int P, const MidParams& p, dim3 grid, int threads, hipStream_t st) {
+  switch (P) {
+    case 2: return launch_mid_p<2, IN>(p, grid, threads, st);
+    case 4: return launch_mid_p<4, IN>(p, grid, threads, st);
+    case 6: return launch_mid_p<6, IN>(p, grid, threads, st);
+    case 8: return launch_mid_p<8, IN>(p, grid, threads, st);
+    case 12: return launch_mid_p<12, IN>(p, grid, threads, st);
+    case 16: return launch_mid_p<16, IN>(p, grid, threads, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
+template <int R, int DT>
+int launch_final_r(const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
+  if (fuse) {
+    dim3 grid((unsigned)(B * p.M));
+    hipLaunchKernelGGL((k_final<R, DT, true>), grid, dim3((unsigned)p.CP2), 0, st, p);
+  } else {
+    dim3 grid((unsigned)((p.lines + 255) / 256));
+    hipLaunchKernelGGL((k_final<R, DT, false>), grid, dim3(256), 0, st, p);
+  }
+  SPECTRE_LAUNCH_CHECK();
+  return SPECTRE_OK;
+}
+
+template <int DT>
+int launch_final(int64_t R, const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
+  switch (R) {
+    case 2: return launch_final_r<2, DT>(p, fuse, B, st);
+    case 4: return launch_final_r<4, DT>(p, fuse, B, st);
+    case 6: return launch_final_r<6, DT>(p, fuse, B, st);
+    case 8: return launch_final_r<8, DT>(p, fuse, B, st);
+    case 12: return launch_final_r<12, DT>(p, fuse, B, st);
+    case 16: return launch_final_r<16, DT>(p, fuse, B, st);
+    case 24: return launch_final_r<24, DT>(p, fuse, B, st);
+    case 32: return launch_final_r<32, DT>(p, fuse, B, st);
+    case 48: return launch_final_r<48, DT>(p, fuse, B, st);
+    case 64: return launch_final_r<64, DT>(p, fuse, B, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
+int launch_norm(const NormParams& p, int dtype, hipStream_t st) {
+  dim3 grid((unsigned)((p.ntok + 3) / 4));
+  if (dtype == SPECTRE_F32)
+    hipLaunchKernelGGL((k_layernorm<IN_F32>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_layernorm<IN_BF16>), grid, dim3(256), 0, st, p);
+  SPECTRE_LAUNCH_CHECK();
+  return SPECTRE_OK;
+}
+
+// The spectral part into `y` (pairs, binary32), and optionally the fused
+// residual + LayerNorm into `out`.
+int run(const void* q, const void* k, const void* v, const void* x, const float* gate,
+        const float* gamma, const float* beta, void* out, float* y, const Shape& s,
+        const Plan& pl, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  LenTables* tab = nullptr;
+  int rc = get_tables(dev, pl, &tab);
+  if (rc) return rc;
+  const bool want_out = out != nullptr;
+  void* ws = nullptr;
+  const size_t wsb = workspace_for(s, pl, want_out);
+  if (wsb) {
+    rc = get_workspace(dev, wsb, &ws);
+    if (rc) return rc;
+  }
+  const int64_t CP2 = s.CP2;
+  const int64_t pairs = s.B * s.L * CP2;  // complex elements per tensor
+  const int in_kind = s.dtype == SPECTRE_F32 ? IN_F32 : IN_BF16;
+  const bool single = is_single(pl);
+  float2* T = reinterpret_cast<float2*>(ws);  // [3][B][L][CP2] complex (multi-level)
+
+  // ---- forward strided passes
+  if (!single) {
+    StridedParams a1{};
+    a1.in[0] = q;
+    a1.in[1] = k;
+    a1.in[2] = v;
+    for (int t = 0; t < 3; ++t) a1.out[t] = T + t * pairs;
+    a1.twL = tab->twL;
+    a1.outer = s.B;
+    a1.inner = pl.L2 * pl.L3;
+    a1.CP2 = CP2;
+    a1.L1 = (int)pl.L1;
+    rc = in_kind == IN_F32 ? strided_fwd<IN_F32>(pl.L1, a1, TW_A1, 3, st)
+                           : strided_fwd<IN_BF16>(pl.L1, a1, TW_A1, 3, st);
+    if (rc) return rc;
+    if (pl.L2 > 1) {
+      StridedParams a2{};
+      for (int t = 0; t < 3; ++t) {
+        a2.in[t] = T + t * pairs;
+        a2.out[t] = T + t * pairs;
+      }
+      a2.twL = tab->twL;
+      a2.outer = s.B * pl.L1;
+      a2.inner = pl.L3;
+      a2.CP2 = CP2;
+      a2.L1 = (int)pl.L1;
+      rc = strided_fwd<IN_C32>(pl.L2, a2, TW_A2, 3, st);
+      if (rc) return rc;
+    }
+  }
+
+  // ---- B: LDS transform, spectral product, inverse
+  {
+    MidParams m{};
+    const int nslot = single ? 1 : 2;
+    const int cpt = choose_cpt(pl, CP2, nslot);
+    if (single) {
+      m.in[0] = q;
+      m.in[1] = k;
+      m.in[2] = v;
+      m.out = want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y);
+    } else {
+      for (int t = 0; t < 3; ++t) m.in[t] = T + t * pairs;
+      m.out = T;  // overwrites q's spectrum in place, workgroup by workgroup
+    }
+    m.gate = gate;
+    m.twN = tab->twN;
+    m.twL = tab->twL;
+    m.wgcols = tab->wgcols;
+    m.L = (int)s.L;
+    m.L1 = (int)pl.L1;
+    m.L2 = (int)pl.L2;
+    m.N = (int)pl.L3;
+    m.M = (int)(pl.L2 * pl.L3);
+    m.CP2 = (int)CP2;
+    m.D = (int)s.D;
+    m.keep = (int)s.keep;
+    m.nbins = (int)(s.L / 2 + 1);
+    m.nslot = nslot;
+    m.cpt = cpt;
+    m.Tc = pl.Tc;
+    m.selfwg = tab->selfwg;
+    m.nrad = pl.nrad;
+    for (int i = 0; i < 8; ++i) m.rad[i] = pl.rad[i];
+    m.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
+    dim3 grid((unsigned)tab->nwg, (unsigned)(CP2 / cpt), (unsigned)s.B);
+    const int threads = pl.Tc * nslot * cpt;
+    const int kind = single ? in_kind : IN_C32;
+    if (kind == IN_F32)
+      rc = launch_mid<IN_F32>(pl.P, m, grid, threads, st);
+    else if (kind == IN_BF16)
+      rc = launch_mid<IN_BF16>(pl.P, m, grid, threads, st);
+    else
+      rc = launch_mid<IN_C32>(pl.P, m, grid, threads, st);
+    if (rc) return rc;
+  }
+
+  const float inv_c = (float)(1.0 / (double)s.C);
+  const float eps = 1e-5f;
+  if (single) {
+    if (!want_out) return SPECTRE_OK;
+    NormParams n{};
+    n.y = reinterpret_cast<const float2*>(ws);
+    n.x = x;
+    n.gamma = gamma;
+    n.beta = beta;
+    n.out = out;
+    n.ntok = s.B * s.L;
+    n.CP2 = CP2;
+    n.inv_c = inv_c;
+    n.eps = eps;
+    return launch_norm(n, s.dtype, st);
+  }
+
+  // ---- inverse strided passes
+  if (pl.L2 > 1) {
+    StridedParams c2{};
+    c2.in[0] = T;
+    c2.out[0] = T;
+    c2.twL = tab->twL;
+    c2.outer = s.B * pl.L1;
+    c2.inner = pl.L3;
+    c2.CP2 = CP2;
+    c2.L1 = (int)pl.L1;
+    rc = strided_inv(pl.L2, c2, st);
+    if (rc) return rc;
+  }
+  const bool fuse = want_out && fused_norm_ok(CP2);
+  FinalParams f{};
+  f.U = T;
+  f.x = x;
+  f.gamma = gamma;
+  f.beta = beta;
+  f.M = pl.L2 * pl.L3;
+  f.CP2 = CP2;
+  f.L = s.L;
+  f.lines = s.B * f.M * CP2;
+  f.inv_c = inv_c;
+  f.eps = eps;
+  // y for a separate LayerNorm: k's spectrum region is free once B has run
+  float* ybuf = want_out ? reinterpret_cast<float*>(T + pairs) : y;
+  if (fuse) {
+    f.out = out;
+    return s.dtype == SPECTRE_F32 ? launch_final<IN_F32>(pl.L1, f, true, s.B, st)
+                                  : launch_final<IN_BF16>(pl.L1, f, true, s.B, st);
+  }
+  f.out = ybuf;
+  rc = launch_final<IN_F32>(pl.L1, f, false, s.B, st);
+  if (rc || !want_out) return rc;
+  NormParams n{};
+  n.y = reinterpret_cast<const float2*>(ybuf);
+  n.x = x;
+  n.gamma = gamma;
+  n.beta = beta;
+  n.out = out;
+  n.ntok = s.B * s.L;
+  n.CP2 = CP2;
+  n.inv_c = inv_c;
+  n.eps = eps;
+  return launch_norm(n, s.dtype, st);
+}
+
+}  // namespace
+}  // namespace spectre
+
+using namespace spectre;
+
+extern "C" {
+
+int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x, const float* gate,
+                    const float* gamma, const float* beta, void* out, int64_t B, int64_t H,
+                    int64_t L, int64_t D, int64_t keep_bins, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v, x})
+    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
+  return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream);
+}
+
+int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate, float* y,
+                  int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                  hipStream_t stream) {
+  if (!q || !k || !v || !gate || !y) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, gate, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v})
+    if (overlaps(y, (size_t)s.N * 4, p, tb)) return SPECTRE_EINVAL;
+  return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream);
+}
+
+size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype) {
+  Shape s;
+  Plan pl;
+  if (check_shape(B, H, L, D, 0, dtype, s, pl) != SPECTRE_OK) return 0;
+  return workspace_for(s, pl, true);
+}
+
+int spectre_mix_plan(int64_t L, int64_t* l1, int64_t* l2, int64_t* l3) {
+  if (!l1 || !l2 || !l3) return SPECTRE_EINVAL;
+  Plan pl;
+  int rc = make_plan(L, pl);
+  if (rc) return rc;
+  *l1 = pl.L1;
+  *l2 = pl.L2;
+  *l3 = pl.L3;
+  return SPECTRE_OK;
+}
+
+int spectre_mix_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int cur = 0;
+  bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  int rc = SPECTRE_OK;
+  for (auto& kv : g_dev) {
+    if (hipSetDevice(kv.first) != hipSuccess) {
+      rc = SPECTRE_EHIP;
+      continue;
+    }
+    DeviceState& ds = kv.second;
+    if (ds.ws && hipFree(ds.ws) != hipSuccess) rc = SPECTRE_EHIP;
+    ds.ws = nullptr;
+    ds.ws_bytes = 0;
+    for (auto& t : ds.tables) {
+      if (hipFree(t.second.twL) != hipSuccess) rc = SPECTRE_EHIP;
+      if (hipFree(t.second.twN) != hipSuccess) rc = SPECTRE_EHIP;
+      if (hipFree(t.second.wgcols) != hipSuccess) rc = SPECTRE_EHIP;
+    }
+    ds.tables.clear();
+  }
+  g_dev.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+  return rc;
+}
+
+const char* spectre_mix_strerror(int status) {
+  switch (status) {
+    case SPECTRE_OK: return "success";
+    case SPECTRE_EINVAL: return "invalid argument";
+    case SPECTRE_EUNSUPPORTED: return "unsupported shape";
+    case SPECTRE_ENOMEM: return "out of device memory";
+    case SPECTRE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

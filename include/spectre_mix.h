@@ -1,0 +1,123 @@
+/*
+ * spectre_mix.h -- C ABI of the MI355X (gfx950) SPECTRE spectral-mix library.
+ *
+ * The operation (SPECTRE FFT-attention article, hotelren.com/news/5925787:
+ * section 2.2 and its pseudocode for the transform / cross-spectrum / gate /
+ * inverse / residual-norm order; section 2.3 for keeping only the first
+ * frequency bins; section 3.1 for treating re/im as two real channels):
+ *
+ *   for each batch b, head h, channel d (one "column" of length L):
+ *     Q[f] = sum_{n<L} q[b,n,h,d] exp(-2 pi i f n / L),  f = 0 .. L/2   (same for K, V)
+ *     O[f] = (G[h][f] / L) * Q[f] * conj(K[f]) * V[f]   if f < keep_bins, else 0
+ *     y[b,t,h,d] = inverse real FFT of O along the sequence (1/L normalisation,
+ *                  imaginary parts of bins 0 and L/2 dropped)
+ *   out[b,t,:] = LayerNorm over the H*D channels of (x[b,t,:] + y[b,t,:]):
+ *                (z - mean) / sqrt(var + 1e-5) * gamma + beta, biased variance.
+ *
+ * Everything runs in hand-written HIP kernels on the GPU; the host code only
+ * validates arguments, plans the transform, manages the workspace and
+ * enqueues kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors q, k, v, x, out: layout [B, L, H, D], contiguous, D fastest,
+ *    storage type `dtype` (SPECTRE_F32: IEEE binary32; SPECTRE_BF16: bfloat16,
+ *    stored as 16-bit patterns, rounded to nearest-even on output).  All
+ *    arithmetic is binary32.
+ *  - gate: [H][L/2 + 1] binary32, a real multiplier per (head, bin), shared
+ *    over b and d.  Bins at or above keep_bins are never read.
+ *  - gamma, beta: [H*D] binary32.
+ *  - All tensor pointers are DEVICE pointers on the current HIP device and
+ *    must be 16-byte aligned.  The caller owns them; the library never frees
+ *    or retains them past the call's stream work.
+ *  - Calls are asynchronous and stream-ordered on `stream` (0 = the null
+ *    stream): inputs must stay valid until the stream reaches the work.
+ *    Execution faults surface at the caller's next synchronisation.
+ *  - Argument validation happens before any device call; on any error code
+ *    nothing is enqueued and `out` is untouched.
+ *  - The library owns a per-device workspace and per-(device, L) twiddle
+ *    tables, created lazily on first use (so the first call on a device
+ *    allocates device memory), guarded by a mutex, reused by later calls,
+ *    and freed by spectre_mix_release().  Two calls that overlap in time on
+ *    different streams of one device share that workspace and race: order
+ *    them on one stream, or give each its own process.
+ *
+ * Supported shapes
+ * ----------------
+ *  B, H, D >= 1; H*D even and at most 4096; L even, L = 2^a * 3^b with
+ *  b <= 3 and 2 <= L <= 3 * 2^20 (longer or other lengths: SPECTRE_EUNSUPPORTED);
+ *  0 <= keep_bins <= L/2 + 1 (keep_bins = L/2 + 1: no truncation;
+ *  keep_bins = 0: y = 0, out = LayerNorm(x)).  B*L*H*D must be below 2^40.
+ */
+#ifndef SPECTRE_MIX_H
+#define SPECTRE_MIX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPECTRE_F32 = 0, SPECTRE_BF16 = 1 } spectre_dtype;
+
+typedef enum {
+  SPECTRE_OK = 0,
+  SPECTRE_EINVAL = -1,       /* a null/misaligned pointer, bad size, dtype or keep_bins, aliasing */
+  SPECTRE_EUNSUPPORTED = -2, /* a valid length/width this library does not implement */
+  SPECTRE_ENOMEM = -3,       /* workspace or table allocation failed */
+  SPECTRE_EHIP = -4          /* a HIP runtime call or kernel launch failed */
+} spectre_status;
+
+/*
+ * The whole mix (see the top of this file): out = LayerNorm(x + y).
+ * q, k, v, x: [B, L, H, D] dtype; gate: [H][L/2+1] f32; gamma, beta: [H*D] f32;
+ * out: [B, L, H, D] dtype, must not overlap any input.
+ * Returns SPECTRE_OK or an error code (nothing enqueued on error).
+ */
+int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x,
+                    const float* gate, const float* gamma, const float* beta, void* out,
+                    int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                    hipStream_t stream);
+
+/*
+ * The spectral part alone (same definition, stopped before the residual and
+ * the norm): y [B, L, H, D] binary32, on the device, caller-owned, must not
+ * overlap an input.  Used to check the transform directly, because the
+ * LayerNorm hides a per-token scale error.
+ */
+int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate, float* y,
+                  int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                  hipStream_t stream);
+
+/*
+ * Device workspace bytes a spectre_mix_fwd call of this shape uses (0 if the
+ * shape is invalid or unsupported).  Pure host arithmetic; no device call.
+ */
+size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype);
+
+/*
+ * Transform plan for length L, for inspection: the sequence length factors
+ * as L = l1 * l2 * l3 (l1: first strided pass, l2: second strided pass, 1 if
+ * absent; l3: the LDS-resident pass).  Returns SPECTRE_OK or
+ * SPECTRE_EUNSUPPORTED / SPECTRE_EINVAL.  No device call.
+ */
+int spectre_mix_plan(int64_t L, int64_t* l1, int64_t* l2, int64_t* l3);
+
+/*
+ * Frees the workspace and twiddle tables on every device the library has
+ * used.  The caller must make sure no call's stream work is still pending.
+ * Later calls recreate what they need.  Returns SPECTRE_OK or SPECTRE_EHIP.
+ */
+int spectre_mix_release(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* spectre_mix_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTRE_MIX_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+the header declares, and rejects bad arguments before touching the device.
+No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import efficient_attention_fft_amd as sm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spectre_mix.h")
+
+GOOD = 1 << 20          # a 16-byte-aligned fake address; never dereferenced here
+SHAPE = (1, 8, 65536, 64)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spectre_mix_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(sm.EXPORTS)
+
+
+@pytest.mark.parametrize("name", sm.EXPORTS)
+def test_library_exports_symbol(name):
+    lib = ctypes.CDLL(sm.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_strerror_names_every_status():
+    for st in (0, -1, -2, -3, -4):
+        assert sm.spectre_mix_strerror(st) not in ("", "unknown status")
+    assert sm.spectre_mix_strerror(7) == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(q=GOOD, k=GOOD + 0x1000000, v=GOOD + 0x2000000, x=GOOD + 0x3000000,
+             gate=GOOD + 0x4000000, gamma=GOOD + 0x5000000, beta=GOOD + 0x6000000,
+             out=GOOD + 0x70000000, B=1, H=8, L=65536, D=64, keep_bins=32769, dtype=0)
+    a.update(kw)
+    return sm.spectre_mix_fwd(a["q"], a["k"], a["v"], a["x"], a["gate"], a["gamma"], a["beta"],
+                              a["out"], a["B"], a["H"], a["L"], a["D"], a["keep_bins"],
+                              a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), sm.SPECTRE_EINVAL),
+    (dict(out=0), sm.SPECTRE_EINVAL),
+    (dict(gate=0), sm.SPECTRE_EINVAL),
+    (dict(B=0), sm.SPECTRE_EINVAL),
+    (dict(H=0), sm.SPECTRE_EINVAL),
+    (dict(D=-1), sm.SPECTRE_EINVAL),
+    (dict(L=0), sm.SPECTRE_EINVAL),
+    (dict(L=65535, keep_bins=1), sm.SPECTRE_EINVAL),  # odd
+    (dict(L=5 * 4096, keep_bins=1), sm.SPECTRE_EUNSUPPORTED),    # prime factor 5
+    (dict(L=9 * 4096, keep_bins=1), sm.SPECTRE_EUNSUPPORTED),    # 3^2
+    (dict(L=6 * 2 ** 20), sm.SPECTRE_EUNSUPPORTED),  # above 3 * 2^20
+    (dict(keep_bins=-1), sm.SPECTRE_EINVAL),
+    (dict(keep_bins=32770), sm.SPECTRE_EINVAL),
+    (dict(dtype=2), sm.SPECTRE_EINVAL),
+    (dict(q=GOOD + 8), sm.SPECTRE_EINVAL),          # misaligned
+    (dict(gamma=GOOD + 0x5000004), sm.SPECTRE_EINVAL),
+    (dict(H=3, D=1), sm.SPECTRE_EUNSUPPORTED),      # odd H*D
+    (dict(H=64, D=128), sm.SPECTRE_EUNSUPPORTED),   # H*D above 4096
+    (dict(out=GOOD + 0x1000000 + 4096), sm.SPECTRE_EINVAL),  # out overlaps k
+    (dict(out=GOOD + 0x3000000), sm.SPECTRE_EINVAL),         # out == x
+])
+def test_fwd_rejects_before_device(kw, expect):
+    assert fwd(**kw) == expect
+
+
+def test_y_rejects_before_device():
+    assert sm.spectre_mix_y(0, GOOD, GOOD, GOOD, GOOD, 1, 8, 4096, 64, 2049, 0, 0) == \
+        sm.SPECTRE_EINVAL
+    assert sm.spectre_mix_y(GOOD, GOOD, GOOD, GOOD, GOOD + 0x40000000, 1, 8, 4096, 64, 2050, 0,
+                            0) == sm.SPECTRE_EINVAL
+    # y overlapping q
+    assert sm.spectre_mix_y(GOOD, GOOD, GOOD, GOOD, GOOD + 16, 1, 8, 4096, 64, 2049, 0, 0) == \
+        sm.SPECTRE_EINVAL
+
+
+def test_plan_factorisation():
+    cases = {256: (1, 1, 256), 4096: (1, 1, 4096), 3072: (1, 1, 3072), 6144: (6, 1, 1024),
+             8192: (8, 1, 1024), 65536: (64, 1, 1024), 98304: (32, 3, 1024),
+             786432: (64, 12, 1024), 3 * 2 ** 20: (64, 48, 1024), 2: (1, 1, 2), 6: (1, 1, 6)}
+    for L, want in cases.items():
+        st, got = sm.spectre_mix_plan(L)
+        assert st == sm.SPECTRE_OK and got == want, (L, got)
+        assert got[0] * got[1] * got[2] == L
+
+
+def test_every_supported_length_plans():
+    ok = 0
+    for a in range(1, 22):
+        for b in range(0, 2):
+            L = 2 ** a * 3 ** b
+            st, (l1, l2, l3) = sm.spectre_mix_plan(L)
+            if L > 3 * 2 ** 20:
+                assert st == sm.SPECTRE_EUNSUPPORTED
+                continue
+            assert st == sm.SPECTRE_OK, L
+            assert l1 * l2 * l3 == L and l1 <= 64 and l2 <= 64 and l3 <= 4096
+            ok += 1
+    assert ok == 41  # 2^1..2^21 and 3*2^1..3*2^20
+
+
+def test_workspace_bytes():
+    N = 1 * 65536 * 512
+    assert sm.spectre_mix_workspace_bytes(1, 8, 65536, 64, 0) == 12 * N
+    assert sm.spectre_mix_workspace_bytes(2, 8, 65536, 64, 1) == 12 * 2 * N
+    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
+    assert sm.spectre_mix_workspace_bytes(1, 8, 65535, 64, 0) == 0
+
+
+def test_release_without_device_is_clean():
+    assert sm.spectre_mix_release() == sm.SPECTRE_OK

@@ -1,0 +1,181 @@
+"""GPU path against the oracle, element by element, through the C ABI.
+
+Tolerances: max-abs error on out of 1e-4 with binary32 storage and 2e-2
+with bfloat16 storage (binary32 arithmetic); y from spectre_mix_y within
+1e-4 * max(1, max|y|).  The workloads are the five seeded shapes; the edge
+cases cover tiny and ragged lengths, every plan shape (single-level,
+two-level, three-level, radix-3 in each position), widths that do and do
+not fuse the LayerNorm, and the truncation extremes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import (DeviceInputs, empty_like_storage, oracle_out, oracle_threads, run_out,
+                      run_y, to_host_f64, tol, torch, y_tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_full(w, keep=None, check_y=True):
+    say("case", w.describe(), "keep", keep)
+    inp = workloads.make_inputs(w)
+    ref_out, ref_y = oracle_out(w, inp, keep, want_y=True)
+    got = run_out(w, inp, keep)
+    err = np.abs(got - ref_out).max()
+    say("  out max-abs err %.3g (tol %.1g), max|ref| %.3f" % (err, tol(w), np.abs(ref_out).max()))
+    assert np.all(np.isfinite(got))
+    assert err <= tol(w)
+    if check_y:
+        gy = run_y(w, inp, keep)
+        ey = np.abs(gy - ref_y).max()
+        say("  y max-abs err %.3g (tol %.3g)" % (ey, y_tol(ref_y)))
+        assert ey <= y_tol(ref_y)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_workload_full(wid):
+    check_full(workloads.WORKLOADS[wid])
+
+
+@pytest.mark.timeout(900)
+def test_workload5_sampled_tokens():
+    """786432 tokens: the oracle transforms every column in full and keeps a
+    sample of tokens; the GPU output is compared at those tokens."""
+    w = workloads.WORKLOADS[5]
+    say("case", w.describe(), "(sampled)")
+    t = torch()
+    inp = workloads.make_inputs(w)
+    toks = workloads.sample_tokens(w, 48)
+    ref_out, ref_y = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"],
+                                               inp["gate"], inp["gamma"], inp["beta"],
+                                               w.keep_bins, toks, nthreads=oracle_threads())
+    d = DeviceInputs(w, inp)
+    _, out = empty_like_storage(w)
+    import efficient_attention_fft_amd as sm
+    sm.check(d.fwd(out))
+    t.cuda.synchronize()
+    sel = t.from_numpy(toks).cuda()
+    got = to_host_f64(out.view(w.tokens, w.C)[sel], w.dtype).reshape(-1, w.H, w.D)
+    err = np.abs(got - ref_out).max()
+    say("  out max-abs err %.3g over %d tokens" % (err, len(toks)))
+    assert err <= tol(w)
+    del out
+    y = t.empty((w.N,), dtype=t.float32, device="cuda")
+    sm.check(d.y(y))
+    t.cuda.synchronize()
+    gy = y.view(w.tokens, w.C)[sel].cpu().numpy().astype(np.float64).reshape(-1, w.H, w.D)
+    ey = np.abs(gy - ref_y).max()
+    say("  y max-abs err %.3g (tol %.3g)" % (ey, y_tol(ref_y)))
+    assert ey <= y_tol(ref_y)
+
+
+EDGE = [
+    # (B, L, H, D, dtype, keep)  keep None = no truncation
+    (1, 2, 1, 2, 0, None),
+    (2, 4, 1, 2, 0, None),
+    (1, 6, 2, 1, 0, None),
+    (3, 8, 1, 6, 0, 3),
+    (1, 12, 2, 2, 1, None),
+    (2, 24, 2, 4, 0, 5),
+    (1, 96, 3, 2, 0, None),         # head size 2, odd head count
+    (1, 256, 1, 32, 0, 0),          # keep 0: out = LayerNorm(x)
+    (1, 256, 2, 16, 0, 1),          # only the DC bin
+    (1, 1536, 4, 8, 1, 700),
+    (2, 4096, 2, 8, 0, 2048),       # Nyquist dropped
+    (1, 3072, 2, 32, 0, None),      # radix 3 in the LDS pass
+    (1, 6144, 2, 64, 0, None),      # two-level, radix 3 in the strided pass (l1 = 6)
+    (2, 8192, 4, 32, 1, 1000),      # two-level, fused norm, bf16
+    (1, 12288, 1, 6, 0, None),      # two-level, narrow: separate norm pass
+    (1, 49152, 2, 64, 0, 20000),    # two-level, l1 = 48
+    (1, 98304, 2, 64, 0, None),     # three-level, l2 = 3
+    (1, 196608, 1, 128, 1, 50000),  # three-level, l2 = 6
+    (1, 16384, 4, 256, 0, None),    # H*D = 1024: separate norm pass
+    (1, 4096, 2, 5, 0, None),       # channel pairs straddle heads (odd D)
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep", EDGE)
+def test_edge_shapes(B, L, H, D, dt, keep):
+    kb = L // 2 + 1 if keep is None else keep
+    w = workloads.custom(200 + L % 97, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=kb, affine=True)
+    check_full(w)
+
+
+def test_truncated_band_matches_zeroed_gate_on_gpu():
+    w = workloads.custom(301, B=1, L=65536, H=2, D=64, keep_bins=8193)
+    inp = workloads.make_inputs(w)
+    a = run_y(w, inp)
+    inp2 = dict(inp)
+    g = inp["gate"].copy()
+    g[:, 8193:] = 0
+    inp2["gate"] = g
+    b = run_y(w, inp2, keep=w.L // 2 + 1)
+    assert np.abs(a - b).max() <= 1e-6 * max(1.0, np.abs(b).max())
+
+
+def test_deterministic_and_inputs_untouched():
+    w = workloads.WORKLOADS[3]
+    t = torch()
+    inp = workloads.make_inputs(w)
+    d = DeviceInputs(w, inp)
+    before = [x.clone() for x in (d.q, d.k, d.v, d.x, d.gate, d.gamma, d.beta)]
+    guard = 4096
+    whole1, o1 = empty_like_storage(w, guard)
+    whole2, o2 = empty_like_storage(w, guard)
+    import efficient_attention_fft_amd as sm
+    sm.check(d.fwd(o1))
+    sm.check(d.fwd(o2))
+    t.cuda.synchronize()
+    assert t.equal(o1, o2), "two calls differ bitwise"
+    for a, b in zip(before, (d.q, d.k, d.v, d.x, d.gate, d.gamma, d.beta)):
+        assert t.equal(a, b), "an input was modified"
+    for whole in (whole1, whole2):
+        assert t.isnan(whole[:guard]).all() and t.isnan(whole[-guard:]).all(), \
+            "write outside out"
+
+
+def test_side_stream_and_release():
+    w = workloads.WORKLOADS[2]
+    t = torch()
+    inp = workloads.make_inputs(w)
+    ref = oracle_out(w, inp)
+    d = DeviceInputs(w, inp)
+    import efficient_attention_fft_amd as sm
+    s = t.cuda.Stream()
+    _, out = empty_like_storage(w)
+    with t.cuda.stream(s):
+        sm.check(d.fwd(out, stream=s))
+    s.synchronize()
+    assert np.abs(to_host_f64(out, w.dtype).reshape(ref.shape) - ref).max() <= tol(w)
+    assert sm.spectre_mix_release() == sm.SPECTRE_OK
+    _, out2 = empty_like_storage(w)
+    sm.check(d.fwd(out2))
+    t.cuda.synchronize()
+    assert t.equal(out, out2)
+
+
+def test_forced_allocation_failure_leaves_out_untouched(monkeypatch):
+    w = workloads.custom(302, B=1, L=8192, H=2, D=64)
+    t = torch()
+    inp = workloads.make_inputs(w)
+    d = DeviceInputs(w, inp)
+    import efficient_attention_fft_amd as sm
+    assert sm.spectre_mix_release() == sm.SPECTRE_OK
+    monkeypatch.setenv("SPECTRE_MIX_FAIL_ALLOC", "1")
+    _, out = empty_like_storage(w)
+    assert d.fwd(out) == sm.SPECTRE_ENOMEM
+    t.cuda.synchronize()
+    assert t.isnan(out).all()
+    monkeypatch.delenv("SPECTRE_MIX_FAIL_ALLOC")
+    sm.check(d.fwd(out))
+    t.cuda.synchronize()
+    assert not t.isnan(out).any()
