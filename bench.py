@@ -1,0 +1,308 @@
+"""Benchmark of the SPECTRE spectral mix forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is one spectre_mix_fwd call over the whole workload (all passes of
+the hot path: forward transforms of q, k, v, the gated spectral product, the
+inverse transform, residual + LayerNorm), with every input already resident
+in device memory.  W untimed steps, then exactly K timed steps between two
+device synchronisations.  Prints one JSON line:
+
+  value        tokens/s = B * L * K / (timed seconds), one GPU
+  roofline     the dominant kernel's algorithmic bytes per launch divided by
+               its average duration (HIP events recorded by the library on
+               its own stream over K traced calls), against 8 TB/s HBM;
+               `traffic` is HBM bytes per launch from the committed
+               rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by a plain
+               copy's reading), or null when the kernels have changed since
+  cpu_baseline the CPU oracle timed on this host on the whole workload
+
+The default workload is the article's long-context shape B=1, L=65536, H=8,
+D=64 in binary32 with no truncation.
+
+Other modes (used to produce the files under profiles/):
+    --profile-run        the timed steps only (no CPU baseline), plus one
+                         known-size device copy for counter calibration
+    --summarize DIR ...  turn rocprofv3 output directories into the text
+                         summaries kept under profiles/
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+CSRC = os.path.join(ROOT, "efficient_attention_fft_amd", "csrc")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(name: str, w) -> int:
+    """Algorithmic HBM bytes of one launch of a pass: every tensor element the
+    pass must read or write once (inputs, the spectra it exchanges, outputs,
+    the kept gate bins)."""
+    N = w.N
+    s = w.elem_bytes
+    spec = 4 * N  # one tensor's spectrum as binary32 complex channel pairs
+    gate = 4 * w.H * min(w.keep_bins, w.nbins)
+    if name == "A1_fwd_strided":
+        return 3 * N * s + 3 * spec
+    if name == "A2_fwd_strided":
+        return 6 * spec
+    if name == "B_mid_lds":
+        import efficient_attention_fft_amd as sm
+        _, (l1, l2, _) = sm.spectre_mix_plan(w.L)
+        if l1 == 1 and l2 == 1:
+            return 3 * N * s + spec + gate
+        return 3 * spec + spec + gate
+    if name == "C2_inv_strided":
+        return 2 * spec
+    if name == "C1_inv_norm":
+        return spec + 2 * N * s + 8 * w.C
+    if name == "C1_inv":
+        return 2 * spec
+    if name == "LN_norm":
+        return spec + 2 * N * s + 8 * w.C
+    raise KeyError(name)
+
+
+def model_bytes(w) -> int:
+    """The frozen byte model of the whole call: read q, k, v, x once and write
+    out once, plus the four-step's exchanges (2 x 4N per forward spectrum and
+    2 x 4N for the inverse) when the column does not fit one workgroup."""
+    N, s = w.N, w.elem_bytes
+    m_min = 5 * N * s + 4 * w.H * min(w.keep_bins, w.nbins) + 8 * w.C
+    if w.L <= 4096:
+        return m_min
+    extra = 32 * N
+    if w.L > 65536 * 4:
+        extra += 24 * N
+    return m_min + extra
+
+
+def cpu_baseline(w, inp):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
+                       inp["beta"], w.keep_bins, dtype=w.dtype, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+            "kind": "oracle", "sample": "the whole workload once: %d columns x %d tokens, "
+            "float64, %.2f s wall" % (w.B * w.C, w.L, dt)}
+
+
+def traffic_for(kernel: str, w):
+    """HBM bytes per launch of `kernel` from the committed counters, or None."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_hash") != source_hash() or c.get("workload") != w.name:
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def run_bench(args):
+    import numpy as np  # noqa: F401
+    import torch
+
+    import efficient_attention_fft_amd as sm
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    print("bench: workload %s, generating inputs" % w.name, file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(w)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    gate, gamma, beta = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return sm.spectre_mix_fwd(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
+                                  w.keep_bins, w.dtype, stream)
+
+    for _ in range(args.warmup):
+        sm.check(step())
+    torch.cuda.synchronize()
+    print("bench: warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        sm.check(step())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = w.tokens * args.steps / wall
+
+    # per-kernel durations: the same K calls again, with the library's events
+    sm.check(sm.spectre_mix_trace_start(args.steps))
+    for _ in range(args.steps):
+        sm.check(step())
+    st, kernels, ncalls = sm.spectre_mix_trace_stop()
+    sm.check(st)
+    per_kernel = {name: tot / max(ncalls, 1) for name, tot in kernels}
+    print("bench: per-kernel ms " + json.dumps({k: round(v, 4) for k, v in per_kernel.items()}),
+          file=sys.stderr, flush=True)
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_bytes = kernel_bytes(dom, w)
+    achieved = dom_bytes / (per_kernel[dom] * 1e-3) / 1e9
+    traffic = traffic_for(dom, w)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                "avg_ms": round(per_kernel[dom], 5)}
+    mb = model_bytes(w)
+    whole = {"model_bytes": mb,
+             "model_GBps": round(mb / (ms_per_step * 1e-3) / 1e9, 1),
+             "model_frac": round(mb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()}}
+
+    if args.profile_run:
+        # one known-size copy, for scaling the HBM counters
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": "tokens/s + achieved HBM GB/s (% peak), FFT spectral mix fwd L=64K H=8 D=64 fp32",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == workloads.F32 else "bf16",
+        "data": "synthetic",
+        "config": dict(w.describe(), parallelism="single GPU"),
+        "roofline": roofline,
+        "whole_call": whole,
+    }
+    if not args.profile_run and not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+# ------------------------------------------------------- rocprofv3 summaries
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    for key, short in (("k_strided", None), ("k_mid", "B_mid_lds"), ("k_final", None),
+                       ("k_layernorm", "LN_norm")):
+        if key in name:
+            if short:
+                return short
+            if key == "k_strided":
+                if "1, -1" in name or "ILi1ELin1E" in name:
+                    return "A1_fwd_strided"
+                if "2, -1" in name or "ILi2ELin1E" in name:
+                    return "A2_fwd_strided"
+                return "C2_inv_strided"
+            if key == "k_final":
+                return "C1_inv_norm" if "true" in name or "Lb1E" in name else "C1_inv"
+    return name[:60]
+
+
+def summarize(dirs, out_json=None):
+    """Kernel durations (kernel_stats) and FETCH_SIZE / WRITE_SIZE
+    (counter_collection) from rocprofv3 output directories."""
+    stats, counters = {}, {}
+    for d in dirs:
+        for p in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            for r in _read_csv(p):
+                nm = r.get("Name") or r.get("KernelName") or ""
+                stats[nm] = r
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in _read_csv(p):
+                nm = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName") or ""
+                cn = r.get("Counter_Name") or r.get("Counter-Name") or ""
+                val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0)
+                key = (nm, cn)
+                counters.setdefault(key, []).append(val)
+    lines = []
+    if stats:
+        lines.append("kernel | calls | avg us | min us | max us | total %")
+        for nm, r in sorted(stats.items(), key=lambda kv: -float(kv[1].get("TotalDurationNs", 0))):
+            avg = float(r.get("AverageNs", 0)) / 1e3
+            lines.append("%s | %s | %.2f | %.2f | %.2f | %s" % (
+                _short(nm), r.get("Calls"), avg, float(r.get("MinNs", 0)) / 1e3,
+                float(r.get("MaxNs", 0)) / 1e3, r.get("Percentage")))
+    if counters:
+        lines.append("")
+        lines.append("kernel | counter | mean per dispatch (KiB) | dispatches")
+        for (nm, cn), vals in sorted(counters.items()):
+            lines.append("%s | %s | %.1f | %d" % (_short(nm), cn, sum(vals) / len(vals), len(vals)))
+    return "\n".join(lines), stats, counters
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize:
+        text, _, _ = summarize(args.summarize)
+        print(text)
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested; run with --gpus 1)" % args.gpus, file=sys.stderr)
+        return 2
+    run_bench(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -24,7 +24,8 @@ SPECTRE_ENOMEM = -3
 SPECTRE_EHIP = -4
 
 EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "spectre_mix_plan",
-           "spectre_mix_release", "spectre_mix_strerror")
+           "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
+           "spectre_mix_strerror")
 
 
 class SpectreError(RuntimeError):
@@ -72,6 +73,11 @@ def _load():
     lib.spectre_mix_plan.restype = ci
     lib.spectre_mix_release.argtypes = []
     lib.spectre_mix_release.restype = ci
+    lib.spectre_mix_trace_start.argtypes = [ci]
+    lib.spectre_mix_trace_start.restype = ci
+    lib.spectre_mix_trace_stop.argtypes = [ci, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ci),
+                                           ctypes.POINTER(ci), ctypes.c_char_p, ci]
+    lib.spectre_mix_trace_stop.restype = ci
     lib.spectre_mix_strerror.argtypes = [ci]
     lib.spectre_mix_strerror.restype = ctypes.c_char_p
     runtimes = _hip_runtimes()
@@ -131,6 +137,28 @@ def spectre_mix_plan(L):
 
 def spectre_mix_release() -> int:
     return _lib.spectre_mix_release()
+
+
+def spectre_mix_trace_start(max_calls: int) -> int:
+    return _lib.spectre_mix_trace_start(max_calls)
+
+
+def spectre_mix_trace_stop(max_kernels: int = 8):
+    """(status, [(kernel name, total ms over the traced calls)], calls traced)."""
+    total = (ctypes.c_float * max_kernels)()
+    nk, nc = ctypes.c_int(), ctypes.c_int()
+    name_len = 32
+    names = ctypes.create_string_buffer(max_kernels * name_len)
+    st = _lib.spectre_mix_trace_stop(max_kernels, total, ctypes.byref(nk), ctypes.byref(nc),
+                                     names, name_len)
+    if st != SPECTRE_OK:
+        return st, [], 0
+    raw = names.raw
+    out = []
+    for k in range(nk.value):
+        nm = raw[k * name_len:(k + 1) * name_len].split(b"\0", 1)[0].decode()
+        out.append((nm, float(total[k])))
+    return st, out, nc.value
 
 
 def spectre_mix_strerror(status: int) -> str:

@@ -154,6 +154,53 @@ struct DeviceState {
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
 
+// ---------------------------------------------------------------- tracing
+//
+// Optional per-kernel HIP events: one before a traced call's first kernel,
+// one after each kernel.  Guarded by g_mu like everything else.
+
+constexpr int kMaxKernelsPerCall = 8;
+
+struct TraceCall {
+  size_t first = 0;  // index of the call's first event in the pool
+  int nk = 0;
+  const char* names[kMaxKernelsPerCall] = {nullptr};
+};
+
+struct TraceState {
+  bool on = false;
+  int max_calls = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<TraceCall> calls;
+  bool active = false;  // the current call is being traced
+  hipStream_t stream = nullptr;
+};
+
+TraceState g_trace;
+
+void trace_call_begin(hipStream_t st) {
+  g_trace.active = false;
+  if (!g_trace.on || (int)g_trace.calls.size() >= g_trace.max_calls) return;
+  if (g_trace.used + kMaxKernelsPerCall + 1 > g_trace.pool.size()) return;
+  TraceCall c;
+  c.first = g_trace.used;
+  if (hipEventRecord(g_trace.pool[g_trace.used], st) != hipSuccess) return;
+  ++g_trace.used;
+  g_trace.calls.push_back(c);
+  g_trace.active = true;
+  g_trace.stream = st;
+}
+
+void trace_kernel(const char* name) {
+  if (!g_trace.active) return;
+  TraceCall& c = g_trace.calls.back();
+  if (c.nk >= kMaxKernelsPerCall) return;
+  if (hipEventRecord(g_trace.pool[g_trace.used], g_trace.stream) != hipSuccess) return;
+  ++g_trace.used;
+  c.names[c.nk++] = name;
+}
+
 // exp(-2 pi i e / n) in double, angle split exactly into a quarter turn and
 // a residual of at most pi/4, then rounded to binary32.
 float2 host_twiddle(int64_t e, int64_t n) {
@@ -318,9 +365,10 @@ size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
 
 // ------------------------------------------------------------ launching
 
-#define SPECTRE_LAUNCH_CHECK()                       \
-  do {                                               \
+#define SPECTRE_LAUNCH_CHECK(name)                            \
+  do {                                                        \
     if (hipGetLastError() != hipSuccess) return SPECTRE_EHIP; \
+    trace_kernel(name);                                       \
   } while (0)
 
 template <int R, int IN>
@@ -331,7 +379,7 @@ int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t 
     hipLaunchKernelGGL((k_strided<R, IN, TW_A1, -1>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((k_strided<R, IN, TW_A2, -1>), grid, dim3(256), 0, st, p);
-  SPECTRE_LAUNCH_CHECK();
+  SPECTRE_LAUNCH_CHECK(tw == TW_A1 ? "A1_fwd_strided" : "A2_fwd_strided");
   return SPECTRE_OK;
 }
 
@@ -358,7 +406,7 @@ int launch_strided_inv(const StridedParams& p, hipStream_t st) {
   const int64_t lines = p.outer * p.inner * p.CP2;
   dim3 grid((unsigned)((lines + 255) / 256), 1);
   hipLaunchKernelGGL((k_strided<R, IN_C32, TW_C2, +1>), grid, dim3(256), 0, st, p);
-  SPECTRE_LAUNCH_CHECK();
+  SPECTRE_LAUNCH_CHECK("C2_inv_strided");
   return SPECTRE_OK;
 }
 
@@ -383,7 +431,7 @@ template <int P, int IN>
 int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
   const size_t lds = (size_t)p.N * p.nslot * p.cpt * sizeof(float2);
   hipLaunchKernelGGL((k_mid<P, IN>), grid, dim3(threads), lds, st, p);
-  SPECTRE_LAUNCH_CHECK();
+  SPECTRE_LAUNCH_CHECK("B_mid_lds");
   return SPECTRE_OK;
 }
 
@@ -409,7 +457,7 @@ int launch_final_r(const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
     dim3 grid((unsigned)((p.lines + 255) / 256));
     hipLaunchKernelGGL((k_final<R, DT, false>), grid, dim3(256), 0, st, p);
   }
-  SPECTRE_LAUNCH_CHECK();
+  SPECTRE_LAUNCH_CHECK(fuse ? "C1_inv_norm" : "C1_inv");
   return SPECTRE_OK;
 }
 
@@ -436,7 +484,7 @@ int launch_norm(const NormParams& p, int dtype, hipStream_t st) {
     hipLaunchKernelGGL((k_layernorm<IN_F32>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((k_layernorm<IN_BF16>), grid, dim3(256), 0, st, p);
-  SPECTRE_LAUNCH_CHECK();
+  SPECTRE_LAUNCH_CHECK("LN_norm");
   return SPECTRE_OK;
 }
 
@@ -458,6 +506,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     rc = get_workspace(dev, wsb, &ws);
     if (rc) return rc;
   }
+  trace_call_begin(st);
   const int64_t CP2 = s.CP2;
   const int64_t pairs = s.B * s.L * CP2;  // complex elements per tensor
   const int in_kind = s.dtype == SPECTRE_F32 ? IN_F32 : IN_BF16;
@@ -688,6 +737,62 @@ int spectre_mix_release(void) {
   }
   g_dev.clear();
   if (have_cur) (void)hipSetDevice(cur);
+  return rc;
+}
+
+int spectre_mix_trace_start(int max_calls) {
+  if (max_calls < 1 || max_calls > 100000) return SPECTRE_EINVAL;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_trace.on) return SPECTRE_EINVAL;
+  const size_t n = (size_t)max_calls * (kMaxKernelsPerCall + 1);
+  g_trace = TraceState();
+  g_trace.pool.resize(n);
+  for (size_t i = 0; i < n; ++i) {
+    if (hipEventCreate(&g_trace.pool[i]) != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(g_trace.pool[j]);
+      g_trace = TraceState();
+      return SPECTRE_EHIP;
+    }
+  }
+  g_trace.on = true;
+  g_trace.max_calls = max_calls;
+  return SPECTRE_OK;
+}
+
+int spectre_mix_trace_stop(int max_kernels, float* total_ms, int* n_kernels, int* n_calls,
+                           char* names, int name_len) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_trace.on) return SPECTRE_EINVAL;
+  int rc = SPECTRE_OK;
+  const int nk = g_trace.calls.empty() ? 0 : g_trace.calls[0].nk;
+  for (const TraceCall& c : g_trace.calls)
+    if (c.nk != nk) rc = SPECTRE_EINVAL;
+  if (g_trace.used > 0 && hipEventSynchronize(g_trace.pool[g_trace.used - 1]) != hipSuccess)
+    rc = SPECTRE_EHIP;
+  if (rc == SPECTRE_OK) {
+    if (nk > max_kernels || !total_ms || !n_kernels || !n_calls) {
+      rc = SPECTRE_EINVAL;
+    } else {
+      for (int k = 0; k < nk; ++k) total_ms[k] = 0.f;
+      for (const TraceCall& c : g_trace.calls)
+        for (int k = 0; k < nk; ++k) {
+          float ms = 0.f;
+          if (hipEventElapsedTime(&ms, g_trace.pool[c.first + k], g_trace.pool[c.first + k + 1]) !=
+              hipSuccess)
+            rc = SPECTRE_EHIP;
+          total_ms[k] += ms;
+        }
+      *n_kernels = nk;
+      *n_calls = (int)g_trace.calls.size();
+      if (names && name_len > 0 && !g_trace.calls.empty())
+        for (int k = 0; k < nk; ++k) {
+          std::strncpy(names + (size_t)k * name_len, g_trace.calls[0].names[k], name_len - 1);
+          names[(size_t)k * name_len + name_len - 1] = 0;
+        }
+    }
+  }
+  for (hipEvent_t e : g_trace.pool) (void)hipEventDestroy(e);
+  g_trace = TraceState();
   return rc;
 }
 

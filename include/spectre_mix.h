@@ -45,7 +45,8 @@
  * Supported shapes
  * ----------------
  *  B, H, D >= 1; H*D even and at most 4096; L even, L = 2^a * 3^b with
- *  b <= 3 and 2 <= L <= 3 * 2^20 (longer or other lengths: SPECTRE_EUNSUPPORTED);
+ *  b <= 1 and 2 <= L <= 3 * 2^20 (other lengths: SPECTRE_EUNSUPPORTED; odd L:
+ *  SPECTRE_EINVAL);
  *  0 <= keep_bins <= L/2 + 1 (keep_bins = L/2 + 1: no truncation;
  *  keep_bins = 0: y = 0, out = LayerNorm(x)).  B*L*H*D must be below 2^40.
  */
@@ -112,6 +113,23 @@ int spectre_mix_plan(int64_t L, int64_t* l1, int64_t* l2, int64_t* l3);
  * Later calls recreate what they need.  Returns SPECTRE_OK or SPECTRE_EHIP.
  */
 int spectre_mix_release(void);
+
+/*
+ * Per-kernel timing with HIP events (tracing).  After spectre_mix_trace_start,
+ * each of the next `max_calls` calls to spectre_mix_fwd / spectre_mix_y also
+ * records a HIP event on its own stream before its first kernel and after
+ * each kernel it enqueues; nothing synchronises.  spectre_mix_trace_stop
+ * waits for those events, stops tracing, and reports per position k of the
+ * calls' launch sequence: total_ms[k] = summed duration over the traced
+ * calls, names[k * name_len ...] = the kernel's short NUL-terminated name;
+ * *n_kernels = kernels per call, *n_calls = calls traced.  Every traced call
+ * must have the same shape (else SPECTRE_EINVAL).  Events are created by
+ * start and destroyed by stop.  Returns SPECTRE_OK, SPECTRE_EINVAL or
+ * SPECTRE_EHIP.
+ */
+int spectre_mix_trace_start(int max_calls);
+int spectre_mix_trace_stop(int max_kernels, float* total_ms, int* n_kernels, int* n_calls,
+                           char* names, int name_len);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* spectre_mix_strerror(int status);
