@@ -54,6 +54,26 @@ __device__ __forceinline__ float2 load_pair(const void* base, int64_t off) {
   }
 }
 
+// Element size of one channel pair in storage kind IN, in bytes.
+template <int IN>
+constexpr int pair_bytes() {
+  return IN == IN_BF16 ? 4 : 8;
+}
+
+// One channel pair at `ubase + off` bytes, where `ubase` is uniform across
+// the wave and `off` a 32-bit per-lane offset: this is the scalar-base +
+// vector-offset addressing form, so a row of R such loads costs scalar adds
+// for the bases and one shared offset register.
+template <int IN>
+__device__ __forceinline__ float2 load_pair_u(const char* ubase, uint32_t off) {
+  if constexpr (IN == IN_BF16) {
+    uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ubase + off));
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float2*>(ubase + off);
+  }
+}
+
 // binary32 -> bfloat16 bits, round to nearest even, NaN kept quiet.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -347,6 +367,203 @@ __global__ __launch_bounds__(512) void k_mid(MidParams p) {
     float2 w = v[i];
     if (tw_mul != 0 && m3 != 0) w = cmul(w, twiddle_lookup(p.twL, m3 * tw_mul, true));
     p.out[gbase + (int64_t)m3 * p.CP2] = w;
+  }
+}
+
+// -------------------------------- B for N = R * R: two register DFTs
+//
+// The same pass as k_mid, specialised for column length N = R^2 (R = 16 or
+// 32).  Each transform is an R-point DFT in registers, one padded LDS
+// transpose, and a second R-point DFT in registers (the four-step split of
+// N itself), so a transform costs one LDS round trip and every index is a
+// compile-time constant.
+//
+//   stage 1 (coalesced mapping: thread (t, col), column fastest):
+//     v[k] = sum_i x[t + R i] w_R^{ik} * w_N^{t k}          -> LDS [k][t][col]
+//   stage 2 (mirror mapping: R lanes per column, the two columns of a pair
+//   in one wave): thread k1 reads [k1][t][col] and gets X[k1 + R k2], k2 < R.
+//
+// The mirror bin of (k1, k2) is held by a lane of the same wave: for a
+// column and its mirror column it is lane (other slot, R-1-k1) at k2' = R-1-k2;
+// inside column (0, 0) it is lane (R - k1) mod R (k2' = R-1-k2, or (R-k2) mod R
+// when k1 = 0); inside the other self-paired column lane R-1-k1.  Each lane
+// pulls its partner's upper half (k2 >= R/2) with ds_bpermute and owns the
+// R/2 pairs whose own element has k2 < R/2 (lane k1 = 0 of column (0, 0)
+// owns its pairs alone, plus the self-mirrored bin k2 = R/2).
+//
+// The inverse runs the split backwards: stage-2 lanes transform along k2,
+// twiddle w_N^{-k1 n}, LDS transpose, stage-1 lanes transform along k1 and
+// hold z[t + R i] -- the input distribution -- for coalesced stores.
+
+__device__ __forceinline__ float lane_pull(float v, int src_byte) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_byte, __float_as_int(v)));
+}
+__device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
+  return make_float2(lane_pull(v.x, src_byte), lane_pull(v.y, src_byte));
+}
+
+template <int R, int IN>
+__global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
+  constexpr int N = R * R;
+  constexpr int H2 = R / 2;
+  extern __shared__ float2 lds[];
+  const int ncols = p.nslot * p.cpt;
+  const int ROW = R * ncols + 1;  // padded: stage-2 lanes stride ROW, an odd count
+  const int tid = threadIdx.x;
+
+  // stage-1 / stage-3 identity
+  const int col1 = tid % ncols;
+  const int t1 = tid / ncols;
+  const int s1 = col1 / p.cpt;
+  const int j1 = col1 - s1 * p.cpt;
+  // stage-2 identity
+  const int G = p.nslot * R;
+  const int j2 = tid / G;
+  const int r2 = tid - j2 * G;
+  const int s2 = r2 / R;
+  const int k1 = r2 - s2 * R;
+  const int col2 = s2 * p.cpt + j2;
+
+  const int2 cols = p.wgcols[blockIdx.x];
+  const bool regular = p.nslot == 2 && (int)blockIdx.x != p.selfwg;
+  int ps, pk1;
+  bool a_zero = false;
+  if (regular) {
+    ps = 1 - s2;
+    pk1 = R - 1 - k1;
+  } else {
+    ps = s2;
+    a_zero = s2 == 0;
+    pk1 = a_zero ? (R - k1) % R : R - 1 - k1;
+  }
+  const int partner_byte = (((j2 * G + ps * R + pk1) & 63) << 2);
+  const bool special = a_zero && k1 == 0;
+
+  const int b = blockIdx.z;
+  const int colid1 = s1 == 0 ? cols.x : cols.y;
+  const int colid2 = s2 == 0 ? cols.x : cols.y;
+  const bool active1 = colid1 >= 0;
+  const int kc1 = active1 ? colid1 % p.L1 : 0, k2c1 = active1 ? colid1 / p.L1 : 0;
+  const int kc2 = colid2 >= 0 ? colid2 % p.L1 : 0, k2c2 = colid2 >= 0 ? colid2 / p.L1 : 0;
+  const int cp1 = blockIdx.y * p.cpt + j1;
+  const int cp2 = blockIdx.y * p.cpt + j2;
+  // element i of this stage-1 lane's column sits at pair index
+  //   b * L * CP2 + lane_pair + i * R * CP2
+  const uint32_t lane_pair = (uint32_t)((kc1 * p.M + k2c1 * N + t1) * p.CP2 + cp1);
+  const int64_t batch_pair = (int64_t)b * p.L * p.CP2;
+  const int64_t row_pair = (int64_t)R * p.CP2;
+  // bin of element (k1, k2) of the stage-2 column: fbase + fstep * k2
+  const int fbase = kc2 + p.L1 * (k2c2 + p.L2 * k1);
+  const int fstep = p.L1 * p.L2 * R;
+  const int ha = (2 * cp2) / p.D, hb = (2 * cp2 + 1) / p.D;
+
+  float2 v[R];
+  float2 sa[H2 + 1], sb[H2 + 1];
+
+#pragma unroll 1
+  for (int x = 0; x < 3; ++x) {
+    // values only one phase needs are made opaque per iteration, so they are
+    // not hoisted out of the loop and kept live across it
+    const float* gate = p.gate;
+    const float2* twn = p.twN;
+    int fb = fbase;
+    asm volatile("" : "+s"(gate), "+s"(twn), "+v"(fb));
+    // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
+    {
+      const char* src = reinterpret_cast<const char*>(p.in[x]) + batch_pair * pair_bytes<IN>();
+      const uint32_t off = lane_pair * pair_bytes<IN>();
+      if (active1) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = load_pair_u<IN>(src + i * row_pair * pair_bytes<IN>(), off);
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
+      }
+    }
+    dft<R, -1>(v);
+#pragma unroll
+    for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twiddle_lookup(twn, t1 * k, false));
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < R; ++k) lds[k * ROW + t1 * ncols + col1] = v[k];
+    __syncthreads();
+    // ---- stage 2: DFT over t -> X[k1 + R k2]
+#pragma unroll
+    for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * ncols + col2];
+    dft<R, -1>(v);
+
+    // ---- split the packed spectra and accumulate / finish the product.
+    // The mirror bin of this lane's k2 = u < R/2 is the partner lane's
+    // k2 = R-1-u (pulled with ds_bpermute); lane k1 = 0 of column (0, 0)
+    // holds its own mirrors at (R-u) mod R and the self-mirrored bin R/2.
+    // 2A = Z[f] + conj Z[L-f], 2B = -i (Z[f] - conj Z[L-f]).
+    // After v, sa holds W[f] = Oa + i Ob and sb W[L-f] = conj(Oa) + i conj(Ob).
+    auto mirror = [&](int u) -> float2 {
+      if (u == H2) return v[H2];
+      const float2 pulled = lane_pull2(v[R - 1 - u], partner_byte);
+      return special ? v[(R - u) % R] : pulled;
+    };
+    if (x == 0) {
+#pragma unroll
+      for (int u = 0; u <= H2; ++u) {
+        const float2 z = v[u], zm = mirror(u);
+        sa[u] = make_float2(z.x + zm.x, z.y - zm.y);
+        sb[u] = make_float2(z.y + zm.y, zm.x - z.x);
+      }
+    } else if (x == 1) {
+#pragma unroll
+      for (int u = 0; u <= H2; ++u) {
+        const float2 z = v[u], zm = mirror(u);
+        sa[u] = cmulc(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+        sb[u] = cmulc(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u <= H2; ++u) {
+        const float2 z = v[u], zm = mirror(u);
+        const int f = fb + fstep * u;
+        const int fc = min(f, p.L - f);
+        const bool kept = fc < p.keep;
+        const int gi = kept ? fc : 0;  // bins at or above keep_bins only ever give 0
+        const float ga = kept ? gate[ha * p.nbins + gi] * p.scale : 0.f;
+        const float gb = kept ? gate[hb * p.nbins + gi] * p.scale : 0.f;
+        const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), ga);
+        const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), gb);
+        sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
+        sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
+      }
+    }
+  }
+  // ---- W back into this lane's own bins k2 = 0 .. R-1
+#pragma unroll
+  for (int u = 0; u < H2; ++u) v[u] = sa[u];
+#pragma unroll
+  for (int q = 0; q < H2; ++q) {
+    const float2 pulled = lane_pull2(sb[H2 - 1 - q], partner_byte);
+    v[H2 + q] = special ? (q == 0 ? sa[H2] : sb[H2 - q]) : pulled;
+  }
+
+  // ---- inverse, stage 2 lanes: along k2, twiddle w_N^{-k1 n}
+  dft<R, +1>(v);
+#pragma unroll
+  for (int n = 1; n < R; ++n) v[n] = cmul(v[n], twiddle_lookup(p.twN, k1 * n, true));
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < R; ++n) lds[k1 * ROW + n * ncols + col2] = v[n];
+  __syncthreads();
+  // ---- inverse, stage 1 lanes: along k1 -> z[t + R i], twiddle, store
+#pragma unroll
+  for (int k = 0; k < R; ++k) v[k] = lds[k * ROW + t1 * ncols + col1];
+  dft<R, +1>(v);
+  if (!active1) return;
+  const int tw_mul = p.L1 * k2c1 + (p.L2 == 1 ? kc1 : 0);
+  char* dst = reinterpret_cast<char*>(p.out) + batch_pair * 8;
+  const uint32_t off = lane_pair * 8;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int m3 = t1 + R * i;
+    *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) =
+        cmul(v[i], twiddle_lookup(p.twL, m3 * tw_mul, true));
   }
 }
 

@@ -33,6 +33,7 @@ constexpr int kLdsBudget = 64 * 1024;  // bytes of LDS per B workgroup
 
 struct Plan {
   int64_t L = 0, L1 = 1, L2 = 1, L3 = 1;
+  int sq = 0;  // R when L3 = R * R uses the two-register-DFT B kernel (R = 16, 32), else 0
   int P = 0;   // points per thread in B
   int Tc = 0;  // threads per column in B
   int nrad = 0;
@@ -112,6 +113,8 @@ int make_plan(int64_t L, Plan& pl) {
     pl.P = (int)std::min<int64_t>(16, N);
   pl.Tc = (int)(N / pl.P);
   if (!plan_radices(N, pl.P, pl)) return SPECTRE_EUNSUPPORTED;
+  if (N == 1024) pl.sq = 32;
+  if (N == 256) pl.sq = 16;
   return SPECTRE_OK;
 }
 
@@ -129,6 +132,13 @@ int choose_cpt(const Plan& pl, int64_t CP2, int nslot) {
     if (next > 16) break;
     cpt = next;
   }
+  return cpt;
+}
+
+// Channel pairs per slot for the square B kernel: 256 threads when possible.
+int choose_cpt_sq(int R, int64_t CP2, int nslot) {
+  int cpt = 256 / (R * nslot);
+  while (cpt > 1 && CP2 % cpt != 0) cpt /= 2;
   return cpt;
 }
 
@@ -341,6 +351,7 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   if (H > kMaxC || D > kMaxC || H * D > kMaxC) return SPECTRE_EUNSUPPORTED;
   const int64_t C = H * D;
   if (C % 2 != 0) return SPECTRE_EUNSUPPORTED;
+  if (L * C >= (int64_t(1) << 29)) return SPECTRE_EUNSUPPORTED;  // 32-bit byte offsets per batch
   if (B > (int64_t(1) << 40) / (L * C)) return SPECTRE_EUNSUPPORTED;
   int st = make_plan(L, pl);
   if (st != SPECTRE_OK) return st;
@@ -433,6 +444,29 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
   hipLaunchKernelGGL((k_mid<P, IN>), grid, dim3(threads), lds, st, p);
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
   return SPECTRE_OK;
+}
+
+template <int R, int IN>
+int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
+  const int ncols = p.nslot * p.cpt;
+  const size_t lds = (size_t)R * (R * ncols + 1) * sizeof(float2);
+  static bool attr_set = false;  // guarded by g_mu
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_sq<R, IN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return SPECTRE_EHIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_mid_sq<R, IN>), grid, dim3(R * ncols), lds, st, p);
+  SPECTRE_LAUNCH_CHECK("B_mid_lds");
+  return SPECTRE_OK;
+}
+
+template <int IN>
+int launch_mid_square(int R, const MidParams& p, dim3 grid, hipStream_t st) {
+  if (R == 32) return launch_mid_sq<32, IN>(p, grid, st);
+  if (R == 16) return launch_mid_sq<16, IN>(p, grid, st);
+  return SPECTRE_EUNSUPPORTED;
 }
 
 template <int IN>
@@ -548,7 +582,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   {
     MidParams m{};
     const int nslot = single ? 1 : 2;
-    const int cpt = choose_cpt(pl, CP2, nslot);
+    const int cpt = pl.sq ? choose_cpt_sq(pl.sq, CP2, nslot) : choose_cpt(pl, CP2, nslot);
     if (single) {
       m.in[0] = q;
       m.in[1] = k;
@@ -581,12 +615,20 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     dim3 grid((unsigned)tab->nwg, (unsigned)(CP2 / cpt), (unsigned)s.B);
     const int threads = pl.Tc * nslot * cpt;
     const int kind = single ? in_kind : IN_C32;
-    if (kind == IN_F32)
+    if (pl.sq) {
+      if (kind == IN_F32)
+        rc = launch_mid_square<IN_F32>(pl.sq, m, grid, st);
+      else if (kind == IN_BF16)
+        rc = launch_mid_square<IN_BF16>(pl.sq, m, grid, st);
+      else
+        rc = launch_mid_square<IN_C32>(pl.sq, m, grid, st);
+    } else if (kind == IN_F32) {
       rc = launch_mid<IN_F32>(pl.P, m, grid, threads, st);
-    else if (kind == IN_BF16)
+    } else if (kind == IN_BF16) {
       rc = launch_mid<IN_BF16>(pl.P, m, grid, threads, st);
-    else
+    } else {
       rc = launch_mid<IN_C32>(pl.P, m, grid, threads, st);
+    }
     if (rc) return rc;
   }
 

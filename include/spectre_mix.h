@@ -25,7 +25,7 @@
  *    stored as 16-bit patterns, rounded to nearest-even on output).  All
  *    arithmetic is binary32.
  *  - gate: [H][L/2 + 1] binary32, a real multiplier per (head, bin), shared
- *    over b and d.  Bins at or above keep_bins are never read.
+ *    over b and d.  Values at bins at or above keep_bins are ignored.
  *  - gamma, beta: [H*D] binary32.
  *  - All tensor pointers are DEVICE pointers on the current HIP device and
  *    must be 16-byte aligned.  The caller owns them; the library never frees
@@ -48,7 +48,8 @@
  *  b <= 1 and 2 <= L <= 3 * 2^20 (other lengths: SPECTRE_EUNSUPPORTED; odd L:
  *  SPECTRE_EINVAL);
  *  0 <= keep_bins <= L/2 + 1 (keep_bins = L/2 + 1: no truncation;
- *  keep_bins = 0: y = 0, out = LayerNorm(x)).  B*L*H*D must be below 2^40.
+ *  keep_bins = 0: y = 0, out = LayerNorm(x)).  L*H*D must be below 2^29 (one
+ *  batch element's q spectrum under 4 GiB) and B*L*H*D below 2^40.
  */
 #ifndef SPECTRE_MIX_H
 #define SPECTRE_MIX_H
