@@ -150,6 +150,51 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
   }
 }
 
+// Forward strided pass with the R-point DFT split over two lanes (l, l^32):
+// lane half h loads the samples r = 2a + h (a < R/2) and transforms them
+// (R/2 points); the halves trade results with a lane permute and finish
+// with a radix-2 step, X[k] = E0[k] + w_R^k E1[k] on half 0 and
+// X[k + R/2] = E0[k] - w_R^k E1[k] on half 1.  Half the registers of the
+// one-lane form, so more waves hide the memory latency.  A wave covers 32
+// consecutive lines; both lanes of a line are active or neither is.
+template <int R, int IN, int TW>
+__global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
+  constexpr int R2 = R / 2;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int64_t line = (((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6) * 32 + (lane & 31);
+  const int64_t lines = p.outer * p.inner * p.CP2;
+  if (line >= lines) return;
+  const int64_t cp = line % p.CP2;
+  const int64_t t = line / p.CP2;
+  const int i = (int)(t % p.inner);
+  const int64_t o = t / p.inner;
+  const int64_t step = p.inner * p.CP2;  // pairs between rows r and r + 1
+  const int64_t base = (o * R * p.inner + i) * p.CP2 + cp;
+  const char* in = reinterpret_cast<const char*>(p.in[blockIdx.y]) + (base + h * step) * pair_bytes<IN>();
+  char* out = reinterpret_cast<char*>(p.out[blockIdx.y]) + (base + h * R2 * step) * 8;
+
+  float2 e[R2];
+#pragma unroll
+  for (int a = 0; a < R2; ++a) {
+    e[a] = load_pair_u<IN>(in, (uint32_t)0);
+    in += 2 * step * pair_bytes<IN>();
+  }
+  dft<R2, -1>(e);
+#pragma unroll
+  for (int k = 0; k < R2; ++k) {
+    const float2 mine = e[k];
+    const float2 other = make_float2(__shfl_xor(mine.x, 32, 64), __shfl_xor(mine.y, 32, 64));
+    const float2 e0 = h ? other : mine;
+    const float2 e1 = twiddle_ct<R, -1>(h ? mine : other, k);
+    float2 xk = h ? csub(e0, e1) : cadd(e0, e1);
+    const int k1 = k + R2 * h;
+    if constexpr (TW == TW_A1) xk = cmul(xk, twiddle_lookup(p.twL, i * k1, false));
+    if constexpr (TW == TW_A2) xk = cmul(xk, twiddle_lookup(p.twL, i * k1 * p.L1, false));
+    *reinterpret_cast<float2*>(out + (int64_t)k * step * 8) = xk;
+  }
+}
+
 // ------------------------------------------- B: LDS Stockham + spectral mix
 
 struct MidParams {

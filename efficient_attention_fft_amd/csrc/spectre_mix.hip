@@ -394,6 +394,19 @@ int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t 
   return SPECTRE_OK;
 }
 
+template <int R, int IN>
+int launch_strided_fwd_split(const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+  const int64_t lines = p.outer * p.inner * p.CP2;
+  const int64_t waves = (lines + 31) / 32;
+  dim3 grid((unsigned)((waves + 3) / 4), ntensor);
+  if (tw == TW_A1)
+    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A2>), grid, dim3(256), 0, st, p);
+  SPECTRE_LAUNCH_CHECK(tw == TW_A1 ? "A1_fwd_strided" : "A2_fwd_strided");
+  return SPECTRE_OK;
+}
+
 template <int IN>
 int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStream_t st) {
   switch (R) {
@@ -406,8 +419,8 @@ int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStrea
     case 16: return launch_strided_fwd<16, IN>(p, tw, ntensor, st);
     case 24: return launch_strided_fwd<24, IN>(p, tw, ntensor, st);
     case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st);
-    case 48: return launch_strided_fwd<48, IN>(p, tw, ntensor, st);
-    case 64: return launch_strided_fwd<64, IN>(p, tw, ntensor, st);
+    case 48: return launch_strided_fwd_split<48, IN>(p, tw, ntensor, st);
+    case 64: return launch_strided_fwd_split<64, IN>(p, tw, ntensor, st);
     default: return SPECTRE_EUNSUPPORTED;
   }
 }
