@@ -25,6 +25,9 @@ Other modes (used to produce the files under profiles/):
                          known-size device copy for counter calibration
     --summarize DIR ...  turn rocprofv3 output directories into the text
                          summaries kept under profiles/
+    --write-counters FETCH_DIR WRITE_DIR
+                         write profiles/hbm_counters.json from a FETCH_SIZE
+                         and a WRITE_SIZE run of --profile-run
 """
 from __future__ import annotations
 
@@ -234,19 +237,23 @@ def _read_csv(path):
 
 
 def _short(name: str) -> str:
-    for key, short in (("k_strided", None), ("k_mid", "B_mid_lds"), ("k_final", None),
-                       ("k_layernorm", "LN_norm")):
-        if key in name:
-            if short:
-                return short
-            if key == "k_strided":
-                if "1, -1" in name or "ILi1ELin1E" in name:
-                    return "A1_fwd_strided"
-                if "2, -1" in name or "ILi2ELin1E" in name:
-                    return "A2_fwd_strided"
-                return "C2_inv_strided"
-            if key == "k_final":
-                return "C1_inv_norm" if "true" in name or "Lb1E" in name else "C1_inv"
+    """Pass name of a library kernel from its demangled name (template
+    arguments: k_strided<R, IN, TW, SIGN>, k_strided_split<R, IN, TW>,
+    k_final<R, DT, FUSE>); other kernels keep their own name."""
+    import re
+    m = re.search(r"spectre::(k_\w+)<([^>]*)>", name)
+    if not m:
+        return "copy (calibration)" if "copyBuffer" in name else name[:60]
+    kern, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    if kern in ("k_strided", "k_strided_split"):
+        return {"1": "A1_fwd_strided", "2": "A2_fwd_strided", "3": "C2_inv_strided"}.get(
+            args[2], name[:60])
+    if kern.startswith("k_mid"):
+        return "B_mid_lds"
+    if kern == "k_final":
+        return "C1_inv_norm" if args[2] == "true" else "C1_inv"
+    if kern == "k_layernorm":
+        return "LN_norm"
     return name[:60]
 
 
@@ -282,6 +289,53 @@ def summarize(dirs, out_json=None):
     return "\n".join(lines), stats, counters
 
 
+def write_counters(fetch_dir, write_dir, workload_id):
+    """profiles/hbm_counters.json from one FETCH_SIZE and one WRITE_SIZE
+    rocprofv3 --pmc run of `bench.py --profile-run`: per kernel, the mean KiB
+    per dispatch of each counter times the factor that maps the calibration
+    copy's reading onto its known size (1 GiB read, 1 GiB written)."""
+    import workloads
+    w = workloads.WORKLOADS[workload_id]
+    _, _, fc = summarize([fetch_dir])
+    _, _, wc = summarize([write_dir])
+
+    def per_kernel(counters, cname):
+        out, copy = {}, None
+        for (nm, cn), vals in counters.items():
+            if cn != cname:
+                continue
+            kib = sum(vals) / len(vals)
+            if "copyBuffer" in nm:
+                big = max(vals)  # the 1 GiB copy is the largest copyBuffer dispatch
+                copy = big if copy is None else max(copy, big)
+            elif "spectre::" in nm:
+                out[_short(nm)] = kib
+        return out, copy
+
+    fetch, fcopy = per_kernel(fc, "FETCH_SIZE")
+    write, wcopy = per_kernel(wc, "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("no calibration copy found in the counter runs")
+    ff = COPY_BYTES / (fcopy * 1024.0)
+    wf = COPY_BYTES / (wcopy * 1024.0)
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        rd = fetch.get(k, 0.0) * 1024.0 * ff
+        wr = write.get(k, 0.0) * 1024.0 * wf
+        kernels[k] = {"fetch_kib": round(fetch.get(k, 0.0), 1), "write_kib": round(write.get(k, 0.0), 1),
+                      "read_bytes": int(rd), "write_bytes": int(wr),
+                      "hbm_bytes_per_launch": int(rd + wr),
+                      "algorithmic_bytes": kernel_bytes(k, w)}
+    doc = {"workload": w.name, "source_hash": source_hash(),
+           "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fcopy, "write_kib": wcopy,
+                                "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": kernels}
+    with open(COUNTERS, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    return doc
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +345,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.write_counters:
+        print(json.dumps(write_counters(*args.write_counters, args.workload), indent=1))
+        return 0
     if args.summarize:
         text, _, _ = summarize(args.summarize)
         print(text)
