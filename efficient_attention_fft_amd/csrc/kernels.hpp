@@ -321,20 +321,35 @@ __device__ __forceinline__ bool pair_at(int i, int P, int s, int tc, int Tc, int
   return false;
 }
 
+// Work-group ids go to the 8 XCDs round-robin (id mod 8), each XCD with its
+// own L2.  Renumbered so that XCD x runs a contiguous eighth of the grid in
+// its natural order, the work-groups that share cache lines (neighbouring
+// channel-pair blocks of one column) share an L2 and run close in time.  A
+// tail beyond a multiple of 8 keeps its own ids.
+__device__ __forceinline__ int3 xcd_grouped_block() {
+  const unsigned gx = gridDim.x, gy = gridDim.y;
+  const unsigned total = gx * gy * gridDim.z;
+  unsigned lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const unsigned per = total / 8;
+  if (lin < per * 8) lin = (lin % 8) * per + lin / 8;
+  return make_int3((int)(lin % gx), (int)((lin / gx) % gy), (int)(lin / (gx * gy)));
+}
+
 template <int P, int IN>
 __global__ __launch_bounds__(512) void k_mid(MidParams p) {
   extern __shared__ float2 lds[];
+  const int3 blk = xcd_grouped_block();
   const int ncols = p.nslot * p.cpt;
   const int tid = threadIdx.x;
   const int col = tid % ncols;
   const int tc = tid / ncols;
   const int s = col / p.cpt;
   const int j = col - s * p.cpt;
-  const int cp = blockIdx.y * p.cpt + j;
-  const int b = blockIdx.z;
-  const int2 cols = p.wgcols[blockIdx.x];
+  const int cp = blk.y * p.cpt + j;
+  const int b = blk.z;
+  const int2 cols = p.wgcols[blk.x];
   const int my_col = s == 0 ? cols.x : cols.y;
-  const bool regular = p.nslot == 2 && (int)blockIdx.x != p.selfwg;
+  const bool regular = p.nslot == 2 && blk.x != p.selfwg;
   const bool active = my_col >= 0;
   const int k1 = active ? my_col % p.L1 : 0;
   const int k2 = active ? my_col / p.L1 : 0;
@@ -448,12 +463,15 @@ __device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
 }
 
 template <int R, int IN>
-__global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
+__global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int N = R * R;
   constexpr int H2 = R / 2;
   extern __shared__ float2 lds[];
+  const int3 blk = p.nslot == 1 ? xcd_grouped_block()
+                                : make_int3((int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
   const int ncols = p.nslot * p.cpt;
   const int ROW = R * ncols + 1;  // padded: stage-2 lanes stride ROW, an odd count
+  float2* twl = lds + R * ROW;     // the N-point twiddles, copied from p.twN
   const int tid = threadIdx.x;
 
   // stage-1 / stage-3 identity
@@ -469,8 +487,8 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
   const int k1 = r2 - s2 * R;
   const int col2 = s2 * p.cpt + j2;
 
-  const int2 cols = p.wgcols[blockIdx.x];
-  const bool regular = p.nslot == 2 && (int)blockIdx.x != p.selfwg;
+  const int2 cols = p.wgcols[blk.x];
+  const bool regular = p.nslot == 2 && blk.x != p.selfwg;
   int ps, pk1;
   bool a_zero = false;
   if (regular) {
@@ -484,14 +502,14 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
   const int partner_byte = (((j2 * G + ps * R + pk1) & 63) << 2);
   const bool special = a_zero && k1 == 0;
 
-  const int b = blockIdx.z;
+  const int b = blk.z;
   const int colid1 = s1 == 0 ? cols.x : cols.y;
   const int colid2 = s2 == 0 ? cols.x : cols.y;
   const bool active1 = colid1 >= 0;
   const int kc1 = active1 ? colid1 % p.L1 : 0, k2c1 = active1 ? colid1 / p.L1 : 0;
   const int kc2 = colid2 >= 0 ? colid2 % p.L1 : 0, k2c2 = colid2 >= 0 ? colid2 / p.L1 : 0;
-  const int cp1 = blockIdx.y * p.cpt + j1;
-  const int cp2 = blockIdx.y * p.cpt + j2;
+  const int cp1 = blk.y * p.cpt + j1;
+  const int cp2 = blk.y * p.cpt + j2;
   // element i of this stage-1 lane's column sits at pair index
   //   b * L * CP2 + lane_pair + i * R * CP2
   const uint32_t lane_pair = (uint32_t)((kc1 * p.M + k2c1 * N + t1) * p.CP2 + cp1);
@@ -510,9 +528,9 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
     // values only one phase needs are made opaque per iteration, so they are
     // not hoisted out of the loop and kept live across it
     const float* gate = p.gate;
-    const float2* twn = p.twN;
     int fb = fbase;
-    asm volatile("" : "+s"(gate), "+s"(twn), "+v"(fb));
+    int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
+    asm volatile("" : "+s"(gate), "+v"(fb), "+v"(t1o));
     // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
     {
       const char* src = reinterpret_cast<const char*>(p.in[x]) + batch_pair * pair_bytes<IN>();
@@ -525,9 +543,13 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
         for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
       }
     }
+    if (x == 0) {
+      for (int e = tid; e < N; e += R * ncols) twl[e] = p.twN[e];
+      __syncthreads();
+    }
     dft<R, -1>(v);
 #pragma unroll
-    for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twiddle_lookup(twn, t1 * k, false));
+    for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twl[t1o * k]);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < R; ++k) lds[k * ROW + t1 * ncols + col1] = v[k];
@@ -589,9 +611,11 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
   }
 
   // ---- inverse, stage 2 lanes: along k2, twiddle w_N^{-k1 n}
+  int k1o = k1;
+  asm volatile("" : "+v"(k1o));
   dft<R, +1>(v);
 #pragma unroll
-  for (int n = 1; n < R; ++n) v[n] = cmul(v[n], twiddle_lookup(p.twN, k1 * n, true));
+  for (int n = 1; n < R; ++n) v[n] = cmul(v[n], cconj(twl[k1o * n]));
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < R; ++n) lds[k1 * ROW + n * ncols + col2] = v[n];
@@ -599,16 +623,26 @@ __global__ __launch_bounds__(256) void k_mid_sq(MidParams p) {
   // ---- inverse, stage 1 lanes: along k1 -> z[t + R i], twiddle, store
 #pragma unroll
   for (int k = 0; k < R; ++k) v[k] = lds[k * ROW + t1 * ncols + col1];
+  // output twiddle w^-(m3 tw_mul), w = w_L, for m3 = t1 + R i, i = 4 a + j:
+  // the seeds w^(t1 + R j), j < 4, times (w^(4 R))^a
+  const int tw_mul = p.L1 * k2c1 + (p.L2 == 1 ? kc1 : 0);
+  float2 tws[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tws[j] = p.twL[(t1 + R * j) * tw_mul];
+  const float2 tw4r = p.twL[4 * R * tw_mul];
   dft<R, +1>(v);
   if (!active1) return;
-  const int tw_mul = p.L1 * k2c1 + (p.L2 == 1 ? kc1 : 0);
   char* dst = reinterpret_cast<char*>(p.out) + batch_pair * 8;
   const uint32_t off = lane_pair * 8;
+  float2 step = make_float2(1.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int m3 = t1 + R * i;
-    *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) =
-        cmul(v[i], twiddle_lookup(p.twL, m3 * tw_mul, true));
+  for (int a = 0; a < R / 4; ++a) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * a + j;
+      *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) = cmul(v[i], cconj(cmul(tws[j], step)));
+    }
+    step = cmul(step, tw4r);
   }
 }
 

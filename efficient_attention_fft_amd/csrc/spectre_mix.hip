@@ -462,7 +462,7 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
 template <int R, int IN>
 int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
   const int ncols = p.nslot * p.cpt;
-  const size_t lds = (size_t)R * (R * ncols + 1) * sizeof(float2);
+  const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2);
   static bool attr_set = false;  // guarded by g_mu
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_sq<R, IN>),
