@@ -156,23 +156,51 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
 // with a radix-2 step, X[k] = E0[k] + w_R^k E1[k] on half 0 and
 // X[k + R/2] = E0[k] - w_R^k E1[k] on half 1.  Half the registers of the
 // one-lane form, so more waves hide the memory latency.  A wave covers 32
-// consecutive lines; both lanes of a line are active or neither is.
-template <int R, int IN, int TW>
+// lines; both lanes of a line are active or neither is.
+//
+// Row output (TILED = false): a wave's 32 lines are 32 consecutive pairs of
+// one row, written back to the same positions ([outer][R][inner][CP2]).
+// Tiled output (TILED = true, used for the first pass of a two-level plan):
+// the outputs of row block r go to [outer][r][CP2 / 4][inner][4], so that
+// the LDS pass finds the inner rows of 4 channel pairs contiguous.  A wave
+// covers RW rows x 32 / RW pairs and a workgroup 4 RW consecutive rows:
+// binary32 inputs use RW = 2 (reads: 128-byte row pieces; writes: 8 rows x
+// 4 pairs = 256 contiguous bytes per block over the 4 waves), bfloat16
+// inputs RW = 1 (reads: 32 pairs = 128 bytes of one row; writes: 4 rows x
+// 4 pairs = 128 bytes per block).  Needs inner % 8 == 0 and CP2 % 32 == 0.
+template <int R, int IN, int TW, bool TILED>
 __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
   constexpr int R2 = R / 2;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
-  const int64_t line = (((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6) * 32 + (lane & 31);
-  const int64_t lines = p.outer * p.inner * p.CP2;
-  if (line >= lines) return;
-  const int64_t cp = line % p.CP2;
-  const int64_t t = line / p.CP2;
-  const int i = (int)(t % p.inner);
-  const int64_t o = t / p.inner;
+  const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // global wave
+  int64_t cp, o;
+  int i;
+  if constexpr (TILED) {
+    constexpr int RW = IN == IN_BF16 ? 1 : 2;  // rows per wave
+    constexpr int PW = 32 / RW;                // pairs per wave
+    const int c = lane & 31;
+    const int64_t g = gw >> 2;
+    const int64_t pgs = p.CP2 / PW, tiles = (p.inner / (4 * RW)) * pgs;
+    o = g / tiles;
+    if (o >= p.outer) return;
+    const int64_t rem = g - o * tiles;
+    i = (int)(rem / pgs) * (4 * RW) + RW * (int)(gw & 3) + c / PW;
+    cp = (rem % pgs) * PW + c % PW;
+  } else {
+    const int64_t line = gw * 32 + (lane & 31);
+    const int64_t lines = p.outer * p.inner * p.CP2;
+    if (line >= lines) return;
+    cp = line % p.CP2;
+    const int64_t t = line / p.CP2;
+    i = (int)(t % p.inner);
+    o = t / p.inner;
+  }
   const int64_t step = p.inner * p.CP2;  // pairs between rows r and r + 1
   const int64_t base = (o * R * p.inner + i) * p.CP2 + cp;
   const char* in = reinterpret_cast<const char*>(p.in[blockIdx.y]) + (base + h * step) * pair_bytes<IN>();
-  char* out = reinterpret_cast<char*>(p.out[blockIdx.y]) + (base + h * R2 * step) * 8;
+  const int64_t obase = TILED ? o * R * step + (cp >> 2) * (p.inner * 4) + i * 4 + (cp & 3) : base;
+  char* out = reinterpret_cast<char*>(p.out[blockIdx.y]) + (obase + h * R2 * step) * 8;
 
   float2 e[R2];
 #pragma unroll
@@ -195,12 +223,43 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
   }
 }
 
+// ------------------------------------------------------------- gate table
+//
+// gtab[(h * ncol + c) * N + k3] = scale * G[h][min(f, L - f)] if that bin is
+// kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 * k3):
+// the gate of every bin in the order the square B kernel's lanes visit them,
+// so that 32 lanes of one column read 32 consecutive values.
+
+struct GateTabParams {
+  const float* gate;  // [H][nbins]
+  float* gtab;        // [H][ncol][N]
+  int64_t L;
+  int L1, L2, N, ncol, nbins;
+  int64_t keep, total;  // total = H * L
+  float scale;
+};
+
+__global__ __launch_bounds__(256) void k_gate_table(GateTabParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.total) return;
+  const int k3 = (int)(idx % p.N);
+  const int64_t r = idx / p.N;
+  const int c = (int)(r % p.ncol);
+  const int h = (int)(r / p.ncol);
+  const int64_t f = c % p.L1 + (int64_t)p.L1 * (c / p.L1 + (int64_t)p.L2 * k3);
+  const int64_t fc = f < p.L - f ? f : p.L - f;
+  p.gtab[idx] = fc < p.keep ? p.gate[(int64_t)h * p.nbins + fc] * p.scale : 0.f;
+}
+
 // ------------------------------------------- B: LDS Stockham + spectral mix
 
 struct MidParams {
   const void* in[3];     // q, k, v sources (raw tensors, or the A-pass output)
   float2* out;           // inverse output (may alias in[0])
   const float* gate;     // [H][nbins]
+  const float* gtab;     // k_mid_sq: [H][ncol][N] gate table (scale, truncation, mirror folded in)
+  int ncol;              // columns per batch element, L1 * L2
+  int tiled;             // k_mid_sq: in[] laid out [b][column][CP2 / 4][N][4] (see k_strided_split)
   const float2* twN;     // twN[e] = exp(-2 pi i e / N), e < N
   const float2* twL;     // twL[e] = exp(-2 pi i e / L)
   const int2* wgcols;    // per workgroup: its column(s), col = k1 + L1 * k2 (-1 = none)
@@ -507,7 +566,6 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   const int colid2 = s2 == 0 ? cols.x : cols.y;
   const bool active1 = colid1 >= 0;
   const int kc1 = active1 ? colid1 % p.L1 : 0, k2c1 = active1 ? colid1 / p.L1 : 0;
-  const int kc2 = colid2 >= 0 ? colid2 % p.L1 : 0, k2c2 = colid2 >= 0 ? colid2 / p.L1 : 0;
   const int cp1 = blk.y * p.cpt + j1;
   const int cp2 = blk.y * p.cpt + j2;
   // element i of this stage-1 lane's column sits at pair index
@@ -515,9 +573,14 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   const uint32_t lane_pair = (uint32_t)((kc1 * p.M + k2c1 * N + t1) * p.CP2 + cp1);
   const int64_t batch_pair = (int64_t)b * p.L * p.CP2;
   const int64_t row_pair = (int64_t)R * p.CP2;
-  // bin of element (k1, k2) of the stage-2 column: fbase + fstep * k2
-  const int fbase = kc2 + p.L1 * (k2c2 + p.L2 * k1);
-  const int fstep = p.L1 * p.L2 * R;
+  // the same element in the tiled input layout: block cp1 / 4 of the column
+  // holds its N rows of 4 pairs contiguously
+  const uint32_t in_pair = p.tiled ? (uint32_t)((kc1 * p.M + k2c1 * N) * p.CP2 + (cp1 >> 2) * (N * 4) +
+                                                t1 * 4 + (cp1 & 3))
+                                   : lane_pair;
+  const int64_t in_row = p.tiled ? (int64_t)R * 4 : row_pair;
+  // element (k1, k2) of the stage-2 column is bin k3 = k1 + R k2 of column colid2
+  const int colid2c = colid2 >= 0 ? colid2 : 0;
   const int ha = (2 * cp2) / p.D, hb = (2 * cp2 + 1) / p.D;
 
   float2 v[R];
@@ -527,17 +590,18 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   for (int x = 0; x < 3; ++x) {
     // values only one phase needs are made opaque per iteration, so they are
     // not hoisted out of the loop and kept live across it
-    const float* gate = p.gate;
-    int fb = fbase;
+    // gate values of this lane's bins (k1 + R u of column colid2)
+    const float* gta = p.gtab + ((int64_t)ha * p.ncol + colid2c) * N + k1;
+    const float* gtb = p.gtab + ((int64_t)hb * p.ncol + colid2c) * N + k1;
     int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
-    asm volatile("" : "+s"(gate), "+v"(fb), "+v"(t1o));
+    asm volatile("" : "+v"(gta), "+v"(gtb), "+v"(t1o));
     // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
     {
       const char* src = reinterpret_cast<const char*>(p.in[x]) + batch_pair * pair_bytes<IN>();
-      const uint32_t off = lane_pair * pair_bytes<IN>();
+      const uint32_t off = in_pair * pair_bytes<IN>();
       if (active1) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) v[i] = load_pair_u<IN>(src + i * row_pair * pair_bytes<IN>(), off);
+        for (int i = 0; i < R; ++i) v[i] = load_pair_u<IN>(src + i * in_row * pair_bytes<IN>(), off);
       } else {
 #pragma unroll
         for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
@@ -588,12 +652,8 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 #pragma unroll
       for (int u = 0; u <= H2; ++u) {
         const float2 z = v[u], zm = mirror(u);
-        const int f = fb + fstep * u;
-        const int fc = min(f, p.L - f);
-        const bool kept = fc < p.keep;
-        const int gi = kept ? fc : 0;  // bins at or above keep_bins only ever give 0
-        const float ga = kept ? gate[ha * p.nbins + gi] * p.scale : 0.f;
-        const float gb = kept ? gate[hb * p.nbins + gi] * p.scale : 0.f;
+        const float ga = gta[R * u];
+        const float gb = ha == hb ? ga : gtb[R * u];
         const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), ga);
         const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), gb);
         sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);

@@ -368,10 +368,32 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   return SPECTRE_OK;
 }
 
-size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
+// Two-level plans whose first pass is the split 48/64-point kernel hand the
+// square B kernel its spectra in the tiled layout ([b][k1][CP2/4][L3][4]);
+// B then writes U (row layout) to a fourth region instead of in place.
+bool tiled_plan(const Shape& s, const Plan& pl) {
+  return !is_single(pl) && pl.L2 == 1 && pl.sq == 32 && (pl.L1 == 48 || pl.L1 == 64) &&
+         s.CP2 % 32 == 0 && pl.L3 % 8 == 0;
+}
+
+// Bytes of the spectra part of the workspace: three complex spectra of pairs
+// (q, k, v; U and y reuse them, or U gets a fourth region with the tiled
+// layout) for multi-level plans, y for the single-level LayerNorm pass.
+size_t spectra_bytes(const Shape& s, const Plan& pl, bool want_fwd) {
   const size_t n = (size_t)s.N;
-  if (is_single(pl)) return want_fwd ? 4 * n : 0;  // y for the LayerNorm pass
-  return 12 * n;  // three complex spectra of pairs (q, k, v); U and y reuse them
+  if (is_single(pl)) return want_fwd ? 4 * n : 0;
+  return (tiled_plan(s, pl) ? 16 : 12) * n;
+}
+
+// Bytes of the gate table the square B kernel reads (H * L binary32 values,
+// in its own bin order), 0 when the plan uses the generic B kernel.
+size_t gate_table_bytes(const Shape& s, const Plan& pl) {
+  return pl.sq ? (size_t)4 * s.H * s.L : 0;
+}
+
+size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
+  const size_t a = (spectra_bytes(s, pl, want_fwd) + 255) & ~(size_t)255;
+  return a + gate_table_bytes(s, pl);
 }
 
 // ------------------------------------------------------------ launching
@@ -395,20 +417,25 @@ int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t 
 }
 
 template <int R, int IN>
-int launch_strided_fwd_split(const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+int launch_strided_fwd_split(const StridedParams& p, int tw, int ntensor, bool tiled, hipStream_t st) {
   const int64_t lines = p.outer * p.inner * p.CP2;
   const int64_t waves = (lines + 31) / 32;
   dim3 grid((unsigned)((waves + 3) / 4), ntensor);
-  if (tw == TW_A1)
-    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A1>), grid, dim3(256), 0, st, p);
+  if (tiled && tw == TW_A1)
+    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A1, true>), grid, dim3(256), 0, st, p);
+  else if (tw == TW_A1)
+    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A1, false>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A2>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_strided_split<R, IN, TW_A2, false>), grid, dim3(256), 0, st, p);
   SPECTRE_LAUNCH_CHECK(tw == TW_A1 ? "A1_fwd_strided" : "A2_fwd_strided");
   return SPECTRE_OK;
 }
 
+// Forward strided pass of length R; `tiled` (first pass of a two-level plan
+// with R = 48 or 64 only) writes the tiled layout the square B kernel reads.
 template <int IN>
-int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStream_t st,
+                bool tiled = false) {
   switch (R) {
     case 2: return launch_strided_fwd<2, IN>(p, tw, ntensor, st);
     case 3: return launch_strided_fwd<3, IN>(p, tw, ntensor, st);
@@ -419,8 +446,8 @@ int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStrea
     case 16: return launch_strided_fwd<16, IN>(p, tw, ntensor, st);
     case 24: return launch_strided_fwd<24, IN>(p, tw, ntensor, st);
     case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st);
-    case 48: return launch_strided_fwd_split<48, IN>(p, tw, ntensor, st);
-    case 64: return launch_strided_fwd_split<64, IN>(p, tw, ntensor, st);
+    case 48: return launch_strided_fwd_split<48, IN>(p, tw, ntensor, tiled, st);
+    case 64: return launch_strided_fwd_split<64, IN>(p, tw, ntensor, tiled, st);
     default: return SPECTRE_EUNSUPPORTED;
   }
 }
@@ -456,6 +483,14 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
   const size_t lds = (size_t)p.N * p.nslot * p.cpt * sizeof(float2);
   hipLaunchKernelGGL((k_mid<P, IN>), grid, dim3(threads), lds, st, p);
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
+  return SPECTRE_OK;
+}
+
+int launch_gate_table(const GateTabParams& g, hipStream_t st) {
+  const int64_t blocks = (g.total + 255) / 256;
+  if (blocks > INT32_MAX) return SPECTRE_EUNSUPPORTED;
+  hipLaunchKernelGGL(k_gate_table, dim3((unsigned)blocks), dim3(256), 0, st, g);
+  SPECTRE_LAUNCH_CHECK("G_gate_table");
   return SPECTRE_OK;
 }
 
@@ -559,6 +594,8 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   const int in_kind = s.dtype == SPECTRE_F32 ? IN_F32 : IN_BF16;
   const bool single = is_single(pl);
   float2* T = reinterpret_cast<float2*>(ws);  // [3][B][L][CP2] complex (multi-level)
+  const bool tiled = tiled_plan(s, pl);
+  float2* U = tiled ? T + 3 * pairs : T;       // B's output, row layout
 
   // ---- forward strided passes
   if (!single) {
@@ -572,8 +609,8 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     a1.inner = pl.L2 * pl.L3;
     a1.CP2 = CP2;
     a1.L1 = (int)pl.L1;
-    rc = in_kind == IN_F32 ? strided_fwd<IN_F32>(pl.L1, a1, TW_A1, 3, st)
-                           : strided_fwd<IN_BF16>(pl.L1, a1, TW_A1, 3, st);
+    rc = in_kind == IN_F32 ? strided_fwd<IN_F32>(pl.L1, a1, TW_A1, 3, st, tiled)
+                           : strided_fwd<IN_BF16>(pl.L1, a1, TW_A1, 3, st, tiled);
     if (rc) return rc;
     if (pl.L2 > 1) {
       StridedParams a2{};
@@ -591,6 +628,28 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     }
   }
 
+  // ---- gate table of the square B kernel: scale, truncation and the mirror
+  // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced
+  float* gtab = nullptr;
+  if (pl.sq) {
+    gtab = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                    ((spectra_bytes(s, pl, want_out) + 255) & ~(size_t)255));
+    GateTabParams g{};
+    g.gate = gate;
+    g.gtab = gtab;
+    g.L = s.L;
+    g.L1 = (int)pl.L1;
+    g.L2 = (int)pl.L2;
+    g.N = (int)pl.L3;
+    g.ncol = (int)(pl.L1 * pl.L2);
+    g.nbins = (int)(s.L / 2 + 1);
+    g.keep = s.keep;
+    g.total = s.H * s.L;
+    g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
+    rc = launch_gate_table(g, st);
+    if (rc) return rc;
+  }
+
   // ---- B: LDS transform, spectral product, inverse
   {
     MidParams m{};
@@ -603,9 +662,12 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       m.out = want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y);
     } else {
       for (int t = 0; t < 3; ++t) m.in[t] = T + t * pairs;
-      m.out = T;  // overwrites q's spectrum in place, workgroup by workgroup
+      m.out = U;  // row layout: q's spectrum in place, workgroup by workgroup, unless tiled
+      m.tiled = tiled ? 1 : 0;
     }
     m.gate = gate;
+    m.gtab = gtab;
+    m.ncol = (int)(pl.L1 * pl.L2);
     m.twN = tab->twN;
     m.twL = tab->twL;
     m.wgcols = tab->wgcols;
@@ -677,7 +739,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   }
   const bool fuse = want_out && fused_norm_ok(CP2);
   FinalParams f{};
-  f.U = T;
+  f.U = U;
   f.x = x;
   f.gamma = gamma;
   f.beta = beta;

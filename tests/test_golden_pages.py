@@ -22,7 +22,8 @@ def test_spectrum_workspace_matches_article_memory_estimate():
     forward pass keeps the three spectra of q, k and v."""
     f = FIG["complex_intermediate"]
     ws = sm.spectre_mix_workspace_bytes(f["B"], f["H"], f["L"], f["D"], sm.SPECTRE_F32)
-    assert ws == 3 * f["bytes"]
+    gate_table = 4 * f["H"] * f["L"]  # the B pass's gate table, the rest of the workspace
+    assert ws - gate_table == 3 * f["bytes"]  # L = 131072 = 64 x 2 x 1024: three spectra
     assert f["bytes"] == 256 * 2 ** 20
 
 
