@@ -150,6 +150,31 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
   }
 }
 
+// Radix-2 join of an R-point DFT split over lanes l (h = 0, the even
+// samples) and l^32 (h = 1, the odd samples), each holding its R/2-point DFT
+// in v[0 .. R/2).  One v_permlane32_swap per dword pairs v[n] of the low
+// half with v[n + Q] of the high half (Q = R/4): lane h then holds E0 and E1
+// at index n + Q h and finishes the butterfly in place, so v[n] becomes
+// output n + Q h and v[n + Q] output n + Q h + R/2.  The twiddle
+// w^(n + Q h), w = exp(SIGN 2 pi i / R), is w^n times w^Q = SIGN i on h = 1.
+template <int R, int SIGN>
+__device__ __forceinline__ void join_swap(float2 (&v)[R / 2], int h) {
+  constexpr int Q = R / 4;
+  static_assert(R % 4 == 0, "join_swap needs R divisible by 4");
+#pragma unroll
+  for (int n = 0; n < Q; ++n) {
+    const auto sx = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[n].x), __float_as_uint(v[n + Q].x),
+                                                     false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[n].y), __float_as_uint(v[n + Q].y),
+                                                     false, false);
+    const float2 e0 = make_float2(__uint_as_float(sx[0]), __uint_as_float(sy[0]));
+    float2 t = twiddle_ct<R, SIGN>(make_float2(__uint_as_float(sx[1]), __uint_as_float(sy[1])), n);
+    if (h) t = SIGN > 0 ? make_float2(-t.y, t.x) : make_float2(t.y, -t.x);
+    v[n] = cadd(e0, t);
+    v[n + Q] = csub(e0, t);
+  }
+}
+
 // Forward strided pass with the R-point DFT split over two lanes (l, l^32):
 // lane half h loads the samples r = 2a + h (a < R/2) and transforms them
 // (R/2 points); the halves trade results with a lane permute and finish
@@ -869,6 +894,97 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
                                    (z[r].y - mean[r]) * rstd[r] * g1 + b1);
       store_pair<DT>(p.out, obase + r * ostep, o);
     }
+  }
+}
+
+// C1 with the R-point inverse DFT split over lanes l and l^32 (R = 48, 64),
+// fused with the residual and the LayerNorm.  One workgroup per (b, m) with
+// 2 CP2 threads: wave w, lane h * 32 + c serves pair 32 w + c; half h loads
+// the rows k1 = 2a + h and transforms them (R/2 points), and join_swap
+// finishes the radix-2 step, leaving half h with R/2 of the R tokens (slot j
+// holds token tok(j)).  Half the registers of k_final, so four times the
+// waves per CU.  Token sums: recursive halving over the 32 lanes of a half
+// (lane c ends with the half-wave total of slot c), then the waves' totals
+// meet in LDS.  Needs CP2 % 32 == 0 and CP2 <= 256.
+template <int R, int DT>
+__global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
+  constexpr int R2 = R / 2;
+  constexpr int T2 = next_pow2(R2);  // 32: token slots per half
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
+  const int nw = blockDim.x >> 6;
+  const int64_t cp = (int64_t)wave * 32 + c;
+  const int64_t bm = blockIdx.x;  // b * M + m
+  const int64_t m = bm % p.M;
+  const int64_t b = bm / p.M;
+  __shared__ float red[8][2 * T2];
+  __shared__ float s_mean[2 * T2], s_rstd[2 * T2];
+
+  float2 z[R2];
+  {
+    const float2* u = p.U + ((b * R + h) * p.M + m) * p.CP2 + cp;
+    const int64_t rs = 2 * p.M * p.CP2;  // rows 2a + h
+#pragma unroll
+    for (int a = 0; a < R2; ++a) z[a] = u[a * rs];
+  }
+  dft<R2, +1>(z);
+  join_swap<R, +1>(z, h);
+  // slot j of half h holds token n1 = tok(j) (join_swap's output order);
+  // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
+  constexpr int Q = R / 4;
+  auto tok = [&](int j) { return (j < Q ? j : j + Q) + Q * h; };
+  const int64_t ostep = p.M * p.CP2;
+  const int64_t obase = (b * p.L + m) * p.CP2 + cp + (int64_t)(Q * h) * ostep;
+  auto toff = [&](int j) { return (int64_t)(j < Q ? j : j + Q) * ostep; };  // tok(j) - Q h
+  // residual, loaded in groups of 8 so that the loads in flight fit the
+  // register budget of four waves per SIMD
+#pragma unroll
+  for (int g = 0; g < R2; g += 8) {
+#pragma unroll
+    for (int j = g; j < g + 8 && j < R2; ++j) z[j] = cadd(z[j], load_pair<DT>(p.x, obase + toff(j)));
+    asm volatile("" ::: "memory");
+  }
+
+  // per-token sums over the workgroup's pairs: lane c ends with slot c's total
+  auto token_sums = [&](float (&t)[T2], float* dst, bool is_var) __attribute__((always_inline)) {
+    halve_sums<T2, 16>(t, lane);
+    if (c < R2) red[wave][tok(c)] = t[0];
+    __syncthreads();
+    if (tid < R) {
+      float a = 0.f;
+      for (int w = 0; w < nw; ++w) a += red[w][tid];
+      dst[tid] = is_var ? 1.0f / sqrtf(a * p.inv_c + p.eps) : a * p.inv_c;
+    }
+    __syncthreads();
+  };
+  {
+    float t[T2];
+#pragma unroll
+    for (int n = 0; n < T2; ++n) t[n] = n < R2 ? z[n].x + z[n].y : 0.f;
+    token_sums(t, s_mean, false);
+  }
+  {
+    float t[T2];
+#pragma unroll
+    for (int n = 0; n < T2; ++n) {
+      if (n < R2) {
+        const float mu = s_mean[tok(n)];
+        const float dx = z[n].x - mu, dy = z[n].y - mu;
+        t[n] = dx * dx + dy * dy;
+      } else {
+        t[n] = 0.f;
+      }
+    }
+    token_sums(t, s_rstd, true);
+  }
+  const float g0 = p.gamma[2 * cp], g1 = p.gamma[2 * cp + 1];
+  const float b0 = p.beta[2 * cp], b1 = p.beta[2 * cp + 1];
+#pragma unroll
+  for (int n = 0; n < R2; ++n) {
+    const float mu = s_mean[tok(n)], rs = s_rstd[tok(n)];
+    const float2 o = make_float2((z[n].x - mu) * rs * g0 + b0, (z[n].y - mu) * rs * g1 + b1);
+    store_pair<DT>(p.out, obase + toff(n), o);
   }
 }
 

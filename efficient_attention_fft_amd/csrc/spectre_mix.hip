@@ -532,6 +532,14 @@ int launch_mid(int P, const MidParams& p, dim3 grid, int threads, hipStream_t st
 
 template <int R, int DT>
 int launch_final_r(const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
+  if constexpr (R == 48 || R == 64) {
+    if (fuse && p.CP2 % 32 == 0) {  // CP2 <= 256 holds whenever fuse does
+      hipLaunchKernelGGL((k_final_split<R, DT>), dim3((unsigned)(B * p.M)), dim3((unsigned)(2 * p.CP2)),
+                         0, st, p);
+      SPECTRE_LAUNCH_CHECK("C1_inv_norm");
+      return SPECTRE_OK;
+    }
+  }
   if (fuse) {
     dim3 grid((unsigned)(B * p.M));
     hipLaunchKernelGGL((k_final<R, DT, true>), grid, dim3((unsigned)p.CP2), 0, st, p);
