@@ -67,7 +67,12 @@ def kernel_bytes(name: str, w) -> int:
     spec = 4 * N  # one tensor's spectrum as binary32 complex channel pairs
     gate = 4 * w.H * min(w.keep_bins, w.nbins)
     if name == "A1_fwd_strided":
-        return 3 * N * s + 3 * spec
+        import efficient_attention_fft_amd as sm
+        _, (l1, l2, l3) = sm.spectre_mix_plan(w.L)
+        folded = 0
+        if l1 in (48, 64) and l3 in (256, 1024):  # this launch also builds the gate table
+            folded = 4 * w.H * min(w.keep_bins, w.nbins) + 4 * w.H * w.L
+        return 3 * N * s + 3 * spec + folded
     if name == "A2_fwd_strided":
         return 6 * spec
     if name == "B_mid_lds":
@@ -254,6 +259,8 @@ def _short(name: str) -> str:
     if kern in ("k_strided", "k_strided_split"):
         return {"1": "A1_fwd_strided", "2": "A2_fwd_strided", "3": "C2_inv_strided"}.get(
             args[2], name[:60])
+    if kern == "k_final_split":
+        return "C1_inv_norm"
     if kern.startswith("k_mid"):
         return "B_mid_lds"
     if kern == "k_final":

@@ -98,6 +98,41 @@ __device__ __forceinline__ float2 twiddle_lookup(const float2* __restrict__ tw, 
   return inverse ? make_float2(w.x, -w.y) : w;
 }
 
+// ------------------------------------------------------------- gate table
+//
+// gtab[(h * ncol + c) * N + k3] = scale * G[h][min(f, L - f)] if that bin is
+// kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 * k3):
+// the gate of every bin in the order the square B kernel's lanes visit them,
+// so that 32 lanes of one column read 32 consecutive values.  Built by
+// extra workgroups of the first strided pass when that pass is the split
+// kernel, else by k_gate_table.
+
+struct GateTabParams {
+  const float* gate;  // [H][nbins]
+  float* gtab;        // [H][ncol][N]; null: no table to build
+  int64_t L;
+  int L1, L2, N, ncol, nbins;
+  int64_t keep, total;  // total = H * L
+  float scale;
+};
+
+// Entries idx0, idx0 + stride, ... of the table.
+__device__ __forceinline__ void gate_table_fill(const GateTabParams& p, int64_t idx0, int64_t stride) {
+  for (int64_t idx = idx0; idx < p.total; idx += stride) {
+    const int k3 = (int)(idx % p.N);
+    const int64_t r = idx / p.N;
+    const int c = (int)(r % p.ncol);
+    const int h = (int)(r / p.ncol);
+    const int64_t f = c % p.L1 + (int64_t)p.L1 * (c / p.L1 + (int64_t)p.L2 * k3);
+    const int64_t fc = f < p.L - f ? f : p.L - f;
+    p.gtab[idx] = fc < p.keep ? p.gate[(int64_t)h * p.nbins + fc] * p.scale : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gate_table(GateTabParams p) {
+  gate_table_fill(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
+}
+
 // ------------------------------------------------------ strided DFT passes
 //
 // Data viewed as [outer][R][inner][CP2] complex elements (CP2 = H*D/2 channel
@@ -106,7 +141,8 @@ __device__ __forceinline__ float2 twiddle_lookup(const float2* __restrict__ tw, 
 // the same positions.  Lanes run along the pair axis, so every load/store
 // instruction of a wave touches 64 consecutive pairs.
 //
-// blockIdx.y selects the tensor (q, k, v) for the forward passes.
+// blockIdx.y selects the tensor (q, k, v) for the forward passes (and, for
+// the split kernel, 3 the gate table).
 
 struct StridedParams {
   const void* in[3];
@@ -114,6 +150,7 @@ struct StridedParams {
   const float2* twL;  // twL[e] = exp(-2 pi i e / L)
   int64_t outer, inner, CP2;
   int L1;
+  GateTabParams gt;   // k_strided_split: blockIdx.y == 3 builds this table
 };
 
 template <int R, int IN, int TW, int SIGN>
@@ -195,6 +232,11 @@ __device__ __forceinline__ void join_swap(float2 (&v)[R / 2], int h) {
 // 4 pairs = 128 bytes per block).  Needs inner % 8 == 0 and CP2 % 32 == 0.
 template <int R, int IN, int TW, bool TILED>
 __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
+  if (blockIdx.y == 3) {  // the gate table, folded into this launch
+    gate_table_fill(p.gt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                    (int64_t)gridDim.x * blockDim.x);
+    return;
+  }
   constexpr int R2 = R / 2;
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
@@ -262,34 +304,6 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     }
     *reinterpret_cast<float2*>(out + (int64_t)k * step * 8) = xk;
   }
-}
-
-// ------------------------------------------------------------- gate table
-//
-// gtab[(h * ncol + c) * N + k3] = scale * G[h][min(f, L - f)] if that bin is
-// kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 * k3):
-// the gate of every bin in the order the square B kernel's lanes visit them,
-// so that 32 lanes of one column read 32 consecutive values.
-
-struct GateTabParams {
-  const float* gate;  // [H][nbins]
-  float* gtab;        // [H][ncol][N]
-  int64_t L;
-  int L1, L2, N, ncol, nbins;
-  int64_t keep, total;  // total = H * L
-  float scale;
-};
-
-__global__ __launch_bounds__(256) void k_gate_table(GateTabParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= p.total) return;
-  const int k3 = (int)(idx % p.N);
-  const int64_t r = idx / p.N;
-  const int c = (int)(r % p.ncol);
-  const int h = (int)(r / p.ncol);
-  const int64_t f = c % p.L1 + (int64_t)p.L1 * (c / p.L1 + (int64_t)p.L2 * k3);
-  const int64_t fc = f < p.L - f ? f : p.L - f;
-  p.gtab[idx] = fc < p.keep ? p.gate[(int64_t)h * p.nbins + fc] * p.scale : 0.f;
 }
 
 // ------------------------------------------- B: LDS Stockham + spectral mix

@@ -420,7 +420,7 @@ template <int R, int IN>
 int launch_strided_fwd_split(const StridedParams& p, int tw, int ntensor, bool tiled, hipStream_t st) {
   const int64_t lines = p.outer * p.inner * p.CP2;
   const int64_t waves = (lines + 31) / 32;
-  dim3 grid((unsigned)((waves + 3) / 4), ntensor);
+  dim3 grid((unsigned)((waves + 3) / 4), ntensor + (p.gt.gtab ? 1 : 0));
   if (tiled && tw == TW_A1)
     hipLaunchKernelGGL((k_strided_split<R, IN, TW_A1, true>), grid, dim3(256), 0, st, p);
   else if (tw == TW_A1)
@@ -487,8 +487,7 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
 }
 
 int launch_gate_table(const GateTabParams& g, hipStream_t st) {
-  const int64_t blocks = (g.total + 255) / 256;
-  if (blocks > INT32_MAX) return SPECTRE_EUNSUPPORTED;
+  const int64_t blocks = std::min<int64_t>((g.total + 255) / 256, 8192);  // grid-stride beyond
   hipLaunchKernelGGL(k_gate_table, dim3((unsigned)blocks), dim3(256), 0, st, g);
   SPECTRE_LAUNCH_CHECK("G_gate_table");
   return SPECTRE_OK;
@@ -605,9 +604,34 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   const bool tiled = tiled_plan(s, pl);
   float2* U = tiled ? T + 3 * pairs : T;       // B's output, row layout
 
+  // ---- gate table of the square B kernel: scale, truncation and the mirror
+  // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced;
+  // built by the first pass when that is the split kernel
+  GateTabParams g{};
+  if (pl.sq) {
+    g.gate = gate;
+    g.gtab = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                      ((spectra_bytes(s, pl, want_out) + 255) & ~(size_t)255));
+    g.L = s.L;
+    g.L1 = (int)pl.L1;
+    g.L2 = (int)pl.L2;
+    g.N = (int)pl.L3;
+    g.ncol = (int)(pl.L1 * pl.L2);
+    g.nbins = (int)(s.L / 2 + 1);
+    g.keep = s.keep;
+    g.total = s.H * s.L;
+    g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
+  }
+  const bool gate_in_a1 = g.gtab && !single && (pl.L1 == 48 || pl.L1 == 64);
+  if (g.gtab && !gate_in_a1) {
+    rc = launch_gate_table(g, st);
+    if (rc) return rc;
+  }
+
   // ---- forward strided passes
   if (!single) {
     StridedParams a1{};
+    if (gate_in_a1) a1.gt = g;
     a1.in[0] = q;
     a1.in[1] = k;
     a1.in[2] = v;
@@ -636,28 +660,6 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     }
   }
 
-  // ---- gate table of the square B kernel: scale, truncation and the mirror
-  // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced
-  float* gtab = nullptr;
-  if (pl.sq) {
-    gtab = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                    ((spectra_bytes(s, pl, want_out) + 255) & ~(size_t)255));
-    GateTabParams g{};
-    g.gate = gate;
-    g.gtab = gtab;
-    g.L = s.L;
-    g.L1 = (int)pl.L1;
-    g.L2 = (int)pl.L2;
-    g.N = (int)pl.L3;
-    g.ncol = (int)(pl.L1 * pl.L2);
-    g.nbins = (int)(s.L / 2 + 1);
-    g.keep = s.keep;
-    g.total = s.H * s.L;
-    g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
-    rc = launch_gate_table(g, st);
-    if (rc) return rc;
-  }
-
   // ---- B: LDS transform, spectral product, inverse
   {
     MidParams m{};
@@ -674,7 +676,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       m.tiled = tiled ? 1 : 0;
     }
     m.gate = gate;
-    m.gtab = gtab;
+    m.gtab = g.gtab;
     m.ncol = (int)(pl.L1 * pl.L2);
     m.twN = tab->twN;
     m.twL = tab->twL;
