@@ -153,19 +153,39 @@ struct StridedParams {
   GateTabParams gt;   // k_strided_split: blockIdx.y == 3 builds this table
 };
 
-template <int R, int IN, int TW, int SIGN>
+// TILED (the forward second pass of a three-level plan, out of place): the
+// outputs of row block r go to [outer][r][CP2 / 4][inner][4] like the tiled
+// first pass; a wave covers 4 rows x 16 pairs and a workgroup 16 rows x 16
+// pairs, so reads come in 128-byte row pieces and each 4-pair block gets
+// 16 rows = 512 contiguous bytes from the workgroup.  Needs inner % 16 == 0
+// and CP2 % 16 == 0.
+template <int R, int IN, int TW, int SIGN, bool TILED = false>
 __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
-  const int64_t line = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t lines = p.outer * p.inner * p.CP2;
-  if (line >= lines) return;
-  const int64_t cp = line % p.CP2;
-  const int64_t t = line / p.CP2;
-  const int i = (int)(t % p.inner);
-  const int64_t o = t / p.inner;
+  int64_t cp, o;
+  int i;
+  if constexpr (TILED) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t pgs = p.CP2 / 16, tiles = (p.inner / 16) * pgs;
+    const int64_t g = blockIdx.x;
+    o = g / tiles;
+    if (o >= p.outer) return;
+    const int64_t rem = g - o * tiles;
+    i = (int)(rem / pgs) * 16 + 4 * w + (lane >> 4);
+    cp = (rem % pgs) * 16 + (lane & 15);
+  } else {
+    const int64_t line = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t lines = p.outer * p.inner * p.CP2;
+    if (line >= lines) return;
+    cp = line % p.CP2;
+    const int64_t t = line / p.CP2;
+    i = (int)(t % p.inner);
+    o = t / p.inner;
+  }
   const void* in = p.in[blockIdx.y];
   float2* out = p.out[blockIdx.y];
   const int64_t step = p.inner * p.CP2;
   const int64_t base = (o * R * p.inner + i) * p.CP2 + cp;
+  const int64_t obase = TILED ? o * R * step + (cp >> 2) * (p.inner * 4) + i * 4 + (cp & 3) : base;
 
   float2 a[R];
 #pragma unroll
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
       const int e = (r * (int)p.inner + i) * k1;
       if (e != 0) v = cmul(v, twiddle_lookup(p.twL, e, true));
     }
-    out[base + r * step] = v;
+    out[obase + r * step] = v;
   }
 }
 

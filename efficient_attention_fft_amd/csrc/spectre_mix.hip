@@ -376,13 +376,22 @@ bool tiled_plan(const Shape& s, const Plan& pl) {
          s.CP2 % 32 == 0 && pl.L3 % 8 == 0;
 }
 
+// Three-level plans whose B is the square kernel: the second pass runs out of
+// place and writes the tiled layout into three more regions; B then writes U
+// over the first pass's q region.
+bool tiled3_plan(const Shape& s, const Plan& pl) {
+  return !is_single(pl) && pl.L2 > 1 && pl.L2 <= 32 && pl.sq == 32 && s.CP2 % 16 == 0 &&
+         pl.L3 % 16 == 0;
+}
+
 // Bytes of the spectra part of the workspace: three complex spectra of pairs
-// (q, k, v; U and y reuse them, or U gets a fourth region with the tiled
-// layout) for multi-level plans, y for the single-level LayerNorm pass.
+// (q, k, v; U and y reuse them), a fourth region for U with the two-level
+// tiled layout, six regions with the three-level one (the second pass out of
+// place), y for the single-level LayerNorm pass.
 size_t spectra_bytes(const Shape& s, const Plan& pl, bool want_fwd) {
   const size_t n = (size_t)s.N;
   if (is_single(pl)) return want_fwd ? 4 * n : 0;
-  return (tiled_plan(s, pl) ? 16 : 12) * n;
+  return (tiled3_plan(s, pl) ? 24 : tiled_plan(s, pl) ? 16 : 12) * n;
 }
 
 // Bytes of the gate table the square B kernel reads (H * L binary32 values,
@@ -448,6 +457,31 @@ int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStrea
     case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st);
     case 48: return launch_strided_fwd_split<48, IN>(p, tw, ntensor, tiled, st);
     case 64: return launch_strided_fwd_split<64, IN>(p, tw, ntensor, tiled, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
+template <int R>
+int launch_strided_fwd_tiled(const StridedParams& p, hipStream_t st) {
+  const int64_t wgs = p.outer * (p.inner / 16) * (p.CP2 / 16);
+  if (wgs > INT32_MAX) return SPECTRE_EUNSUPPORTED;
+  hipLaunchKernelGGL((k_strided<R, IN_C32, TW_A2, -1, true>), dim3((unsigned)wgs, 3), dim3(256), 0, st, p);
+  SPECTRE_LAUNCH_CHECK("A2_fwd_strided");
+  return SPECTRE_OK;
+}
+
+// The second forward pass of a three-level plan, writing the tiled layout.
+int strided_fwd_tiled(int64_t R, const StridedParams& p, hipStream_t st) {
+  switch (R) {
+    case 2: return launch_strided_fwd_tiled<2>(p, st);
+    case 3: return launch_strided_fwd_tiled<3>(p, st);
+    case 4: return launch_strided_fwd_tiled<4>(p, st);
+    case 6: return launch_strided_fwd_tiled<6>(p, st);
+    case 8: return launch_strided_fwd_tiled<8>(p, st);
+    case 12: return launch_strided_fwd_tiled<12>(p, st);
+    case 16: return launch_strided_fwd_tiled<16>(p, st);
+    case 24: return launch_strided_fwd_tiled<24>(p, st);
+    case 32: return launch_strided_fwd_tiled<32>(p, st);
     default: return SPECTRE_EUNSUPPORTED;
   }
 }
@@ -602,7 +636,9 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   const bool single = is_single(pl);
   float2* T = reinterpret_cast<float2*>(ws);  // [3][B][L][CP2] complex (multi-level)
   const bool tiled = tiled_plan(s, pl);
+  const bool tiled3 = tiled3_plan(s, pl);
   float2* U = tiled ? T + 3 * pairs : T;       // B's output, row layout
+  float2* S = tiled3 ? T + 3 * pairs : T;      // the spectra B reads
 
   // ---- gate table of the square B kernel: scale, truncation and the mirror
   // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced;
@@ -648,14 +684,14 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       StridedParams a2{};
       for (int t = 0; t < 3; ++t) {
         a2.in[t] = T + t * pairs;
-        a2.out[t] = T + t * pairs;
+        a2.out[t] = S + t * pairs;
       }
       a2.twL = tab->twL;
       a2.outer = s.B * pl.L1;
       a2.inner = pl.L3;
       a2.CP2 = CP2;
       a2.L1 = (int)pl.L1;
-      rc = strided_fwd<IN_C32>(pl.L2, a2, TW_A2, 3, st);
+      rc = tiled3 ? strided_fwd_tiled(pl.L2, a2, st) : strided_fwd<IN_C32>(pl.L2, a2, TW_A2, 3, st);
       if (rc) return rc;
     }
   }
@@ -671,9 +707,9 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       m.in[2] = v;
       m.out = want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y);
     } else {
-      for (int t = 0; t < 3; ++t) m.in[t] = T + t * pairs;
+      for (int t = 0; t < 3; ++t) m.in[t] = S + t * pairs;
       m.out = U;  // row layout: q's spectrum in place, workgroup by workgroup, unless tiled
-      m.tiled = tiled ? 1 : 0;
+      m.tiled = tiled || tiled3 ? 1 : 0;
     }
     m.gate = gate;
     m.gtab = g.gtab;

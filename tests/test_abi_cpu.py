@@ -112,7 +112,8 @@ def test_every_supported_length_plans():
 def test_workspace_bytes():
     """Three binary32 complex spectra (12 bytes per real element) for
     multi-level plans, a fourth for B's output when the first pass writes the
-    tiled layout (two-level, 48- or 64-point first pass), y (4 bytes per
+    tiled layout (two-level, 48- or 64-point first pass), six when a
+    three-level plan's second pass writes it out of place, y (4 bytes per
     element) for single-level ones, plus the H * L binary32 gate table when
     the column length is 256 or 1024."""
     N = 1 * 65536 * 512
@@ -121,6 +122,9 @@ def test_workspace_bytes():
     assert sm.spectre_mix_workspace_bytes(2, 8, 65536, 64, 1) == 16 * 2 * N + gate_tab
     # L = 16384 = 16 x 1024: row layout, three spectra
     assert sm.spectre_mix_workspace_bytes(1, 8, 16384, 64, 0) == 12 * 16384 * 512 + 4 * 8 * 16384
+    # L = 786432 = 64 x 12 x 1024: second pass out of place, six spectra
+    N5 = 786432 * 512
+    assert sm.spectre_mix_workspace_bytes(1, 8, 786432, 64, 0) == 24 * N5 + 4 * 8 * 786432
     # L = 4096: single level, generic LDS kernel, no gate table
     assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
     # L = 256: single level, square kernel with its gate table

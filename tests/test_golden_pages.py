@@ -18,12 +18,16 @@ FIG = json.load(open(os.path.join(HERE, "golden", "page_figures.json")))
 def test_spectrum_workspace_matches_article_memory_estimate():
     """One tensor's spectrum in the workspace (binary32 half spectrum: L/2
     complex bins per channel = 4 bytes per real element) is the size the
-    article gives for the half-precision full spectrum of the same shape; the
-    forward pass keeps the three spectra of q, k and v."""
+    article gives for the half-precision full spectrum of the same shape.
+    L = 131072 plans as 64 x 2 x 1024: the first pass writes the spectra of
+    q, k and v, the second pass writes them again (out of place, in the LDS
+    pass's layout), so the workspace holds six spectra plus the gate table."""
     f = FIG["complex_intermediate"]
+    st, plan = sm.spectre_mix_plan(f["L"])
+    assert st == sm.SPECTRE_OK and plan == (64, 2, 1024)
     ws = sm.spectre_mix_workspace_bytes(f["B"], f["H"], f["L"], f["D"], sm.SPECTRE_F32)
     gate_table = 4 * f["H"] * f["L"]  # the B pass's gate table, the rest of the workspace
-    assert ws - gate_table == 3 * f["bytes"]  # L = 131072 = 64 x 2 x 1024: three spectra
+    assert ws - gate_table == 6 * f["bytes"]
     assert f["bytes"] == 256 * 2 ** 20
 
 
