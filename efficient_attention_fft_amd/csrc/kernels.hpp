@@ -153,14 +153,20 @@ struct StridedParams {
   GateTabParams gt;   // k_strided_split: blockIdx.y == 3 builds this table
 };
 
-// TILED (the forward second pass of a three-level plan, out of place): the
-// outputs of row block r go to [outer][r][CP2 / 4][inner][4] like the tiled
-// first pass; a wave covers 4 rows x 16 pairs and a workgroup 16 rows x 16
-// pairs, so reads come in 128-byte row pieces and each 4-pair block gets
-// 16 rows = 512 contiguous bytes from the workgroup.  Needs inner % 16 == 0
-// and CP2 % 16 == 0.
+// TILED (the forward first pass of a two-level plan, or the second pass of
+// a three-level one, out of place): the outputs of row block r go to
+// [outer][r][CP2 / 4][inner][4] like the tiled split pass; a wave covers
+// 4 rows x 16 pairs and a workgroup 16 rows x 16 pairs, so reads come in
+// 64- or 128-byte row pieces and each 4-pair block gets 16 rows = 512
+// contiguous bytes from the workgroup.  Needs inner % 16 == 0 and
+// CP2 % 16 == 0.  blockIdx.y == 3, when launched, builds the gate table.
 template <int R, int IN, int TW, int SIGN, bool TILED = false>
 __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
+  if (blockIdx.y == 3) {  // the gate table, folded into this launch
+    gate_table_fill(p.gt, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                    (int64_t)gridDim.x * blockDim.x);
+    return;
+  }
   int64_t cp, o;
   int i;
   if constexpr (TILED) {

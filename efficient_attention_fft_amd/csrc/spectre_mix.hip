@@ -25,7 +25,7 @@ namespace {
 // ------------------------------------------------------------------ plan
 
 constexpr int64_t kMaxL = 3 * (int64_t(1) << 20);
-constexpr int64_t kMaxSingle = 4096;  // longest column kept whole in one workgroup's LDS
+constexpr int64_t kMaxSingle = 2048;  // longest column kept whole in one workgroup's LDS
 constexpr int kMaxC = 4096;
 constexpr int kMaxMidThreads = 512;   // launch bound of the B kernel
 constexpr int kMaxFusedPairs = 256; // launch bound of the fused C1 kernel
@@ -368,12 +368,11 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   return SPECTRE_OK;
 }
 
-// Two-level plans whose first pass is the split 48/64-point kernel hand the
-// square B kernel its spectra in the tiled layout ([b][k1][CP2/4][L3][4]);
-// B then writes U (row layout) to a fourth region instead of in place.
+// Two-level plans with the square B kernel hand it the spectra in the tiled
+// layout ([b][k1][CP2/4][L3][4]); B then writes U (row layout) to a fourth
+// region instead of in place.
 bool tiled_plan(const Shape& s, const Plan& pl) {
-  return !is_single(pl) && pl.L2 == 1 && pl.sq == 32 && (pl.L1 == 48 || pl.L1 == 64) &&
-         s.CP2 % 32 == 0 && pl.L3 % 8 == 0;
+  return !is_single(pl) && pl.L2 == 1 && pl.sq == 32 && s.CP2 % 32 == 0 && pl.L3 % 16 == 0;
 }
 
 // Three-level plans whose B is the square kernel: the second pass runs out of
@@ -414,9 +413,20 @@ size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
   } while (0)
 
 template <int R, int IN>
-int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t st) {
+int launch_strided_fwd(const StridedParams& p, int tw, int ntensor, hipStream_t st, bool tiled) {
   const int64_t lines = p.outer * p.inner * p.CP2;
-  dim3 grid((unsigned)((lines + 255) / 256), ntensor);
+  const unsigned planes = ntensor + (p.gt.gtab ? 1 : 0);
+  if (tiled) {
+    const int64_t wgs = p.outer * (p.inner / 16) * (p.CP2 / 16);
+    if (wgs > INT32_MAX) return SPECTRE_EUNSUPPORTED;
+    if (tw == TW_A1)
+      hipLaunchKernelGGL((k_strided<R, IN, TW_A1, -1, true>), dim3((unsigned)wgs, planes), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_strided<R, IN, TW_A2, -1, true>), dim3((unsigned)wgs, planes), dim3(256), 0, st, p);
+    SPECTRE_LAUNCH_CHECK(tw == TW_A1 ? "A1_fwd_strided" : "A2_fwd_strided");
+    return SPECTRE_OK;
+  }
+  dim3 grid((unsigned)((lines + 255) / 256), planes);
   if (tw == TW_A1)
     hipLaunchKernelGGL((k_strided<R, IN, TW_A1, -1>), grid, dim3(256), 0, st, p);
   else
@@ -440,48 +450,24 @@ int launch_strided_fwd_split(const StridedParams& p, int tw, int ntensor, bool t
   return SPECTRE_OK;
 }
 
-// Forward strided pass of length R; `tiled` (first pass of a two-level plan
-// with R = 48 or 64 only) writes the tiled layout the square B kernel reads.
+// Forward strided pass of length R; `tiled` writes the tiled layout the
+// square B kernel reads (the first pass of a two-level plan, or the second
+// of a three-level one with R <= 32).
 template <int IN>
 int strided_fwd(int64_t R, const StridedParams& p, int tw, int ntensor, hipStream_t st,
                 bool tiled = false) {
   switch (R) {
-    case 2: return launch_strided_fwd<2, IN>(p, tw, ntensor, st);
-    case 3: return launch_strided_fwd<3, IN>(p, tw, ntensor, st);
-    case 4: return launch_strided_fwd<4, IN>(p, tw, ntensor, st);
-    case 6: return launch_strided_fwd<6, IN>(p, tw, ntensor, st);
-    case 8: return launch_strided_fwd<8, IN>(p, tw, ntensor, st);
-    case 12: return launch_strided_fwd<12, IN>(p, tw, ntensor, st);
-    case 16: return launch_strided_fwd<16, IN>(p, tw, ntensor, st);
-    case 24: return launch_strided_fwd<24, IN>(p, tw, ntensor, st);
-    case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st);
+    case 2: return launch_strided_fwd<2, IN>(p, tw, ntensor, st, tiled);
+    case 3: return launch_strided_fwd<3, IN>(p, tw, ntensor, st, tiled);
+    case 4: return launch_strided_fwd<4, IN>(p, tw, ntensor, st, tiled);
+    case 6: return launch_strided_fwd<6, IN>(p, tw, ntensor, st, tiled);
+    case 8: return launch_strided_fwd<8, IN>(p, tw, ntensor, st, tiled);
+    case 12: return launch_strided_fwd<12, IN>(p, tw, ntensor, st, tiled);
+    case 16: return launch_strided_fwd<16, IN>(p, tw, ntensor, st, tiled);
+    case 24: return launch_strided_fwd<24, IN>(p, tw, ntensor, st, tiled);
+    case 32: return launch_strided_fwd<32, IN>(p, tw, ntensor, st, tiled);
     case 48: return launch_strided_fwd_split<48, IN>(p, tw, ntensor, tiled, st);
     case 64: return launch_strided_fwd_split<64, IN>(p, tw, ntensor, tiled, st);
-    default: return SPECTRE_EUNSUPPORTED;
-  }
-}
-
-template <int R>
-int launch_strided_fwd_tiled(const StridedParams& p, hipStream_t st) {
-  const int64_t wgs = p.outer * (p.inner / 16) * (p.CP2 / 16);
-  if (wgs > INT32_MAX) return SPECTRE_EUNSUPPORTED;
-  hipLaunchKernelGGL((k_strided<R, IN_C32, TW_A2, -1, true>), dim3((unsigned)wgs, 3), dim3(256), 0, st, p);
-  SPECTRE_LAUNCH_CHECK("A2_fwd_strided");
-  return SPECTRE_OK;
-}
-
-// The second forward pass of a three-level plan, writing the tiled layout.
-int strided_fwd_tiled(int64_t R, const StridedParams& p, hipStream_t st) {
-  switch (R) {
-    case 2: return launch_strided_fwd_tiled<2>(p, st);
-    case 3: return launch_strided_fwd_tiled<3>(p, st);
-    case 4: return launch_strided_fwd_tiled<4>(p, st);
-    case 6: return launch_strided_fwd_tiled<6>(p, st);
-    case 8: return launch_strided_fwd_tiled<8>(p, st);
-    case 12: return launch_strided_fwd_tiled<12>(p, st);
-    case 16: return launch_strided_fwd_tiled<16>(p, st);
-    case 24: return launch_strided_fwd_tiled<24>(p, st);
-    case 32: return launch_strided_fwd_tiled<32>(p, st);
     default: return SPECTRE_EUNSUPPORTED;
   }
 }
@@ -642,7 +628,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
 
   // ---- gate table of the square B kernel: scale, truncation and the mirror
   // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced;
-  // built by the first pass when that is the split kernel
+  // built by an extra grid plane of the first pass for multi-level plans
   GateTabParams g{};
   if (pl.sq) {
     g.gate = gate;
@@ -658,7 +644,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     g.total = s.H * s.L;
     g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
   }
-  const bool gate_in_a1 = g.gtab && !single && (pl.L1 == 48 || pl.L1 == 64);
+  const bool gate_in_a1 = g.gtab && !single;
   if (g.gtab && !gate_in_a1) {
     rc = launch_gate_table(g, st);
     if (rc) return rc;
@@ -691,7 +677,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       a2.inner = pl.L3;
       a2.CP2 = CP2;
       a2.L1 = (int)pl.L1;
-      rc = tiled3 ? strided_fwd_tiled(pl.L2, a2, st) : strided_fwd<IN_C32>(pl.L2, a2, TW_A2, 3, st);
+      rc = strided_fwd<IN_C32>(pl.L2, a2, TW_A2, 3, st, tiled3);
       if (rc) return rc;
     }
   }

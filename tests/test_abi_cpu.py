@@ -85,7 +85,7 @@ def test_y_rejects_before_device():
 
 
 def test_plan_factorisation():
-    cases = {256: (1, 1, 256), 4096: (1, 1, 4096), 3072: (1, 1, 3072), 6144: (6, 1, 1024),
+    cases = {256: (1, 1, 256), 2048: (1, 1, 2048), 4096: (4, 1, 1024), 3072: (6, 1, 512), 6144: (6, 1, 1024),
              8192: (8, 1, 1024), 65536: (64, 1, 1024), 98304: (32, 3, 1024),
              786432: (64, 12, 1024), 3 * 2 ** 20: (64, 48, 1024), 2: (1, 1, 2), 6: (1, 1, 6)}
     for L, want in cases.items():
@@ -120,13 +120,16 @@ def test_workspace_bytes():
     gate_tab = 4 * 8 * 65536
     assert sm.spectre_mix_workspace_bytes(1, 8, 65536, 64, 0) == 16 * N + gate_tab
     assert sm.spectre_mix_workspace_bytes(2, 8, 65536, 64, 1) == 16 * 2 * N + gate_tab
-    # L = 16384 = 16 x 1024: row layout, three spectra
-    assert sm.spectre_mix_workspace_bytes(1, 8, 16384, 64, 0) == 12 * 16384 * 512 + 4 * 8 * 16384
+    # L = 16384 = 16 x 1024: tiled with CP2 = 256; row layout (three spectra) with CP2 = 8
+    assert sm.spectre_mix_workspace_bytes(1, 8, 16384, 64, 0) == 16 * 16384 * 512 + 4 * 8 * 16384
+    assert sm.spectre_mix_workspace_bytes(1, 2, 16384, 8, 0) == 12 * 16384 * 16 + 4 * 2 * 16384
     # L = 786432 = 64 x 12 x 1024: second pass out of place, six spectra
     N5 = 786432 * 512
     assert sm.spectre_mix_workspace_bytes(1, 8, 786432, 64, 0) == 24 * N5 + 4 * 8 * 786432
-    # L = 4096: single level, generic LDS kernel, no gate table
-    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
+    # L = 4096 = 4 x 1024: two-level with the tiled layout
+    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 16 * 4 * 4096 * 512 + 4 * 8 * 4096
+    # L = 2048: single level, generic LDS kernel, y only, no gate table
+    assert sm.spectre_mix_workspace_bytes(4, 8, 2048, 64, 0) == 4 * 4 * 2048 * 512
     # L = 256: single level, square kernel with its gate table
     assert sm.spectre_mix_workspace_bytes(1, 2, 256, 16, 0) == 4 * 256 * 32 + 4 * 2 * 256
     assert sm.spectre_mix_workspace_bytes(1, 8, 65535, 64, 0) == 0

@@ -90,8 +90,9 @@ EDGE = [
     (1, 256, 1, 32, 0, 0),          # keep 0: out = LayerNorm(x)
     (1, 256, 2, 16, 0, 1),          # only the DC bin
     (1, 1536, 4, 8, 1, 700),
-    (2, 4096, 2, 8, 0, 2048),       # Nyquist dropped
-    (1, 3072, 2, 32, 0, None),      # radix 3 in the LDS pass
+    (2, 4096, 2, 8, 0, 2048),       # Nyquist dropped (4 x 1024, row layout: CP2 = 8)
+    (1, 3072, 2, 32, 0, None),      # two-level 6 x 512: radix 3 in the strided pass, generic LDS pass
+    (1, 2048, 2, 64, 0, 700),       # the longest single-level column
     (1, 6144, 2, 64, 0, None),      # two-level, radix 3 in the strided pass (l1 = 6)
     (2, 8192, 4, 32, 1, 1000),      # two-level, fused norm, bf16
     (1, 12288, 1, 6, 0, None),      # two-level, narrow: separate norm pass
