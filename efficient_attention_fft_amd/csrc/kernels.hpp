@@ -167,8 +167,8 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
                     (int64_t)gridDim.x * blockDim.x);
     return;
   }
-  int64_t cp, o;
-  int i;
+  int64_t cp, o, cp0 = 0;
+  int i, i0 = 0;
   if constexpr (TILED) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t pgs = p.CP2 / 16, tiles = (p.inner / 16) * pgs;
@@ -176,8 +176,10 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
     o = g / tiles;
     if (o >= p.outer) return;
     const int64_t rem = g - o * tiles;
-    i = (int)(rem / pgs) * 16 + 4 * w + (lane >> 4);
-    cp = (rem % pgs) * 16 + (lane & 15);
+    i0 = (int)(rem / pgs) * 16;
+    cp0 = (rem % pgs) * 16;
+    i = i0 + 4 * w + (lane >> 4);
+    cp = cp0 + (lane & 15);
   } else {
     const int64_t line = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t lines = p.outer * p.inner * p.CP2;
@@ -197,8 +199,7 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
 #pragma unroll
   for (int r = 0; r < R; ++r) a[r] = load_pair<IN>(in, base + r * step);
   dft<R, SIGN>(a);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
+  auto twiddled = [&](int r) __attribute__((always_inline)) {
     float2 v = a[r];
     if constexpr (TW == TW_A1) {
       if (r != 0 && i != 0) v = cmul(v, twiddle_lookup(p.twL, i * r, false));
@@ -209,7 +210,34 @@ __global__ __launch_bounds__(256) void k_strided(StridedParams p) {
       const int e = (r * (int)p.inner + i) * k1;
       if (e != 0) v = cmul(v, twiddle_lookup(p.twL, e, true));
     }
-    out[obase + r * step] = v;
+    return v;
+  };
+  if constexpr (TILED) {
+    // the workgroup's 16 rows x 16 pairs of each output row block are 4
+    // blocks of 16 rows x 4 pairs = 512 contiguous bytes; outputs go through
+    // LDS 8 at a time so that every store instruction writes a whole block
+    __shared__ float2 stg[8][16][17];
+    const int tid = threadIdx.x;
+    const int rl = tid >> 4, pl = tid & 15;  // = 4 w + lane / 16, lane % 16
+    float2* ob = out + o * R * step + (cp0 >> 2) * (p.inner * 4) + i0 * 4;
+#pragma unroll
+    for (int r0 = 0; r0 < R; r0 += 8) {
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+        if (r0 + rr < R) stg[rr][rl][pl] = twiddled(r0 + rr);
+      __syncthreads();
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        // element e = e2 * 256 + tid: pair pr, row r, block blk, local output rr
+        const int e = e2 * 256 + tid;
+        const int pr = e & 3, r = (e >> 2) & 15, blk = (e >> 6) & 3, rr = e >> 8;
+        if (r0 + rr < R) ob[(int64_t)(r0 + rr) * step + blk * (p.inner * 4) + r * 4 + pr] = stg[rr][r][4 * blk + pr];
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) out[obase + r * step] = twiddled(r);
   }
 }
 
@@ -267,8 +295,8 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // global wave
-  int64_t cp, o;
-  int i;
+  int64_t cp, o, cp0 = 0;
+  int i, i0 = 0;
   if constexpr (TILED) {
     constexpr int RW = IN == IN_BF16 ? 1 : 2;  // rows per wave
     constexpr int PW = 32 / RW;                // pairs per wave
@@ -278,8 +306,10 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     o = g / tiles;
     if (o >= p.outer) return;
     const int64_t rem = g - o * tiles;
-    i = (int)(rem / pgs) * (4 * RW) + RW * (int)(gw & 3) + c / PW;
-    cp = (rem % pgs) * PW + c % PW;
+    i0 = (int)(rem / pgs) * (4 * RW);
+    cp0 = (rem % pgs) * PW;
+    i = i0 + RW * (int)(gw & 3) + c / PW;
+    cp = cp0 + c % PW;
   } else {
     const int64_t line = gw * 32 + (lane & 31);
     const int64_t lines = p.outer * p.inner * p.CP2;
@@ -315,8 +345,7 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     tw4 = p.twL[4 * tw_i];
   }
   float2 stp = make_float2(1.f, 0.f);
-#pragma unroll
-  for (int k = 0; k < R2; ++k) {
+  auto output = [&](int k) __attribute__((always_inline)) {
     const float2 mine = e[k];
     const float2 other = make_float2(__shfl_xor(mine.x, 32, 64), __shfl_xor(mine.y, 32, 64));
     const float2 e0 = h ? other : mine;
@@ -328,7 +357,37 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     } else {
       xk = cmul(xk, twiddle_lookup(p.twL, tw_i * (k + R2 * h), false));
     }
-    *reinterpret_cast<float2*>(out + (int64_t)k * step * 8) = xk;
+    return xk;
+  };
+  if constexpr (TILED && IN != IN_BF16) {
+    // Binary32: the workgroup's 8 rows x 16 pairs of each output row block
+    // are 4 blocks of 8 rows x 4 pairs = 256 contiguous bytes each.  Outputs
+    // go through LDS 8 k at a time (16 row blocks with both halves) so that
+    // every store instruction writes two whole blocks.
+    __shared__ float2 stg[16][8][17];
+    const int rl = 2 * (int)(gw & 3) + (lane & 31) / 16, pl = lane & 15;
+    const int tid = threadIdx.x;
+    char* obase_wg = reinterpret_cast<char*>(p.out[blockIdx.y]) +
+                     (o * R * step + (cp0 >> 2) * (p.inner * 4) + i0 * 4) * 8;
+#pragma unroll
+    for (int k0 = 0; k0 < R2; k0 += 8) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) stg[kk + 8 * h][rl][pl] = output(k0 + kk);
+      __syncthreads();
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        // element e = e2 * 256 + tid: pair pr, row r, block blk, local row block kl
+        const int e = e2 * 256 + tid;
+        const int pr = e & 3, r = (e >> 2) & 7, blk = (e >> 5) & 3, kl = e >> 7;
+        const int k1 = k0 + (kl & 7) + R2 * (kl >> 3);
+        *reinterpret_cast<float2*>(obase_wg + ((int64_t)k1 * step + blk * (p.inner * 4) + r * 4 + pr) * 8) =
+            stg[kl][r][4 * blk + pr];
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < R2; ++k) *reinterpret_cast<float2*>(out + (int64_t)k * step * 8) = output(k);
   }
 }
 
