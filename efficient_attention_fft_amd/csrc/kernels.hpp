@@ -359,13 +359,14 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     }
     return xk;
   };
-  if constexpr (TILED && IN != IN_BF16) {
-    // Binary32: the workgroup's 8 rows x 16 pairs of each output row block
-    // are 4 blocks of 8 rows x 4 pairs = 256 contiguous bytes each.  Outputs
-    // go through LDS 8 k at a time (16 row blocks with both halves) so that
-    // every store instruction writes two whole blocks.
-    __shared__ float2 stg[16][8][17];
-    const int rl = 2 * (int)(gw & 3) + (lane & 31) / 16, pl = lane & 15;
+  if constexpr (TILED) {
+    // The workgroup covers RWG = 4 RW rows x PWG = 32 / RW pairs; each output
+    // row block holds PWG / 4 blocks of RWG rows x 4 pairs (128 or 256
+    // contiguous bytes).  Outputs go through LDS 8 k at a time (16 row blocks
+    // with both halves) so that each store instruction writes whole blocks.
+    constexpr int RW = IN == IN_BF16 ? 1 : 2, RWG = 4 * RW, PWG = 32 / RW;
+    __shared__ float2 stg[16][RWG][PWG + 1];
+    const int rl = RW * (int)(gw & 3) + (lane & 31) / PWG, pl = (lane & 31) % PWG;
     const int tid = threadIdx.x;
     char* obase_wg = reinterpret_cast<char*>(p.out[blockIdx.y]) +
                      (o * R * step + (cp0 >> 2) * (p.inner * 4) + i0 * 4) * 8;
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
       for (int e2 = 0; e2 < 8; ++e2) {
         // element e = e2 * 256 + tid: pair pr, row r, block blk, local row block kl
         const int e = e2 * 256 + tid;
-        const int pr = e & 3, r = (e >> 2) & 7, blk = (e >> 5) & 3, kl = e >> 7;
+        const int pr = e & 3, r = (e >> 2) % RWG, blk = ((e >> 2) / RWG) % (PWG / 4), kl = e >> 7;
         const int k1 = k0 + (kl & 7) + R2 * (kl >> 3);
         *reinterpret_cast<float2*>(obase_wg + ((int64_t)k1 * step + blk * (p.inner * 4) + r * 4 + pr) * 8) =
             stg[kl][r][4 * blk + pr];
