@@ -111,6 +111,17 @@ def test_edge_shapes(B, L, H, D, dt, keep):
     check_full(w)
 
 
+@pytest.mark.timeout(600)
+def test_longest_supported_length():
+    """L = 3 * 2^20, the longest length the library plans: 64 x 48 x 1024,
+    whose 48-point second pass runs in place in row layout."""
+    import efficient_attention_fft_amd as sm
+    st, plan = sm.spectre_mix_plan(3 * 2 ** 20)
+    assert st == sm.SPECTRE_OK and plan == (64, 48, 1024)
+    w = workloads.custom(303, B=1, L=3 * 2 ** 20, H=1, D=32, keep_bins=3 * 2 ** 19 + 1)
+    check_full(w)
+
+
 def test_truncated_band_matches_zeroed_gate_on_gpu():
     w = workloads.custom(301, B=1, L=65536, H=2, D=64, keep_bins=8193)
     inp = workloads.make_inputs(w)
