@@ -143,7 +143,7 @@ def spectre_mix_trace_start(max_calls: int) -> int:
     return _lib.spectre_mix_trace_start(max_calls)
 
 
-def spectre_mix_trace_stop(max_kernels: int = 8):
+def spectre_mix_trace_stop(max_kernels: int = 40):
     """(status, [(kernel name, total ms over the traced calls)], calls traced)."""
     total = (ctypes.c_float * max_kernels)()
     nk, nc = ctypes.c_int(), ctypes.c_int()
