@@ -70,7 +70,7 @@ def kernel_bytes(name: str, w) -> int:
         import efficient_attention_fft_amd as sm
         _, (l1, l2, l3) = sm.spectre_mix_plan(w.L)
         folded = 0
-        if l1 in (48, 64) and l3 in (256, 1024):  # this launch also builds the gate table
+        if l3 in (256, 1024):  # multi-level square B kernel: this launch also builds the gate table
             folded = 4 * w.H * min(w.keep_bins, w.nbins) + 4 * w.H * w.L
         return 3 * N * s + 3 * spec + folded
     if name == "A2_fwd_strided":
@@ -78,15 +78,13 @@ def kernel_bytes(name: str, w) -> int:
     if name == "B_mid_lds":
         import efficient_attention_fft_amd as sm
         _, (l1, l2, l3) = sm.spectre_mix_plan(w.L)
-        if l3 in (256, 1024):
-            gate = 4 * w.H * w.L  # the gate table written by G_gate_table
-        if l1 == 1 and l2 == 1:
+        if l1 == 1 and l2 == 1:  # single level: the kept gate bins themselves
             return 3 * N * s + spec + gate
+        if l3 in (256, 1024):
+            gate = 4 * w.H * w.L  # the gate table A1's launch writes
         return 3 * spec + spec + gate
     if name == "C2_inv_strided":
         return 2 * spec
-    if name == "G_gate_table":
-        return 4 * w.H * min(w.keep_bins, w.nbins) + 4 * w.H * w.L
     if name == "C1_inv_norm":
         return spec + 2 * N * s + 8 * w.C
     if name == "C1_inv":
@@ -256,8 +254,6 @@ def _short(name: str) -> str:
     arguments: k_strided<R, IN, TW, SIGN>, k_strided_split<R, IN, TW>,
     k_final<R, DT, FUSE>); other kernels keep their own name."""
     import re
-    if "spectre::k_gate_table" in name:
-        return "G_gate_table"
     m = re.search(r"spectre::(k_\w+)<([^>]*)>", name)
     if not m:
         return "copy (calibration)" if "copyBuffer" in name else name[:60]
@@ -273,8 +269,6 @@ def _short(name: str) -> str:
         return "C1_inv_norm" if args[2] == "true" else "C1_inv"
     if kern == "k_layernorm":
         return "LN_norm"
-    if kern == "k_gate_table":
-        return "G_gate_table"
     return name[:60]
 
 

@@ -103,9 +103,9 @@ __device__ __forceinline__ float2 twiddle_lookup(const float2* __restrict__ tw, 
 // gtab[(h * ncol + c) * N + k3] = scale * G[h][min(f, L - f)] if that bin is
 // kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 * k3):
 // the gate of every bin in the order the square B kernel's lanes visit them,
-// so that 32 lanes of one column read 32 consecutive values.  Built by
-// extra workgroups of the first strided pass when that pass is the split
-// kernel, else by k_gate_table.
+// so that 32 lanes of one column read 32 consecutive values.  Built by an
+// extra grid plane of the first strided pass (multi-level plans only: a
+// single-level square kernel reads the gate itself).
 
 struct GateTabParams {
   const float* gate;  // [H][nbins]
@@ -127,10 +127,6 @@ __device__ __forceinline__ void gate_table_fill(const GateTabParams& p, int64_t 
     const int64_t fc = f < p.L - f ? f : p.L - f;
     p.gtab[idx] = fc < p.keep ? p.gate[(int64_t)h * p.nbins + fc] * p.scale : 0.f;
   }
-}
-
-__global__ __launch_bounds__(256) void k_gate_table(GateTabParams p) {
-  gate_table_fill(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
 
 // ------------------------------------------------------ strided DFT passes
@@ -398,7 +394,8 @@ struct MidParams {
   const void* in[3];     // q, k, v sources (raw tensors, or the A-pass output)
   float2* out;           // inverse output (may alias in[0])
   const float* gate;     // [H][nbins]
-  const float* gtab;     // k_mid_sq: [H][ncol][N] gate table (scale, truncation, mirror folded in)
+  const float* gtab;     // k_mid_sq: [H][ncol][N] gate table (scale, truncation, mirror folded
+                         // in), or null for a single-level plan, which reads gate directly
   int ncol;              // columns per batch element, L1 * L2
   int tiled;             // k_mid_sq: in[] laid out [b][column][CP2 / 4][N][4] (see k_strided_split)
   const float2* twN;     // twN[e] = exp(-2 pi i e / N), e < N
@@ -793,8 +790,18 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 #pragma unroll
       for (int u = 0; u <= H2; ++u) {
         const float2 z = v[u], zm = mirror(u);
-        const float ga = gta[R * u];
-        const float gb = ha == hb ? ga : gtb[R * u];
+        float ga, gb;
+        if constexpr (IN == IN_C32) {  // multi-level: the gate table
+          ga = gta[R * u];
+          gb = ha == hb ? ga : gtb[R * u];
+        } else {  // raw inputs, one column (single level): bin k1 + R u, from the gate itself
+          const int f = k1 + R * u;
+          const int fc = min(f, p.L - f);
+          const bool kept = fc < p.keep;
+          const int gi = kept ? fc : 0;
+          ga = kept ? p.gate[ha * p.nbins + gi] * p.scale : 0.f;
+          gb = kept ? p.gate[hb * p.nbins + gi] * p.scale : 0.f;
+        }
         const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), ga);
         const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), gb);
         sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);

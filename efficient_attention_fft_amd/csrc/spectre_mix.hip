@@ -393,10 +393,10 @@ size_t spectra_bytes(const Shape& s, const Plan& pl, bool want_fwd) {
   return (tiled3_plan(s, pl) ? 24 : tiled_plan(s, pl) ? 16 : 12) * n;
 }
 
-// Bytes of the gate table the square B kernel reads (H * L binary32 values,
-// in its own bin order), 0 when the plan uses the generic B kernel.
+// Bytes of the gate table the square B kernel of a multi-level plan reads
+// (H * L binary32 values, in its own bin order), else 0.
 size_t gate_table_bytes(const Shape& s, const Plan& pl) {
-  return pl.sq ? (size_t)4 * s.H * s.L : 0;
+  return pl.sq && !is_single(pl) ? (size_t)4 * s.H * s.L : 0;
 }
 
 size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
@@ -503,13 +503,6 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
   const size_t lds = (size_t)p.N * p.nslot * p.cpt * sizeof(float2);
   hipLaunchKernelGGL((k_mid<P, IN>), grid, dim3(threads), lds, st, p);
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
-  return SPECTRE_OK;
-}
-
-int launch_gate_table(const GateTabParams& g, hipStream_t st) {
-  const int64_t blocks = std::min<int64_t>((g.total + 255) / 256, 8192);  // grid-stride beyond
-  hipLaunchKernelGGL(k_gate_table, dim3((unsigned)blocks), dim3(256), 0, st, g);
-  SPECTRE_LAUNCH_CHECK("G_gate_table");
   return SPECTRE_OK;
 }
 
@@ -630,7 +623,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   // bin folded in, laid out [h][column][k3] so B's lanes read it coalesced;
   // built by an extra grid plane of the first pass for multi-level plans
   GateTabParams g{};
-  if (pl.sq) {
+  if (pl.sq && !single) {
     g.gate = gate;
     g.gtab = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                       ((spectra_bytes(s, pl, want_out) + 255) & ~(size_t)255));
@@ -644,11 +637,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     g.total = s.H * s.L;
     g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
   }
-  const bool gate_in_a1 = g.gtab && !single;
-  if (g.gtab && !gate_in_a1) {
-    rc = launch_gate_table(g, st);
-    if (rc) return rc;
-  }
+  const bool gate_in_a1 = g.gtab != nullptr;  // multi-level square B: A1 builds the table
 
   // ---- forward strided passes
   if (!single) {

@@ -130,8 +130,8 @@ def test_workspace_bytes():
     assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 16 * 4 * 4096 * 512 + 4 * 8 * 4096
     # L = 2048: single level, generic LDS kernel, y only, no gate table
     assert sm.spectre_mix_workspace_bytes(4, 8, 2048, 64, 0) == 4 * 4 * 2048 * 512
-    # L = 256: single level, square kernel with its gate table
-    assert sm.spectre_mix_workspace_bytes(1, 2, 256, 16, 0) == 4 * 256 * 32 + 4 * 2 * 256
+    # L = 256: single level, square kernel reading the gate itself (no table)
+    assert sm.spectre_mix_workspace_bytes(1, 2, 256, 16, 0) == 4 * 256 * 32
     assert sm.spectre_mix_workspace_bytes(1, 8, 65535, 64, 0) == 0
 
 
