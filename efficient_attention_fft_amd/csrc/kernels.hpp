@@ -42,6 +42,19 @@ enum InKind { IN_F32 = 0, IN_BF16 = 1, IN_C32 = 2 };
 enum TwKind { TW_NONE = 0, TW_A1 = 1, TW_A2 = 2, TW_C2 = 3 };
 
 // ------------------------------------------------------------- storage I/O
+//
+// Every tensor and spectrum is read exactly once per call, so all of them
+// are loaded nontemporally: the read stream then does not push out of L2
+// the lines that the row-layout stores of the LDS pass fill piece by piece
+// (those pieces come from several workgroups; a line evicted half written
+// costs a partial write to HBM).  Tables (twiddles, gate) use plain loads.
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float2 load_nt(const float2* p) {
+  const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+  return make_float2(v.x, v.y);
+}
 
 // One channel pair at complex-element offset `off`: (ch 2j, ch 2j+1).
 template <int IN>
@@ -50,7 +63,7 @@ __device__ __forceinline__ float2 load_pair(const void* base, int64_t off) {
     uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base) + off);
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
   } else {
-    return reinterpret_cast<const float2*>(base)[off];
+    return load_nt(reinterpret_cast<const float2*>(base) + off);
   }
 }
 
@@ -70,7 +83,7 @@ __device__ __forceinline__ float2 load_pair_u(const char* ubase, uint32_t off) {
     uint32_t u = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ubase + off));
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
   } else {
-    return *reinterpret_cast<const float2*>(ubase + off);
+    return load_nt(reinterpret_cast<const float2*>(ubase + off));
   }
 }
 
@@ -930,7 +943,7 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
   float2 z[R];
   const int64_t ubase = (b * R * p.M + m) * p.CP2 + cp;
 #pragma unroll
-  for (int r = 0; r < R; ++r) z[r] = p.U[ubase + (int64_t)r * p.M * p.CP2];
+  for (int r = 0; r < R; ++r) z[r] = load_nt(p.U + ubase + (int64_t)r * p.M * p.CP2);
   dft<R, +1>(z);
 
   // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
@@ -1033,7 +1046,7 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
     const float2* u = p.U + ((b * R + h) * p.M + m) * p.CP2 + cp;
     const int64_t rs = 2 * p.M * p.CP2;  // rows 2a + h
 #pragma unroll
-    for (int a = 0; a < R2; ++a) z[a] = u[a * rs];
+    for (int a = 0; a < R2; ++a) z[a] = load_nt(u + a * rs);
   }
   dft<R2, +1>(z);
   join_swap<R, +1>(z, h);
@@ -1124,7 +1137,7 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
   for (int it = 0; it < MAXIT; ++it) {
     const int64_t c = lane + 64 * it;
     if (c < p.CP2) {
-      z[it] = cadd(p.y[base + c], load_pair<DT>(p.x, base + c));
+      z[it] = cadd(load_nt(p.y + base + c), load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
   }
