@@ -545,6 +545,24 @@ __device__ __forceinline__ int3 xcd_grouped_block() {
   return make_int3((int)(lin % gx), (int)((lin / gx) % gy), (int)(lin / (gx * gy)));
 }
 
+// Block order for the multi-level square B pass, whose workgroup writes 32
+// bytes (4 channel pairs) of each output row: the 4 workgroups that fill
+// one 128-byte line (channel-pair blocks 4 q .. 4 q + 3 of one column pair)
+// get ids 8 apart, so they run on one XCD one after another and the line is
+// whole before L2 evicts it.  Groups of 4 go to the XCDs round-robin.
+// Needs gridDim.y % 4 == 0 and a grid size that is a multiple of 32;
+// otherwise the natural order.
+__device__ __forceinline__ int3 sharer_grouped_block() {
+  const unsigned gx = gridDim.x, gy = gridDim.y;
+  const unsigned total = gx * gy * gridDim.z;
+  if (gy % 4 != 0 || total % 32 != 0) return make_int3((int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
+  const unsigned lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const unsigned w = (lin / 8) % 4;             // position in the group
+  const unsigned g = lin % 8 + 8 * (lin / 32);  // group: one column pair, 4 channel-pair blocks
+  const unsigned rest = g / gx, yq = gy / 4;
+  return make_int3((int)(g % gx), (int)(4 * (rest % yq) + w), (int)(rest / yq));
+}
+
 template <int P, int IN>
 __global__ __launch_bounds__(512) void k_mid(MidParams p) {
   extern __shared__ float2 lds[];
@@ -678,6 +696,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int H2 = R / 2;
   extern __shared__ float2 lds[];
   const int3 blk = p.nslot == 1 ? xcd_grouped_block()
+                  : p.cpt == 4  ? sharer_grouped_block()
                                 : make_int3((int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
   const int ncols = p.nslot * p.cpt;
   const int ROW = R * ncols + 1;  // padded: stage-2 lanes stride ROW, an odd count
