@@ -682,6 +682,11 @@ __global__ __launch_bounds__(512) void k_mid(MidParams p) {
 // The inverse runs the split backwards: stage-2 lanes transform along k2,
 // twiddle w_N^{-k1 n}, LDS transpose, stage-1 lanes transform along k1 and
 // hold z[t + R i] -- the input distribution -- for coalesced stores.
+//
+// GL (multi-level plans whose workgroup's channel pairs share one head): the
+// workgroup's gate values, nslot x (R/2 + 1) x R of the table, are copied to
+// LDS during the first tensor, so the product reads them from LDS instead of
+// waiting on global loads.
 
 __device__ __forceinline__ float lane_pull(float v, int src_byte) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src_byte, __float_as_int(v)));
@@ -690,7 +695,7 @@ __device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
   return make_float2(lane_pull(v.x, src_byte), lane_pull(v.y, src_byte));
 }
 
-template <int R, int IN>
+template <int R, int IN, bool GL = false>
 __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int N = R * R;
   constexpr int H2 = R / 2;
@@ -701,6 +706,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   const int ncols = p.nslot * p.cpt;
   const int ROW = R * ncols + 1;  // padded: stage-2 lanes stride ROW, an odd count
   float2* twl = lds + R * ROW;     // the N-point twiddles, copied from p.twN
+  float* gl = reinterpret_cast<float*>(twl + N);  // GL: gate values [slot][u <= R/2][k1]
   const int tid = threadIdx.x;
 
   // stage-1 / stage-3 identity
@@ -779,6 +785,14 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
     }
     if (x == 0) {
       for (int e = tid; e < N; e += R * ncols) twl[e] = p.twN[e];
+      if constexpr (GL) {
+        const int hw = (2 * blk.y * p.cpt) / p.D;  // the workgroup's head
+        for (int e = tid; e < p.nslot * (H2 + 1) * R; e += R * ncols) {
+          const int sl = e / ((H2 + 1) * R), u = (e / R) % (H2 + 1), kk = e % R;
+          const int c = sl == 0 ? cols.x : cols.y;
+          gl[e] = p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u];
+        }
+      }
       __syncthreads();
     }
     dft<R, -1>(v);
@@ -823,7 +837,10 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
       for (int u = 0; u <= H2; ++u) {
         const float2 z = v[u], zm = mirror(u);
         float ga, gb;
-        if constexpr (IN == IN_C32) {  // multi-level: the gate table
+        if constexpr (GL) {
+          ga = gl[(s2 * (H2 + 1) + u) * R + k1];
+          gb = ga;
+        } else if constexpr (IN == IN_C32) {  // multi-level: the gate table
           ga = gta[R * u];
           gb = ha == hb ? ga : gtb[R * u];
         } else {  // raw inputs, one column (single level): bin k1 + R u, from the gate itself

@@ -509,15 +509,22 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
 template <int R, int IN>
 int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
   const int ncols = p.nslot * p.cpt;
-  const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2);
-  static bool attr_set = false;  // guarded by g_mu
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_sq<R, IN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+  // gate values in LDS when every workgroup's channel pairs lie in one head
+  const bool gl = IN == IN_C32 && p.gtab != nullptr && p.D % 2 == 0 && (p.D / 2) % p.cpt == 0;
+  const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
+                     (gl ? (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float) : 0);
+  static bool attr_set[2] = {false, false};  // guarded by g_mu
+  const void* fn = gl ? reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>)
+                      : reinterpret_cast<const void*>(&k_mid_sq<R, IN, false>);
+  if (!attr_set[gl]) {
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SPECTRE_EHIP;
-    attr_set = true;
+    attr_set[gl] = true;
   }
-  hipLaunchKernelGGL((k_mid_sq<R, IN>), grid, dim3(R * ncols), lds, st, p);
+  if (gl)
+    hipLaunchKernelGGL((k_mid_sq<R, IN, true>), grid, dim3(R * ncols), lds, st, p);
+  else
+    hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
   return SPECTRE_OK;
 }
