@@ -695,7 +695,7 @@ __device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
   return make_float2(lane_pull(v.x, src_byte), lane_pull(v.y, src_byte));
 }
 
-template <int R, int IN, bool GL = false>
+template <int R, int IN, bool GL = false, bool DMA = false>
 __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int N = R * R;
   constexpr int H2 = R / 2;
@@ -762,6 +762,55 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   float2 v[R];
   float2 sa[H2 + 1], sb[H2 + 1];
 
+  // DMA (tiled input, two slots of 4 channel pairs): each slot's input block
+  // (N rows x 4 pairs, 32 KB contiguous) is copied global -> LDS by
+  // asynchronous 16-byte-per-lane loads into the transpose buffer, slot 1 at
+  // a 128-byte offset so that the two slots' reads fall in different banks.
+  // Tensor x + 1's copy is issued once tensor x's stage-2 reads are done and
+  // runs under its stage-2 DFT and spectral product.
+  constexpr int kSlot = 4 * N + 16;  // float2 between the slots' blocks
+  auto dma_tile = [&](int x) __attribute__((always_inline)) {
+    // wave-uniform parts (scalar registers): block base and the wave's 1 KB
+    // row of each 4 KB round; the lane adds 16 bytes per lane
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lane_off = (uint32_t)(tid & 63) * 16;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int c = sl == 0 ? cols.x : cols.y;
+      if (c < 0) continue;
+      const char* g = reinterpret_cast<const char*>(p.in[x]) +
+                      (batch_pair + (int64_t)((c % p.L1) * p.M + (c / p.L1) * N) * p.CP2 +
+                       (int64_t)blk.y * (N * 4)) * 8 + wv * 1024;
+      char* l = reinterpret_cast<char*>(lds + sl * kSlot) + wv * 1024;
+#pragma unroll
+      for (int q = 0; q < (N * 32) / 4096; ++q)
+        __builtin_amdgcn_global_load_lds(g + q * 4096 + lane_off, l + q * 4096, 16, 0, 2 /* nontemporal */);
+    }
+  };
+  if constexpr (DMA) {
+    // the tables' loads go out first, all at once, then q's block copy
+    constexpr int NT = 256;  // R * ncols for this variant
+    constexpr int NGL = 2 * (H2 + 1) * R;
+    float2 tv[N / NT];
+    float gv[(NGL + NT - 1) / NT];
+    const int hw = (2 * blk.y * p.cpt) / p.D;
+#pragma unroll
+    for (int r = 0; r < N / NT; ++r) tv[r] = p.twN[tid + NT * r];
+#pragma unroll
+    for (int r = 0; r < (NGL + NT - 1) / NT; ++r) {
+      const int e = tid + NT * r;
+      const int sl = e / ((H2 + 1) * R), u = (e / R) % (H2 + 1), kk = e % R;
+      const int c = sl == 0 ? cols.x : cols.y;
+      gv[r] = e < NGL ? p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u] : 0.f;
+    }
+    dma_tile(0);
+#pragma unroll
+    for (int r = 0; r < N / NT; ++r) twl[tid + NT * r] = tv[r];
+#pragma unroll
+    for (int r = 0; r < (NGL + NT - 1) / NT; ++r)
+      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+  }
+
 #pragma unroll 1
   for (int x = 0; x < 3; ++x) {
     // values only one phase needs are made opaque per iteration, so they are
@@ -772,7 +821,19 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
     int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
     asm volatile("" : "+v"(gta), "+v"(gtb), "+v"(t1o));
     // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
-    {
+    if constexpr (DMA) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+      __syncthreads();                // and every other wave's
+      if (active1) {
+        const float2* raw = lds + s1 * kSlot + t1 * 4 + j1;
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = raw[i * R * 4];
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
+      }
+      __syncthreads();  // the block is read before the transpose overwrites it
+    } else {
       const char* src = reinterpret_cast<const char*>(p.in[x]) + batch_pair * pair_bytes<IN>();
       const uint32_t off = in_pair * pair_bytes<IN>();
       if (active1) {
@@ -783,7 +844,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
         for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
       }
     }
-    if (x == 0) {
+    if (!DMA && x == 0) {
       for (int e = tid; e < N; e += R * ncols) twl[e] = p.twN[e];
       if constexpr (GL) {
         const int hw = (2 * blk.y * p.cpt) / p.D;  // the workgroup's head
@@ -798,13 +859,19 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
     dft<R, -1>(v);
 #pragma unroll
     for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twl[t1o * k]);
-    __syncthreads();
+    if constexpr (!DMA) __syncthreads();
 #pragma unroll
     for (int k = 0; k < R; ++k) lds[k * ROW + t1 * ncols + col1] = v[k];
     __syncthreads();
     // ---- stage 2: DFT over t -> X[k1 + R k2]
 #pragma unroll
     for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * ncols + col2];
+    if constexpr (DMA) {
+      if (x < 2) {
+        __syncthreads();  // the transpose buffer is free: fetch the next tensor
+        dma_tile(x + 1);
+      }
+    }
     dft<R, -1>(v);
 
     // ---- split the packed spectra and accumulate / finish the product.

@@ -513,18 +513,30 @@ int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
   const bool gl = IN == IN_C32 && p.gtab != nullptr && p.D % 2 == 0 && (p.D / 2) % p.cpt == 0;
   const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
                      (gl ? (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float) : 0);
-  static bool attr_set[2] = {false, false};  // guarded by g_mu
-  const void* fn = gl ? reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>)
-                      : reinterpret_cast<const void*>(&k_mid_sq<R, IN, false>);
-  if (!attr_set[gl]) {
+  // input blocks copied to LDS asynchronously: tiled input, two slots of 4 pairs
+  const bool dma = gl && R == 32 && p.tiled && p.nslot == 2 && p.cpt == 4;
+  static bool attr_set[3] = {false, false, false};  // guarded by g_mu
+  const int kind = dma ? 2 : gl ? 1 : 0;
+  const void* fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, false>);
+  if constexpr (IN == IN_C32) {
+    if (kind == 2) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true, true>);
+    if (kind == 1) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>);
+  }
+  if (!attr_set[kind]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SPECTRE_EHIP;
-    attr_set[gl] = true;
+    attr_set[kind] = true;
   }
-  if (gl)
-    hipLaunchKernelGGL((k_mid_sq<R, IN, true>), grid, dim3(R * ncols), lds, st, p);
-  else
+  if constexpr (IN == IN_C32) {
+    if (kind == 2)
+      hipLaunchKernelGGL((k_mid_sq<R, IN, true, true>), grid, dim3(R * ncols), lds, st, p);
+    else if (kind == 1)
+      hipLaunchKernelGGL((k_mid_sq<R, IN, true>), grid, dim3(R * ncols), lds, st, p);
+    else
+      hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
+  } else {
     hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
+  }
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
   return SPECTRE_OK;
 }
