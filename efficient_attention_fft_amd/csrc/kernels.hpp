@@ -420,6 +420,7 @@ struct MidParams {
   int nrad;
   int rad[8];            // Stockham radices, product N
   float scale;           // 1 / (8 L^2): the mix's 1/L, the inverse's 1/L, the (1/2)^3 of the split
+  int gx, gy, gz;        // k_mid_dma: the work items (column pairs, channel-pair blocks, batch)
 };
 
 // One Stockham autosort pass of radix R over the LDS-resident columns.
@@ -552,15 +553,19 @@ __device__ __forceinline__ int3 xcd_grouped_block() {
 // whole before L2 evicts it.  Groups of 4 go to the XCDs round-robin.
 // Needs gridDim.y % 4 == 0 and a grid size that is a multiple of 32;
 // otherwise the natural order.
-__device__ __forceinline__ int3 sharer_grouped_block() {
-  const unsigned gx = gridDim.x, gy = gridDim.y;
-  const unsigned total = gx * gy * gridDim.z;
-  if (gy % 4 != 0 || total % 32 != 0) return make_int3((int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z);
-  const unsigned lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+__device__ __forceinline__ int3 sharer_block_of(unsigned lin, unsigned gx, unsigned gy, unsigned gz) {
+  const unsigned total = gx * gy * gz;
+  if (gy % 4 != 0 || total % 32 != 0)
+    return make_int3((int)(lin % gx), (int)((lin / gx) % gy), (int)(lin / (gx * gy)));
   const unsigned w = (lin / 8) % 4;             // position in the group
   const unsigned g = lin % 8 + 8 * (lin / 32);  // group: one column pair, 4 channel-pair blocks
   const unsigned rest = g / gx, yq = gy / 4;
   return make_int3((int)(g % gx), (int)(4 * (rest % yq) + w), (int)(rest / yq));
+}
+
+__device__ __forceinline__ int3 sharer_grouped_block() {
+  return sharer_block_of(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x,
+                         gridDim.y, gridDim.z);
 }
 
 template <int P, int IN>
@@ -695,7 +700,7 @@ __device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
   return make_float2(lane_pull(v.x, src_byte), lane_pull(v.y, src_byte));
 }
 
-template <int R, int IN, bool GL = false, bool DMA = false>
+template <int R, int IN, bool GL = false>
 __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int N = R * R;
   constexpr int H2 = R / 2;
@@ -762,55 +767,6 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   float2 v[R];
   float2 sa[H2 + 1], sb[H2 + 1];
 
-  // DMA (tiled input, two slots of 4 channel pairs): each slot's input block
-  // (N rows x 4 pairs, 32 KB contiguous) is copied global -> LDS by
-  // asynchronous 16-byte-per-lane loads into the transpose buffer, slot 1 at
-  // a 128-byte offset so that the two slots' reads fall in different banks.
-  // Tensor x + 1's copy is issued once tensor x's stage-2 reads are done and
-  // runs under its stage-2 DFT and spectral product.
-  constexpr int kSlot = 4 * N + 16;  // float2 between the slots' blocks
-  auto dma_tile = [&](int x) __attribute__((always_inline)) {
-    // wave-uniform parts (scalar registers): block base and the wave's 1 KB
-    // row of each 4 KB round; the lane adds 16 bytes per lane
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t lane_off = (uint32_t)(tid & 63) * 16;
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int c = sl == 0 ? cols.x : cols.y;
-      if (c < 0) continue;
-      const char* g = reinterpret_cast<const char*>(p.in[x]) +
-                      (batch_pair + (int64_t)((c % p.L1) * p.M + (c / p.L1) * N) * p.CP2 +
-                       (int64_t)blk.y * (N * 4)) * 8 + wv * 1024;
-      char* l = reinterpret_cast<char*>(lds + sl * kSlot) + wv * 1024;
-#pragma unroll
-      for (int q = 0; q < (N * 32) / 4096; ++q)
-        __builtin_amdgcn_global_load_lds(g + q * 4096 + lane_off, l + q * 4096, 16, 0, 2 /* nontemporal */);
-    }
-  };
-  if constexpr (DMA) {
-    // the tables' loads go out first, all at once, then q's block copy
-    constexpr int NT = 256;  // R * ncols for this variant
-    constexpr int NGL = 2 * (H2 + 1) * R;
-    float2 tv[N / NT];
-    float gv[(NGL + NT - 1) / NT];
-    const int hw = (2 * blk.y * p.cpt) / p.D;
-#pragma unroll
-    for (int r = 0; r < N / NT; ++r) tv[r] = p.twN[tid + NT * r];
-#pragma unroll
-    for (int r = 0; r < (NGL + NT - 1) / NT; ++r) {
-      const int e = tid + NT * r;
-      const int sl = e / ((H2 + 1) * R), u = (e / R) % (H2 + 1), kk = e % R;
-      const int c = sl == 0 ? cols.x : cols.y;
-      gv[r] = e < NGL ? p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u] : 0.f;
-    }
-    dma_tile(0);
-#pragma unroll
-    for (int r = 0; r < N / NT; ++r) twl[tid + NT * r] = tv[r];
-#pragma unroll
-    for (int r = 0; r < (NGL + NT - 1) / NT; ++r)
-      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
-  }
-
 #pragma unroll 1
   for (int x = 0; x < 3; ++x) {
     // values only one phase needs are made opaque per iteration, so they are
@@ -821,19 +777,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
     int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
     asm volatile("" : "+v"(gta), "+v"(gtb), "+v"(t1o));
     // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
-    if constexpr (DMA) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
-      __syncthreads();                // and every other wave's
-      if (active1) {
-        const float2* raw = lds + s1 * kSlot + t1 * 4 + j1;
-#pragma unroll
-        for (int i = 0; i < R; ++i) v[i] = raw[i * R * 4];
-      } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
-      }
-      __syncthreads();  // the block is read before the transpose overwrites it
-    } else {
+    {
       const char* src = reinterpret_cast<const char*>(p.in[x]) + batch_pair * pair_bytes<IN>();
       const uint32_t off = in_pair * pair_bytes<IN>();
       if (active1) {
@@ -844,7 +788,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
         for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
       }
     }
-    if (!DMA && x == 0) {
+    if (x == 0) {
       for (int e = tid; e < N; e += R * ncols) twl[e] = p.twN[e];
       if constexpr (GL) {
         const int hw = (2 * blk.y * p.cpt) / p.D;  // the workgroup's head
@@ -859,19 +803,13 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
     dft<R, -1>(v);
 #pragma unroll
     for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twl[t1o * k]);
-    if constexpr (!DMA) __syncthreads();
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < R; ++k) lds[k * ROW + t1 * ncols + col1] = v[k];
     __syncthreads();
     // ---- stage 2: DFT over t -> X[k1 + R k2]
 #pragma unroll
     for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * ncols + col2];
-    if constexpr (DMA) {
-      if (x < 2) {
-        __syncthreads();  // the transpose buffer is free: fetch the next tensor
-        dma_tile(x + 1);
-      }
-    }
     dft<R, -1>(v);
 
     // ---- split the packed spectra and accumulate / finish the product.
@@ -967,6 +905,267 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
       *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) = cmul(v[i], cconj(cmul(tws[j], step)));
     }
     step = cmul(step, tw4r);
+  }
+}
+
+// ------------------------- B, N = 1024, tiled input: LDS copies, persistent
+//
+// The square pass for R = 32 when its input is in the tiled layout and a
+// workgroup holds two slots (a column and its mirror) of 4 channel pairs
+// whose gate values share one head.  The arithmetic and the lane mappings
+// are those of k_mid_sq; the data movement differs:
+//  - each slot's input block (N rows x 4 pairs, 32 KB contiguous) is copied
+//    global -> LDS by 16-byte-per-lane asynchronous loads (global_load_lds)
+//    into the transpose buffer, slot 1 at a 128-byte offset so the two
+//    slots' reads fall in different banks, and stage 1 reads its strided
+//    elements from there;
+//  - tensor x + 1's copy is issued as soon as tensor x's stage-2 reads are
+//    done, and runs under its stage-2 DFT and spectral product;
+//  - a workgroup takes several work items: w, w + gridDim.x, ... (with the
+//    grid a multiple of 8 an item's XCD is its index mod 8, as for one item
+//    per workgroup), and the next item's q copy runs under this item's last
+//    inverse DFT and its stores.
+// Every wave issues the same sequence of memory operations (each wave has
+// active slot-0 lanes), so a wave's vmcnt counts are exact: at the top of an
+// item, the 32 stores of the previous one may still be in flight.
+
+__device__ __forceinline__ void wait_vmcnt_32() {
+  __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | 0x0F70);  // vmcnt(32)
+}
+
+__global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
+  constexpr int R = 32, N = R * R, H2 = R / 2, NT = 256, ROW = R * 8 + 1;
+  constexpr int kSlot = 4 * N + 16;          // float2 between the slots' blocks
+  constexpr int NGL = 2 * (H2 + 1) * R;      // gate values per item
+  constexpr int NGR = (NGL + NT - 1) / NT;
+  extern __shared__ float2 lds[];
+  float2* twl = lds + R * ROW;                         // w_N^e, e < N
+  float* gl = reinterpret_cast<float*>(twl + N);       // gate values [slot][u <= R/2][k1]
+  const int tid = threadIdx.x;
+  // stage-1 / stage-3 identity: thread (t1, col1), col1 = slot * 4 + pair
+  const int col1 = tid & 7, t1 = tid >> 3, s1 = col1 >> 2, j1 = col1 & 3;
+  // stage-2 identity: thread (j2, s2, k1)
+  const int j2 = tid >> 6, s2 = (tid >> 5) & 1, k1 = tid & 31, col2 = s2 * 4 + j2;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lane16 = (uint32_t)(tid & 63) * 16;
+  const int ntile = p.gx * p.gy * p.gz;
+
+  // work item -> (column pair, channel-pair block, batch), wave-uniform, and
+  // its columns (scalar loads)
+  auto item = [&](int t) __attribute__((always_inline)) {
+    const int3 g = sharer_block_of(t, p.gx, p.gy, p.gz);
+    return make_int3(__builtin_amdgcn_readfirstlane(g.x), __builtin_amdgcn_readfirstlane(g.y),
+                     __builtin_amdgcn_readfirstlane(g.z));
+  };
+  auto copy_block = [&](const void* src, int3 blk, int2 cols) __attribute__((always_inline)) {
+    const int64_t bp = (int64_t)blk.z * p.L * p.CP2;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int c = sl == 0 ? cols.x : cols.y;
+      if (c < 0) continue;
+      const char* g = reinterpret_cast<const char*>(src) +
+                      (bp + (int64_t)((c % p.L1) * p.M + (c / p.L1) * N) * p.CP2 + (int64_t)blk.y * (N * 4)) * 8 +
+                      wv * 1024;
+      char* l = reinterpret_cast<char*>(lds + sl * kSlot) + wv * 1024;
+#pragma unroll
+      for (int q = 0; q < (N * 32) / 4096; ++q)
+        __builtin_amdgcn_global_load_lds(g + q * 4096 + lane16, l + q * 4096, 16, 0, 2 /* nontemporal */);
+    }
+  };
+  auto gate_load = [&](int3 blk, int2 cols, float* gv) __attribute__((always_inline)) {
+    const int hw = (2 * blk.y * 4) / p.D;  // the item's head
+#pragma unroll
+    for (int r = 0; r < NGR; ++r) {
+      const int e = min(tid + NT * r, NGL - 1);
+      const int sl = e / ((H2 + 1) * R), u = (e / R) % (H2 + 1), kk = e % R;
+      const int c = sl == 0 ? cols.x : cols.y;
+      gv[r] = p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u];
+    }
+  };
+
+  int tile = blockIdx.x;
+  if (tile >= ntile) return;
+  int3 blk = item(tile);
+  int2 cols = p.wgcols[blk.x];
+  float gv[NGR];
+  {
+    float2 tv[N / NT];
+#pragma unroll
+    for (int r = 0; r < N / NT; ++r) tv[r] = p.twN[tid + NT * r];
+    gate_load(blk, cols, gv);
+    copy_block(p.in[0], blk, cols);
+#pragma unroll
+    for (int r = 0; r < N / NT; ++r) twl[tid + NT * r] = tv[r];
+#pragma unroll
+    for (int r = 0; r < NGR; ++r)
+      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+  }
+  bool first = true;
+  float2 v[R];
+  float2 sa[H2 + 1], sb[H2 + 1];
+
+#pragma unroll 1
+  while (true) {
+    // the next item; its columns and gate values are loaded during this one
+    const int next = tile + (int)gridDim.x;
+    const bool more = next < ntile;
+    const int3 nblk = more ? item(next) : blk;
+    int2 ncols_v = make_int2(0, 0);
+    // ---- this item's identity
+    const bool regular = blk.x != p.selfwg;
+    int ps, pk1;
+    bool a_zero = false;
+    if (regular) {
+      ps = 1 - s2;
+      pk1 = R - 1 - k1;
+    } else {
+      ps = s2;
+      a_zero = s2 == 0;
+      pk1 = a_zero ? (R - k1) % R : R - 1 - k1;
+    }
+    const int partner_byte = (((j2 * 64 + ps * R + pk1) & 63) << 2);
+    const bool special = a_zero && k1 == 0;
+    const int colid1 = s1 == 0 ? cols.x : cols.y;
+    const bool active1 = colid1 >= 0;
+
+#pragma unroll 1
+    for (int x = 0; x < 3; ++x) {
+      int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
+      asm volatile("" : "+v"(t1o));
+      // ---- stage 1 input: this wave's copies have landed (at the top of an
+      // item, the previous item's 32 stores may still be in flight), then
+      // every other wave's
+      if (x == 0 && !first)
+        wait_vmcnt_32();
+      else
+        __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (active1) {
+        const float2* raw = lds + s1 * kSlot + t1 * 4 + j1;
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = raw[i * R * 4];
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
+      }
+      // the next item's columns (a vector load: the top of the next tensor
+      // waits for it), then its gate values, both used at the end of the item
+      if (x == 0) ncols_v = p.wgcols[nblk.x];
+      if (x == 1) gate_load(nblk, ncols_v, gv);
+      __syncthreads();  // the blocks are read before the transpose overwrites them
+      // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
+      dft<R, -1>(v);
+#pragma unroll
+      for (int k = 1; k < R; ++k) v[k] = cmul(v[k], twl[t1o * k]);
+#pragma unroll
+      for (int k = 0; k < R; ++k) lds[k * ROW + t1 * 8 + col1] = v[k];
+      __syncthreads();
+      // ---- stage 2: DFT over t -> X[k1 + R k2]
+#pragma unroll
+      for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * 8 + col2];
+      if (x < 2) {
+        __syncthreads();  // the transpose buffer is free: fetch the next tensor
+        copy_block(p.in[x + 1], blk, cols);
+      }
+      dft<R, -1>(v);
+
+      // ---- split the packed spectra and accumulate / finish the product
+      // (the same arithmetic as k_mid_sq)
+      auto mirror = [&](int u) -> float2 {
+        if (u == H2) return v[H2];
+        const float2 pulled = lane_pull2(v[R - 1 - u], partner_byte);
+        return special ? v[(R - u) % R] : pulled;
+      };
+      if (x == 0) {
+#pragma unroll
+        for (int u = 0; u <= H2; ++u) {
+          const float2 z = v[u], zm = mirror(u);
+          sa[u] = make_float2(z.x + zm.x, z.y - zm.y);
+          sb[u] = make_float2(z.y + zm.y, zm.x - z.x);
+        }
+      } else if (x == 1) {
+#pragma unroll
+        for (int u = 0; u <= H2; ++u) {
+          const float2 z = v[u], zm = mirror(u);
+          sa[u] = cmulc(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+          sb[u] = cmulc(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u <= H2; ++u) {
+          const float2 z = v[u], zm = mirror(u);
+          const float g = gl[(s2 * (H2 + 1) + u) * R + k1];
+          const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), g);
+          const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), g);
+          sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
+          sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
+        }
+      }
+    }
+    // ---- W back into this lane's own bins k2 = 0 .. R-1
+#pragma unroll
+    for (int u = 0; u < H2; ++u) v[u] = sa[u];
+#pragma unroll
+    for (int q = 0; q < H2; ++q) {
+      const float2 pulled = lane_pull2(sb[H2 - 1 - q], partner_byte);
+      v[H2 + q] = special ? (q == 0 ? sa[H2] : sb[H2 - q]) : pulled;
+    }
+    // ---- inverse, stage 2 lanes: along k2, twiddle w_N^{-k1 n}
+    int k1o = k1;
+    asm volatile("" : "+v"(k1o));
+    dft<R, +1>(v);
+#pragma unroll
+    for (int n = 1; n < R; ++n) v[n] = cmul(v[n], cconj(twl[k1o * n]));
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < R; ++n) lds[k1 * ROW + n * 8 + col2] = v[n];
+    // the next item's gate values (every wave has read this item's)
+#pragma unroll
+    for (int r = 0; r < NGR; ++r)
+      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+    // output twiddle w^-(m3 tw_mul), w = w_L, for m3 = t1 + R i, i = 4 a + j:
+    // the seeds w^(t1 + R j), j < 4, times (w^(4 R))^a; loaded before the
+    // next item's copy so that waiting for them does not wait for it
+    const int kc1 = active1 ? colid1 % p.L1 : 0, k2c1 = active1 ? colid1 / p.L1 : 0;
+    const int tw_mul = p.L1 * k2c1 + (p.L2 == 1 ? kc1 : 0);
+    float2 tws[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tws[j] = p.twL[(t1 + R * j) * tw_mul];
+    float2 tw4r = p.twL[4 * R * tw_mul];
+    __syncthreads();
+    // ---- inverse, stage 1 lanes: along k1 -> z[t + R i]
+#pragma unroll
+    for (int k = 0; k < R; ++k) v[k] = lds[k * ROW + t1 * 8 + col1];
+    // the seeds have arrived before the copy is issued, so that nothing
+    // after it waits on the copy
+    asm volatile("" : "+v"(tws[0]), "+v"(tws[1]), "+v"(tws[2]), "+v"(tws[3]), "+v"(tw4r));
+    asm volatile("" : "+v"(ncols_v));
+    const int2 ncols = make_int2(__builtin_amdgcn_readfirstlane(ncols_v.x), __builtin_amdgcn_readfirstlane(ncols_v.y));
+    __syncthreads();  // the transpose buffer is free: fetch the next item's q
+    if (more) copy_block(p.in[0], nblk, ncols);
+    dft<R, +1>(v);
+    // U in row layout: element i of this lane is token row m3 = t1 + R i
+    const int cp1 = blk.y * 4 + j1;
+    const uint32_t lane_pair = (uint32_t)((kc1 * p.M + k2c1 * N + t1) * p.CP2 + cp1);
+    const int64_t row_pair = (int64_t)R * p.CP2;
+    char* dst = reinterpret_cast<char*>(p.out) + (int64_t)blk.z * p.L * p.CP2 * 8;
+    const uint32_t off = lane_pair * 8;
+    float2 step = make_float2(1.f, 0.f);
+#pragma unroll
+    for (int a = 0; a < R / 4; ++a) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * a + j;
+        if (active1)
+          *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) = cmul(v[i], cconj(cmul(tws[j], step)));
+      }
+      step = cmul(step, tw4r);
+    }
+    if (!more) break;
+    tile = next;
+    blk = nblk;
+    cols = ncols;
+    first = false;
   }
 }
 

@@ -158,6 +158,7 @@ struct LenTables {
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  int cus = 0;  // compute units, queried once
   std::map<int64_t, LenTables> tables;
 };
 
@@ -513,24 +514,56 @@ int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
   const bool gl = IN == IN_C32 && p.gtab != nullptr && p.D % 2 == 0 && (p.D / 2) % p.cpt == 0;
   const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
                      (gl ? (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float) : 0);
-  // input blocks copied to LDS asynchronously: tiled input, two slots of 4 pairs
-  const bool dma = gl && R == 32 && p.tiled && p.nslot == 2 && p.cpt == 4;
-  static bool attr_set[3] = {false, false, false};  // guarded by g_mu
-  const int kind = dma ? 2 : gl ? 1 : 0;
+  // tiled input, two slots of 4 pairs, R = 32: the persistent kernel that
+  // copies its input blocks to LDS asynchronously
+  if (IN == IN_C32 && gl && R == 32 && p.tiled && p.nslot == 2 && p.cpt == 4) {
+    static bool dma_attr = false;  // guarded by g_mu
+    if (!dma_attr) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_dma),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        return SPECTRE_EHIP;
+      dma_attr = true;
+    }
+    MidParams q = p;
+    q.gx = (int)grid.x;
+    q.gy = (int)grid.y;
+    q.gz = (int)grid.z;
+    const int64_t ntile = (int64_t)grid.x * grid.y * grid.z;
+    // When two workgroups per CU can hold every item in at most 4 rounds,
+    // each workgroup takes that many items in turn (the next item's first
+    // copy then runs under this item's end); the workgroups sharing output
+    // lines (items 8 apart: with a grid that is a multiple of 32, the same
+    // turn of workgroups on one XCD) stay close in time.  Larger grids keep
+    // one item per workgroup: over more turns the sharers drift apart, and
+    // the dispatcher's own order keeps them together.
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
+    int& cus = g_dev[dev].cus;  // guarded by g_mu
+    if (cus <= 0 && (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0))
+      return SPECTRE_EHIP;
+    const int64_t slots = 2 * (int64_t)cus;
+    int64_t wgs = ntile;
+    if (ntile <= 4 * slots) {
+      const int64_t items = (ntile + slots - 1) / slots;
+      wgs = ((ntile + items - 1) / items + 31) / 32 * 32;
+      if (wgs > ntile) wgs = ntile;
+    }
+    hipLaunchKernelGGL(k_mid_dma, dim3((unsigned)wgs), dim3(256), lds, st, q);
+    SPECTRE_LAUNCH_CHECK("B_mid_lds");
+    return SPECTRE_OK;
+  }
+  static bool attr_set[2] = {false, false};  // guarded by g_mu
   const void* fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, false>);
   if constexpr (IN == IN_C32) {
-    if (kind == 2) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true, true>);
-    if (kind == 1) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>);
+    if (gl) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>);
   }
-  if (!attr_set[kind]) {
+  if (!attr_set[gl]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SPECTRE_EHIP;
-    attr_set[kind] = true;
+    attr_set[gl] = true;
   }
   if constexpr (IN == IN_C32) {
-    if (kind == 2)
-      hipLaunchKernelGGL((k_mid_sq<R, IN, true, true>), grid, dim3(R * ncols), lds, st, p);
-    else if (kind == 1)
+    if (gl)
       hipLaunchKernelGGL((k_mid_sq<R, IN, true>), grid, dim3(R * ncols), lds, st, p);
     else
       hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
