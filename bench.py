@@ -254,6 +254,8 @@ def _short(name: str) -> str:
     arguments: k_strided<R, IN, TW, SIGN>, k_strided_split<R, IN, TW>,
     k_final<R, DT, FUSE>); other kernels keep their own name."""
     import re
+    if "spectre::k_mid_dma" in name:
+        return "B_mid_lds"
     m = re.search(r"spectre::(k_\w+)<([^>]*)>", name)
     if not m:
         return "copy (calibration)" if "copyBuffer" in name else name[:60]
@@ -354,8 +356,8 @@ def write_counters(fetch_dir, write_dir, workload_id):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true")
