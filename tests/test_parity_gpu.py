@@ -101,6 +101,9 @@ EDGE = [
     (1, 196608, 1, 128, 1, 50000),  # three-level, l2 = 6
     (1, 16384, 4, 256, 0, None),    # H*D = 1024: separate norm pass
     (1, 4096, 2, 5, 0, None),       # channel pairs straddle heads (odd D)
+    (2, 65536, 4, 64, 0, None),     # LDS-copy B kernel, 4 work items per workgroup across batches
+    (1, 65536, 4, 64, 1, 30000),    # LDS-copy B kernel, 2 work items per workgroup, bf16, truncated
+    (1, 8192, 32, 6, 0, None),      # tiled input, 4-pair blocks spanning heads: gate from the table
 ]
 
 
