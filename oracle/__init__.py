@@ -6,7 +6,10 @@ its binding never import it.
 
 Every function takes host numpy arrays: q, k, v, x as [B, L, H, D] float32
 (dtype 0) or uint16 bfloat16 bit patterns (dtype 1); gate as [H, L//2 + 1]
-float32; gamma, beta as [H*D] float32.  Results are float64.
+float32 (gate_kind 0: the multiplier, 1: its logit), or [H, L//2 + 1, 2]
+float32 (gate_kind 2: real and imaginary parts); gamma, beta as [H*D]
+float32.  norm_order 0 is out = LN(x + y), 1 is out = x + LN(y).  Results
+are float64.
 """
 from __future__ import annotations
 
@@ -51,8 +54,16 @@ def _bind(lib):
     lib.oracle_spectre_mix_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                               i64, i64, ci, vp, i64, vp, vp, ci]
     lib.oracle_threads.argtypes = [ci]
+    lib.oracle_spectre_y_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, ci, vp, ci]
+    lib.oracle_layernorm_residual_ex.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, vp]
+    lib.oracle_spectre_mix_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          ci, ci, ci, vp, vp, ci]
+    lib.oracle_spectre_mix_tokens_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                                 i64, i64, ci, ci, ci, vp, i64, vp, vp, ci]
     for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
-              lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads):
+              lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads,
+              lib.oracle_spectre_y_ex, lib.oracle_layernorm_residual_ex,
+              lib.oracle_spectre_mix_ex, lib.oracle_spectre_mix_tokens_ex):
         f.restype = ci
     return lib
 
@@ -120,21 +131,29 @@ def fft(x: np.ndarray, sign: int = -1) -> np.ndarray:
     return ore + 1j * oim
 
 
-def spectre_y(q, k, v, gate, keep_bins: int, dtype: int = 0, nthreads: int = 0) -> np.ndarray:
+def _gate(gate, H: int, L: int, gate_kind: int) -> np.ndarray:
+    gate = _c(gate, np.float32)
+    shape = (H, L // 2 + 1, 2) if gate_kind == 2 else (H, L // 2 + 1)
+    assert gate.shape == shape, (gate.shape, shape)
+    return gate
+
+
+def spectre_y(q, k, v, gate, keep_bins: int, dtype: int = 0, nthreads: int = 0,
+              gate_kind: int = 0) -> np.ndarray:
     """y = irfft(G Q conj(K) V / L) per column, [B, L, H, D] float64."""
     B, L, H, D = q.shape
     q, k, v = (_storage(t, dtype) for t in (q, k, v))
-    gate = _c(gate, np.float32)
-    assert gate.shape == (H, L // 2 + 1)
+    gate = _gate(gate, H, L, gate_kind)
     y = np.empty((B, L, H, D), np.float64)
-    _check(_load().oracle_spectre_y(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                    gate.ctypes.data, B, H, L, D, keep_bins, dtype,
-                                    y.ctypes.data, nthreads))
+    _check(_load().oracle_spectre_y_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                       gate.ctypes.data, B, H, L, D, keep_bins, dtype,
+                                       gate_kind, y.ctypes.data, nthreads))
     return y
 
 
-def layernorm_residual(y, x, gamma, beta, dtype: int = 0) -> np.ndarray:
-    """LayerNorm over the last two axes' H*D channels of (x + y), eps 1e-5."""
+def layernorm_residual(y, x, gamma, beta, dtype: int = 0, norm_order: int = 0) -> np.ndarray:
+    """LayerNorm over the last two axes' H*D channels of (x + y) (norm_order
+    0), or x + the LayerNorm of y (norm_order 1); eps 1e-5."""
     shape = y.shape
     C = shape[-1] * shape[-2]
     ntok = int(np.prod(shape[:-2]))
@@ -142,41 +161,47 @@ def layernorm_residual(y, x, gamma, beta, dtype: int = 0) -> np.ndarray:
     x = _storage(x, dtype)
     gamma, beta = _c(gamma, np.float32), _c(beta, np.float32)
     out = np.empty(shape, np.float64)
-    _check(_load().oracle_layernorm_residual(y.ctypes.data, x.ctypes.data, gamma.ctypes.data,
-                                             beta.ctypes.data, ntok, C, dtype, out.ctypes.data))
+    _check(_load().oracle_layernorm_residual_ex(y.ctypes.data, x.ctypes.data, gamma.ctypes.data,
+                                                beta.ctypes.data, ntok, C, dtype, norm_order,
+                                                out.ctypes.data))
     return out
 
 
 def spectre_mix(q, k, v, x, gate, gamma, beta, keep_bins: int, dtype: int = 0,
-                nthreads: int = 0, want_y: bool = False):
+                nthreads: int = 0, want_y: bool = False, gate_kind: int = 0,
+                norm_order: int = 0):
     """The whole mix; returns out [B, L, H, D] float64 (and y if want_y)."""
     B, L, H, D = q.shape
     q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
-    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
-    assert gate.shape == (H, L // 2 + 1) and gamma.size == H * D and beta.size == H * D
+    gate = _gate(gate, H, L, gate_kind)
+    gamma, beta = (_c(t, np.float32) for t in (gamma, beta))
+    assert gamma.size == H * D and beta.size == H * D
     out = np.empty((B, L, H, D), np.float64)
     y = np.empty((B, L, H, D), np.float64) if want_y else None
-    _check(_load().oracle_spectre_mix(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                      x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
-                                      beta.ctypes.data, B, H, L, D, keep_bins, dtype,
-                                      out.ctypes.data, y.ctypes.data if want_y else None,
-                                      nthreads))
+    _check(_load().oracle_spectre_mix_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
+                                         beta.ctypes.data, B, H, L, D, keep_bins, dtype,
+                                         gate_kind, norm_order, out.ctypes.data,
+                                         y.ctypes.data if want_y else None, nthreads))
     return (out, y) if want_y else out
 
 
 def spectre_mix_tokens(q, k, v, x, gate, gamma, beta, keep_bins: int, tokens,
-                       dtype: int = 0, nthreads: int = 0):
+                       dtype: int = 0, nthreads: int = 0, gate_kind: int = 0,
+                       norm_order: int = 0):
     """The mix at sampled flat token ids b*L + t; returns (out, y), each [ntok, H, D]."""
     B, L, H, D = q.shape
     q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
-    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
+    gate = _gate(gate, H, L, gate_kind)
+    gamma, beta = (_c(t, np.float32) for t in (gamma, beta))
     tokens = _c(tokens, np.int64)
     n = tokens.size
     out = np.empty((n, H, D), np.float64)
     y = np.empty((n, H, D), np.float64)
-    _check(_load().oracle_spectre_mix_tokens(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                             x.ctypes.data, gate.ctypes.data,
-                                             gamma.ctypes.data, beta.ctypes.data, B, H, L, D,
-                                             keep_bins, dtype, tokens.ctypes.data, n,
-                                             out.ctypes.data, y.ctypes.data, nthreads))
+    _check(_load().oracle_spectre_mix_tokens_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                x.ctypes.data, gate.ctypes.data,
+                                                gamma.ctypes.data, beta.ctypes.data, B, H, L,
+                                                D, keep_bins, dtype, gate_kind, norm_order,
+                                                tokens.ctypes.data, n, out.ctypes.data,
+                                                y.ctypes.data, nthreads))
     return out, y

@@ -39,6 +39,20 @@
  * Storage types: dtype 0 = IEEE binary32, dtype 1 = bfloat16 (the upper 16
  * bits of a binary32; decoded exactly by shifting left 16).  All arithmetic
  * is double.
+ *
+ * Variants (the *_ex entry points; the plain ones are gate kind 0, post-norm):
+ *  - gate kind 0: G[h][f] is the real multiplier itself;
+ *    gate kind 1: G[h][f] is a logit and the multiplier is the logistic
+ *    sigmoid 1 / (1 + exp(-G)) (section 3.1 recommends a sigmoid gate);
+ *    gate kind 2: the gate array is [H][L/2 + 1][2], the real and imaginary
+ *    parts of a complex multiplier (section 2.4 carries relative position as
+ *    a frequency-dependent rotation inside G(f)).  The bins above L/2 take
+ *    the conjugate through the Hermitian extension, and an inverse real FFT
+ *    ignores the imaginary part of bins 0 and L/2, so only the real part of
+ *    the gate acts there.
+ *  - norm order 0 (post-norm, section 2.2's pseudocode): out = LN(x + y);
+ *    norm order 1 (pre-norm, the order section 3.3 settles on): out =
+ *    x + LN(y), the same LayerNorm applied to y alone.
  */
 #include <math.h>
 #include <pthread.h>
@@ -66,6 +80,10 @@ static inline cpx cadd(cpx a, cpx b) {
 }
 static inline cpx csub(cpx a, cpx b) {
   cpx r = {a.re - b.re, a.im - b.im};
+  return r;
+}
+static inline cpx cscale(cpx a, double s) {
+  cpx r = {a.re * s, a.im * s};
   return r;
 }
 static inline cpx cconj(cpx a) {
@@ -264,6 +282,7 @@ typedef struct {
   const float *gate;
   int64_t B, H, L, D, keep;
   int dtype;
+  int gate_kind; /* 0 real, 1 logit (sigmoid), 2 complex (re, im pairs) */
   const fft_table *tab;
   /* output: either the full y [B, L, H*D] or sampled tokens */
   double *y;             /* full output, or NULL */
@@ -275,6 +294,20 @@ typedef struct {
   double max_imag_ratio;
   pthread_mutex_t mu;
 } mix_job;
+
+/* The gate multiplier of head h at half-spectrum bin f (see the variants in
+ * the header). */
+static cpx gate_at(const mix_job *J, int64_t h, int64_t f, int64_t nbins) {
+  cpx g = {0.0, 0.0};
+  if (J->gate_kind == 2) {
+    g.re = (double)J->gate[2 * (h * nbins + f)];
+    g.im = (double)J->gate[2 * (h * nbins + f) + 1];
+  } else {
+    double a = (double)J->gate[h * nbins + f];
+    g.re = J->gate_kind == 1 ? 1.0 / (1.0 + exp(-a)) : a;
+  }
+  return g;
+}
 
 /* y for one column (b, c): fills ycol[0..L). Returns the largest |Im| seen
  * after the inverse transform, relative to max |Re| (a self-check). */
@@ -309,10 +342,8 @@ static double mix_column(const mix_job *J, int64_t b, int64_t c, cpx *bufq, cpx 
   for (int64_t f = 0; f <= half; ++f) {
     cpx o = {0.0, 0.0};
     if (f < J->keep) {
-      double g = (double)J->gate[h * nbins + f] * invL;
-      o = cmul(cmul(bufq[f], cconj(bufk[f])), bufv[f]);
-      o.re *= g;
-      o.im *= g;
+      cpx g = gate_at(J, h, f, nbins);
+      o = cscale(cmul(cmul(cmul(bufq[f], cconj(bufk[f])), bufv[f]), g), invL);
     }
     if (f == 0 || (L % 2 == 0 && f == half)) o.im = 0.0;
     tmp[f] = o;
@@ -419,12 +450,18 @@ static int check_dims(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, 
   return ORACLE_OK;
 }
 
+static int check_variant(int gate_kind, int norm_order) {
+  if (gate_kind < 0 || gate_kind > 2 || norm_order < 0 || norm_order > 1) return ORACLE_EINVAL;
+  return ORACLE_OK;
+}
+
 /* y[b, t, h*D + d] for every token, double. */
-int oracle_spectre_y(const void *q, const void *k, const void *v, const float *gate,
-                     int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype,
-                     double *y, int nthreads) {
+int oracle_spectre_y_ex(const void *q, const void *k, const void *v, const float *gate,
+                        int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype,
+                        int gate_kind, double *y, int nthreads) {
   if (!q || !k || !v || !gate || !y) return ORACLE_EINVAL;
   int s = check_dims(B, H, L, D, keep, dtype);
+  if (!s) s = check_variant(gate_kind, 0);
   if (s) return s;
   mix_job J;
   memset(&J, 0, sizeof J);
@@ -438,8 +475,15 @@ int oracle_spectre_y(const void *q, const void *k, const void *v, const float *g
   J.D = D;
   J.keep = keep;
   J.dtype = dtype;
+  J.gate_kind = gate_kind;
   J.y = y;
   return run_mix(&J, nthreads);
+}
+
+int oracle_spectre_y(const void *q, const void *k, const void *v, const float *gate,
+                     int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype,
+                     double *y, int nthreads) {
+  return oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, 0, y, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -447,13 +491,15 @@ int oracle_spectre_y(const void *q, const void *k, const void *v, const float *g
 /* ------------------------------------------------------------------------ */
 
 /*
- * out[i, c] = (z - mean) / sqrt(var + 1e-5) * gamma[c] + beta[c], with
- * z = x[xrow_i, c] + y[i, c], mean and biased variance over c (two passes).
- * xrow[i] selects the row of x for row i of y (NULL: row i).
+ * Post-norm (pre = 0): out[i, c] = (z - mean) / sqrt(var + 1e-5) * gamma[c] +
+ * beta[c], with z = x[xrow_i, c] + y[i, c], mean and biased variance over c
+ * (two passes).  Pre-norm (pre = 1): z = y[i, c], and x[xrow_i, c] is added
+ * after the affine step.  xrow[i] selects the row of x for row i of y (NULL:
+ * row i).
  */
 static void layernorm_rows(const double *y, const void *x, int dtype, const int64_t *xrow,
                            const float *gamma, const float *beta, int64_t nrows, int64_t C,
-                           double *out) {
+                           int pre, double *out) {
   const double eps = 1e-5;
   for (int64_t i = 0; i < nrows; ++i) {
     int64_t xr = xrow ? xrow[i] : i;
@@ -461,7 +507,7 @@ static void layernorm_rows(const double *y, const void *x, int dtype, const int6
     double *o = out + i * C;
     double sum = 0.0;
     for (int64_t c = 0; c < C; ++c) {
-      o[c] = load_elem(x, dtype, xr * C + c) + yr[c];
+      o[c] = pre ? yr[c] : load_elem(x, dtype, xr * C + c) + yr[c];
       sum += o[c];
     }
     double mean = sum / (double)C;
@@ -469,35 +515,54 @@ static void layernorm_rows(const double *y, const void *x, int dtype, const int6
     for (int64_t c = 0; c < C; ++c) var += (o[c] - mean) * (o[c] - mean);
     var /= (double)C;
     double rstd = 1.0 / sqrt(var + eps);
-    for (int64_t c = 0; c < C; ++c)
+    for (int64_t c = 0; c < C; ++c) {
       o[c] = (o[c] - mean) * rstd * (double)gamma[c] + (double)beta[c];
+      if (pre) o[c] += load_elem(x, dtype, xr * C + c);
+    }
   }
+}
+
+int oracle_layernorm_residual_ex(const double *y, const void *x, const float *gamma,
+                                 const float *beta, int64_t ntok, int64_t C, int dtype,
+                                 int norm_order, double *out) {
+  if (!y || !x || !gamma || !beta || !out || ntok < 0 || C < 1) return ORACLE_EINVAL;
+  if (dtype != 0 && dtype != 1) return ORACLE_EINVAL;
+  if (check_variant(0, norm_order)) return ORACLE_EINVAL;
+  layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, norm_order, out);
+  return ORACLE_OK;
 }
 
 int oracle_layernorm_residual(const double *y, const void *x, const float *gamma,
                               const float *beta, int64_t ntok, int64_t C, int dtype,
                               double *out) {
-  if (!y || !x || !gamma || !beta || !out || ntok < 0 || C < 1) return ORACLE_EINVAL;
-  if (dtype != 0 && dtype != 1) return ORACLE_EINVAL;
-  layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, out);
-  return ORACLE_OK;
+  return oracle_layernorm_residual_ex(y, x, gamma, beta, ntok, C, dtype, 0, out);
 }
 
 /* The whole mix: out (and optionally y) for every token, double. */
-int oracle_spectre_mix(const void *q, const void *k, const void *v, const void *x,
-                       const float *gate, const float *gamma, const float *beta, int64_t B,
-                       int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, double *out,
-                       double *y_out, int nthreads) {
+int oracle_spectre_mix_ex(const void *q, const void *k, const void *v, const void *x,
+                          const float *gate, const float *gamma, const float *beta, int64_t B,
+                          int64_t H, int64_t L, int64_t D, int64_t keep, int dtype,
+                          int gate_kind, int norm_order, double *out, double *y_out,
+                          int nthreads) {
   if (!x || !gamma || !beta || !out) return ORACLE_EINVAL;
   int s = check_dims(B, H, L, D, keep, dtype);
+  if (!s) s = check_variant(gate_kind, norm_order);
   if (s) return s;
   const int64_t C = H * D, ntok = B * L;
   double *y = y_out ? y_out : (double *)malloc(sizeof(double) * (size_t)(ntok * C));
   if (!y) return ORACLE_ENOMEM;
-  s = oracle_spectre_y(q, k, v, gate, B, H, L, D, keep, dtype, y, nthreads);
-  if (s == ORACLE_OK) layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, out);
+  s = oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, gate_kind, y, nthreads);
+  if (s == ORACLE_OK) layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, norm_order, out);
   if (!y_out) free(y);
   return s;
+}
+
+int oracle_spectre_mix(const void *q, const void *k, const void *v, const void *x,
+                       const float *gate, const float *gamma, const float *beta, int64_t B,
+                       int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, double *out,
+                       double *y_out, int nthreads) {
+  return oracle_spectre_mix_ex(q, k, v, x, gate, gamma, beta, B, H, L, D, keep, dtype, 0, 0,
+                               out, y_out, nthreads);
 }
 
 /*
@@ -506,14 +571,16 @@ int oracle_spectre_mix(const void *q, const void *k, const void *v, const void *
  * stays O(ntok * H * D) at any L.  out_tok and y_tok (optional) are
  * [ntok, H*D].
  */
-int oracle_spectre_mix_tokens(const void *q, const void *k, const void *v, const void *x,
-                              const float *gate, const float *gamma, const float *beta,
-                              int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
-                              int dtype, const int64_t *tokens, int64_t ntok,
-                              double *out_tok, double *y_tok, int nthreads) {
+int oracle_spectre_mix_tokens_ex(const void *q, const void *k, const void *v, const void *x,
+                                 const float *gate, const float *gamma, const float *beta,
+                                 int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
+                                 int dtype, int gate_kind, int norm_order,
+                                 const int64_t *tokens, int64_t ntok, double *out_tok,
+                                 double *y_tok, int nthreads) {
   if (!q || !k || !v || !x || !gate || !gamma || !beta || !tokens || !out_tok || ntok < 1)
     return ORACLE_EINVAL;
   int s = check_dims(B, H, L, D, keep, dtype);
+  if (!s) s = check_variant(gate_kind, norm_order);
   if (s) return s;
   for (int64_t i = 0; i < ntok; ++i)
     if (tokens[i] < 0 || tokens[i] >= B * L) return ORACLE_EINVAL;
@@ -532,13 +599,24 @@ int oracle_spectre_mix_tokens(const void *q, const void *k, const void *v, const
   J.D = D;
   J.keep = keep;
   J.dtype = dtype;
+  J.gate_kind = gate_kind;
   J.tokens = tokens;
   J.ntok = ntok;
   J.y_tok = y;
   s = run_mix(&J, nthreads);
-  if (s == ORACLE_OK) layernorm_rows(y, x, dtype, tokens, gamma, beta, ntok, C, out_tok);
+  if (s == ORACLE_OK)
+    layernorm_rows(y, x, dtype, tokens, gamma, beta, ntok, C, norm_order, out_tok);
   if (!y_tok) free(y);
   return s;
+}
+
+int oracle_spectre_mix_tokens(const void *q, const void *k, const void *v, const void *x,
+                              const float *gate, const float *gamma, const float *beta,
+                              int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
+                              int dtype, const int64_t *tokens, int64_t ntok,
+                              double *out_tok, double *y_tok, int nthreads) {
+  return oracle_spectre_mix_tokens_ex(q, k, v, x, gate, gamma, beta, B, H, L, D, keep, dtype,
+                                      0, 0, tokens, ntok, out_tok, y_tok, nthreads);
 }
 
 /* Number of threads a call with `nthreads` would use (0 = all online CPUs). */

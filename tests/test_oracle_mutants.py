@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from test_oracle_pins import closed_form_y, naive_dft
+from test_oracle_pins import (closed_form_y, closed_form_y_g, complex_gate,
+                              irfft_gate_complex, naive_dft)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "spectre_oracle.c")
 
@@ -18,8 +19,17 @@ MUTANTS = {
                      "cmul(cmul(bufq[f], bufk[f]), bufv[f])"),
     "conj_on_q": ("cmul(cmul(bufq[f], cconj(bufk[f])), bufv[f])",
                   "cmul(cmul(cconj(bufq[f]), bufk[f]), bufv[f])"),
-    "gate_scale_dropped": ("double g = (double)J->gate[h * nbins + f] * invL;",
-                           "double g = (double)J->gate[h * nbins + f];"),
+    "gate_scale_dropped": ("bufv[f]), g), invL);", "bufv[f]), g), 1.0);"),
+    "complex_gate_conj": ("g.im = (double)J->gate[2 * (h * nbins + f) + 1];",
+                          "g.im = -(double)J->gate[2 * (h * nbins + f) + 1];"),
+    "complex_gate_im_index": ("g.im = (double)J->gate[2 * (h * nbins + f) + 1];",
+                              "g.im = (double)J->gate[2 * (h * nbins + f)];"),
+    "logit_sign": ("1.0 / (1.0 + exp(-a))", "1.0 / (1.0 + exp(a))"),
+    "logit_ignored": ("g.re = J->gate_kind == 1 ? 1.0 / (1.0 + exp(-a)) : a;", "g.re = a;"),
+    "pre_norm_stats_with_x": ("o[c] = pre ? yr[c] : load_elem(x, dtype, xr * C + c) + yr[c];",
+                              "o[c] = load_elem(x, dtype, xr * C + c) + yr[c];"),
+    "pre_norm_residual_dropped": ("if (pre) o[c] += load_elem(x, dtype, xr * C + c);",
+                                  "if (pre) o[c] += 0.0;"),
     "inverse_scale_dropped": ("double re = bufq[t].re * invL, im = bufq[t].im * invL;",
                               "double re = bufq[t].re, im = bufq[t].im * invL;"),
     "truncation_inclusive": ("if (f < J->keep) {", "if (f <= J->keep) {"),
@@ -37,7 +47,8 @@ MUTANTS = {
                          "double rstd = 1.0 / (sqrt(var) + eps);"),
     "gamma_beta_swapped": ("o[c] = (o[c] - mean) * rstd * (double)gamma[c] + (double)beta[c];",
                            "o[c] = (o[c] - mean) * rstd * (double)beta[c] + (double)gamma[c];"),
-    "residual_dropped": ("o[c] = load_elem(x, dtype, xr * C + c) + yr[c];", "o[c] = yr[c];"),
+    "residual_dropped": ("pre ? yr[c] : load_elem(x, dtype, xr * C + c) + yr[c];",
+                         "pre ? yr[c] : yr[c];"),
     "nyquist_dropped": ("if (f == 0 || (L % 2 == 0 && f == half)) o.im = 0.0;",
                         "if (f == 0 || (L % 2 == 0 && f == half)) { o.im = 0.0; "
                         "if (f == half) o.re = 0.0; }"),
@@ -94,6 +105,30 @@ def _pins_pass() -> bool:
         ref_y = closed_form_y(*(dec.astype(np.float64),) * 3, g, L // 2 + 1)
         ref = oracle.layernorm_residual(ref_y, dec, ones, zeros)
         if np.abs(a - ref).max() > 1e-9:
+            return False
+        # gate variants: a complex gate against its closed form, logits at
+        # known sigmoid values, and the pre-norm order with y = 0
+        for L, keep in ((12, 7), (17, 9)):
+            B, H, D = 1, 2, 2
+            q, k, v = (rng.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+            g32, gc = complex_gate(H, L, rng)
+            ref = closed_form_y_g(*(a.astype(np.float64) for a in (q, k, v)),
+                                  [irfft_gate_complex(gc[h], keep, L) for h in range(H)])
+            if np.abs(oracle.spectre_y(q, k, v, g32, keep, gate_kind=2) - ref).max() > 1e-10:
+                return False
+        L, H = 16, 2
+        q, k, v = (rng.standard_normal((1, L, H, 2)).astype(np.float32) for _ in range(3))
+        nb = L // 2 + 1
+        y1 = oracle.spectre_y(q, k, v, np.ones((H, nb), np.float32), nb)
+        for logit, factor in ((0.0, 0.5), (30.0, 1.0), (-30.0, 0.0)):
+            y = oracle.spectre_y(q, k, v, np.full((H, nb), logit, np.float32), nb, gate_kind=1)
+            if np.abs(y - factor * y1).max() > 1e-9 * np.abs(y1).max():
+                return False
+        x = rng.standard_normal((1, L, H, 2)).astype(np.float32)
+        beta = rng.standard_normal(H * 2).astype(np.float32)
+        out = oracle.spectre_mix(q, k, v, x, np.ones((H, nb), np.float32),
+                                 np.ones(H * 2, np.float32), beta, 0, norm_order=1)
+        if np.abs(out - (x.astype(np.float64) + beta.reshape(H, 2))).max() > 0.0:
             return False
     except oracle.OracleError:
         return False

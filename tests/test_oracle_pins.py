@@ -354,3 +354,138 @@ def test_rejects_bad_arguments():
         oracle.spectre_y(q, q, q, gate, 6)   # keep_bins > L/2 + 1
     with pytest.raises(oracle.OracleError):
         oracle.spectre_y(q, q, q, gate, -1)
+
+
+# ------------------------------------------------------------- gate variants
+#
+# Gate kind 2 (complex multiplier: SPECTRE article, section 2.4's rotation
+# inside G(f)) and kind 1 (logit through a sigmoid: section 3.1), and the
+# pre-norm order of section 3.3.
+
+def irfft_gate_complex(G, keep, L):
+    """g[t] = inverse real transform of the complex gate G[f] * [f < keep],
+    f = 0..L//2, as a cosine/sine series: the Hermitian extension gives the
+    bins above L/2 the conjugate, and only the real part of bins 0 and L/2
+    enters, as an inverse real transform reads them."""
+    t = np.arange(L)
+    g = np.zeros(L)
+    for f in range(L // 2 + 1):
+        if f >= keep:
+            continue
+        a, b = G[f].real, G[f].imag
+        if f == 0:
+            g += a
+        elif L % 2 == 0 and f == L // 2:
+            g += a * np.cos(np.pi * t)
+        else:
+            ang = 2 * np.pi * ((f * t) % L) / L
+            g += 2 * (a * np.cos(ang) - b * np.sin(ang))
+    return g / L
+
+
+def closed_form_y_g(q, k, v, gseq):
+    """y[b, :, h, d] = (1/L) g_h (*) (q * k) (*) v with g_h = gseq[h]."""
+    B, L, H, D = q.shape
+    y = np.zeros((B, L, H, D))
+    for h in range(H):
+        for b in range(B):
+            for d in range(D):
+                r = circ_xcorr(q[b, :, h, d], k[b, :, h, d])
+                y[b, :, h, d] = circ_conv(gseq[h], circ_conv(r, v[b, :, h, d])) / L
+    return y
+
+
+def complex_gate(H, L, rng):
+    g = rng.uniform(-1, 1, (H, L // 2 + 1, 2)).astype(np.float32)
+    return g, g[..., 0].astype(np.float64) + 1j * g[..., 1].astype(np.float64)
+
+
+@pytest.mark.parametrize("L,keep", [(1, 1), (2, 2), (4, 3), (5, 3), (6, 4), (8, 5), (12, 7),
+                                    (16, 9), (17, 9), (48, 25), (64, 33)])
+def test_complex_gate_equals_closed_form(L, keep):
+    B, H, D = 1, 2, 2
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    g32, gc = complex_gate(H, L, RNG)
+    y = oracle.spectre_y(q, k, v, g32, keep, gate_kind=2)
+    ref = closed_form_y_g(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                          [irfft_gate_complex(gc[h], keep, L) for h in range(H)])
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("L,shift", [(96, 7), (96, -13), (4096, 5), (4096, 2047)])
+def test_complex_gate_linear_phase_is_a_shift(L, shift):
+    """A gate exp(-2 pi i f d / L) times a real gate delays the output by d
+    tokens (the shift theorem)."""
+    B, H, D = 2, 2, 3
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    real = RNG.uniform(0, 1, (H, L // 2 + 1))
+    f = np.arange(L // 2 + 1)
+    rot = np.exp(-2j * np.pi * ((f * shift) % L) / L)
+    g = real * rot
+    g32 = np.stack([g.real, g.imag], -1).astype(np.float32)
+    # the reference uses the float32-rounded magnitudes, so both see one gate
+    real32 = np.abs(g32[..., 0].astype(np.float64) + 1j * g32[..., 1].astype(np.float64))
+    y = oracle.spectre_y(q, k, v, g32, L // 2 + 1, gate_kind=2)
+    yr = oracle.spectre_y(q, k, v, real32.astype(np.float32), L // 2 + 1)
+    assert np.abs(y - np.roll(yr, shift, axis=1)).max() <= 2e-6 * np.abs(yr).max()
+
+
+def test_complex_gate_with_zero_imaginary_part_is_the_real_gate():
+    L, H = 4096, 2
+    q, k, v = (RNG.standard_normal((1, L, H, 4)).astype(np.float32) for _ in range(3))
+    g = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gc = np.stack([g, np.zeros_like(g)], -1)
+    a = oracle.spectre_y(q, k, v, gc, 1500, gate_kind=2)
+    b = oracle.spectre_y(q, k, v, g, 1500)
+    assert np.abs(a - b).max() <= 1e-13 * np.abs(b).max()
+
+
+def test_logit_gate_known_values():
+    """sigmoid(0) = 1/2, sigmoid(30) = 1 - 9.4e-14, sigmoid(+-ln 3) = 3/4, 1/4;
+    y is linear in the gate."""
+    L, H = 256, 2
+    q, k, v = (RNG.standard_normal((2, L, H, 4)).astype(np.float32) for _ in range(3))
+    nb = L // 2 + 1
+    y1 = oracle.spectre_y(q, k, v, np.ones((H, nb), np.float32), nb)
+    scale = np.abs(y1).max()
+    for logit, factor, tol in ((0.0, 0.5, 1e-13), (30.0, 1.0, 1e-12), (np.log(3.0), 0.75, 1e-6),
+                               (-np.log(3.0), 0.25, 1e-6)):
+        y = oracle.spectre_y(q, k, v, np.full((H, nb), logit, np.float32), nb, gate_kind=1)
+        assert np.abs(y - factor * y1).max() <= tol * scale, logit
+
+
+def test_pre_norm_known_cases():
+    """With y = 0 (keep 0) the pre-norm output is x + beta exactly (the
+    LayerNorm of a zero row is beta); with x = 0 both orders agree; and in
+    general out - x is the LayerNorm of y alone."""
+    B, L, H, D = 2, 48, 2, 4
+    rng = np.random.default_rng(5)
+    q, k, v, x = (rng.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    gate = rng.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, H * D).astype(np.float32)
+    beta = rng.standard_normal(H * D).astype(np.float32)
+    out0 = oracle.spectre_mix(q, k, v, x, gate, gamma, beta, 0, norm_order=1)
+    assert np.abs(out0 - (x.astype(np.float64) + beta.reshape(H, D))).max() == 0.0
+    z = np.zeros_like(x)
+    a = oracle.spectre_mix(q, k, v, z, gate, gamma, beta, 20, norm_order=1)
+    b = oracle.spectre_mix(q, k, v, z, gate, gamma, beta, 20, norm_order=0)
+    assert np.abs(a - b).max() == 0.0
+    c, y = oracle.spectre_mix(q, k, v, x, gate, gamma, beta, 20, norm_order=1, want_y=True)
+    # LayerNorm of y by its definition, per token
+    yt = y.reshape(B * L, H * D)
+    mu = yt.mean(1, keepdims=True)
+    var = ((yt - mu) ** 2).mean(1, keepdims=True)
+    ln = (yt - mu) / np.sqrt(var + 1e-5) * gamma + beta
+    assert np.abs(c.reshape(B * L, H * D) - x.reshape(B * L, H * D) - ln).max() <= 1e-12
+
+
+def test_variant_arguments_rejected():
+    q = np.zeros((1, 8, 1, 2), np.float32)
+    g = np.ones((1, 5), np.float32)
+    with pytest.raises(AssertionError):
+        oracle.spectre_y(q, q, q, g, 5, gate_kind=2)  # a complex gate needs [H, bins, 2]
+    with pytest.raises(oracle.OracleError):
+        oracle.spectre_y(q, q, q, g, 5, gate_kind=3)
+    with pytest.raises(oracle.OracleError):
+        oracle.spectre_mix(q, q, q, q, g, np.ones(2, np.float32), np.zeros(2, np.float32), 5,
+                           norm_order=2)
