@@ -22,10 +22,16 @@ SPECTRE_EINVAL = -1
 SPECTRE_EUNSUPPORTED = -2
 SPECTRE_ENOMEM = -3
 SPECTRE_EHIP = -4
+SPECTRE_GATE_REAL = 0
+SPECTRE_GATE_LOGIT = 1
+SPECTRE_GATE_COMPLEX = 2
+SPECTRE_NORM_POST = 0
+SPECTRE_NORM_PRE = 1
 
 EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "spectre_mix_plan",
            "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
-           "spectre_mix_strerror")
+           "spectre_mix_strerror", "spectre_mix_fwd_ex", "spectre_mix_y_ex",
+           "spectre_mix_workspace_bytes_ex")
 
 
 class SpectreError(RuntimeError):
@@ -68,6 +74,13 @@ def _load():
     lib.spectre_mix_y.restype = ci
     lib.spectre_mix_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
     lib.spectre_mix_workspace_bytes.restype = ctypes.c_size_t
+    lib.spectre_mix_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ci, ci, ci, vp]
+    lib.spectre_mix_fwd_ex.restype = ci
+    lib.spectre_mix_y_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, ci, vp]
+    lib.spectre_mix_y_ex.restype = ci
+    lib.spectre_mix_workspace_bytes_ex.argtypes = [i64, i64, i64, i64, ci, ci]
+    lib.spectre_mix_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.spectre_mix_plan.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
     lib.spectre_mix_plan.restype = ci
@@ -124,8 +137,25 @@ def spectre_mix_y(q, k, v, gate, y, B, H, L, D, keep_bins, dtype, stream=None) -
                               keep_bins, dtype, _stream(stream))
 
 
+def spectre_mix_fwd_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, dtype,
+                       gate_kind, norm_order, stream=None) -> int:
+    return _lib.spectre_mix_fwd_ex(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
+                                   _addr(gamma), _addr(beta), _addr(out), B, H, L, D, keep_bins,
+                                   dtype, gate_kind, norm_order, _stream(stream))
+
+
+def spectre_mix_y_ex(q, k, v, gate, y, B, H, L, D, keep_bins, dtype, gate_kind,
+                     stream=None) -> int:
+    return _lib.spectre_mix_y_ex(_addr(q), _addr(k), _addr(v), _addr(gate), _addr(y), B, H, L, D,
+                                 keep_bins, dtype, gate_kind, _stream(stream))
+
+
 def spectre_mix_workspace_bytes(B, H, L, D, dtype) -> int:
     return _lib.spectre_mix_workspace_bytes(B, H, L, D, dtype)
+
+
+def spectre_mix_workspace_bytes_ex(B, H, L, D, dtype, gate_kind) -> int:
+    return _lib.spectre_mix_workspace_bytes_ex(B, H, L, D, dtype, gate_kind)
 
 
 def spectre_mix_plan(L):

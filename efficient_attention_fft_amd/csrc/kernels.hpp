@@ -3,7 +3,9 @@
 // The operation (SPECTRE FFT-attention article, section 2.2 and its
 // pseudocode; section 2.3 for truncation): per column (b, h, d) of length L,
 // y = irfft( G[h][f] / L * Q[f] conj(K[f]) V[f] * [f < keep] ), then
-// out = LayerNorm_{H*D}(x + y).
+// out = LayerNorm_{H*D}(x + y).  Variants: a logit gate (G = sigmoid of the
+// given values, section 3.1), a complex gate (section 2.4's rotation inside
+// G(f)), and the pre-norm order out = x + LayerNorm(y) (section 3.3).
 //
 // Data path.  Two real channels (2j, 2j+1) of one token share a complex
 // number z = x[2j] + i x[2j+1] (the article's section 3.1 treats re/im as two
@@ -113,20 +115,48 @@ __device__ __forceinline__ float2 twiddle_lookup(const float2* __restrict__ tw, 
 
 // ------------------------------------------------------------- gate table
 //
-// gtab[(h * ncol + c) * N + k3] = scale * G[h][min(f, L - f)] if that bin is
-// kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 * k3):
-// the gate of every bin in the order the square B kernel's lanes visit them,
-// so that 32 lanes of one column read 32 consecutive values.  Built by an
-// extra grid plane of the first strided pass (multi-level plans only: a
-// single-level square kernel reads the gate itself).
+// Gate kinds (SPECTRE article: section 2.2's learnable G(f); section 3.1's
+// sigmoid gate; section 2.4's relative position as a frequency-dependent
+// rotation inside G(f)):
+//   GATE_REAL    gate [H][nbins]: the multiplier itself;
+//   GATE_LOGIT   gate [H][nbins]: logits, multiplier 1 / (1 + exp(-G));
+//   GATE_COMPLEX gate [H][nbins][2]: real and imaginary parts.
+// The multiplier of full-spectrum bin f (0 <= f < L) is the gate of bin
+// fc = min(f, L - f), conjugated for f > L/2 (the Hermitian extension of the
+// product); at f = 0 and f = L/2 only its real part acts, as the inverse
+// real transform reads only the real part of those bins.
+
+enum GateKind { GATE_REAL = 0, GATE_LOGIT = 1, GATE_COMPLEX = 2 };
+
+// scale * multiplier of full-spectrum bin f of head h (fc = min(f, L - f) < keep).
+__device__ __forceinline__ float2 gate_value(const float* gate, int kind, int64_t nbins, int64_t h,
+                                             int64_t fc, int64_t f, int64_t L, float scale) {
+  if (kind == GATE_COMPLEX) {
+    const float2 g = reinterpret_cast<const float2*>(gate)[h * nbins + fc];
+    const bool real_bin = f == 0 || 2 * f == L;
+    return make_float2(g.x * scale, real_bin ? 0.f : (2 * f > L ? -g.y : g.y) * scale);
+  }
+  float a = gate[h * nbins + fc];
+  if (kind == GATE_LOGIT) a = 1.0f / (1.0f + expf(-a));
+  return make_float2(a * scale, 0.f);
+}
+
+// gtab[(h * ncol + c) * N + k3] = scale * the multiplier of bin f if that bin
+// is kept, else 0, for column c = kc + L1 * k2c and f = kc + L1 * (k2c + L2 *
+// k3): the gate of every bin in the order the square B kernel's lanes visit
+// them, so that 32 lanes of one column read 32 consecutive values (binary32
+// values, or binary32 pairs for a complex gate).  Built by an extra grid
+// plane of the first strided pass (multi-level plans only: a single-level
+// square kernel reads the gate itself).
 
 struct GateTabParams {
-  const float* gate;  // [H][nbins]
-  float* gtab;        // [H][ncol][N]; null: no table to build
+  const float* gate;  // [H][nbins], or [H][nbins][2] for a complex gate
+  float* gtab;        // [H][ncol][N] (pairs for a complex gate); null: no table to build
   int64_t L;
   int L1, L2, N, ncol, nbins;
   int64_t keep, total;  // total = H * L
   float scale;
+  int kind;  // GateKind
 };
 
 // Entries idx0, idx0 + stride, ... of the table.
@@ -138,7 +168,12 @@ __device__ __forceinline__ void gate_table_fill(const GateTabParams& p, int64_t 
     const int h = (int)(r / p.ncol);
     const int64_t f = c % p.L1 + (int64_t)p.L1 * (c / p.L1 + (int64_t)p.L2 * k3);
     const int64_t fc = f < p.L - f ? f : p.L - f;
-    p.gtab[idx] = fc < p.keep ? p.gate[(int64_t)h * p.nbins + fc] * p.scale : 0.f;
+    const float2 g = fc < p.keep ? gate_value(p.gate, p.kind, p.nbins, h, fc, f, p.L, p.scale)
+                                 : make_float2(0.f, 0.f);
+    if (p.kind == GATE_COMPLEX)
+      reinterpret_cast<float2*>(p.gtab)[idx] = g;
+    else
+      p.gtab[idx] = g.x;
   }
 }
 
@@ -409,6 +444,7 @@ struct MidParams {
   const float* gate;     // [H][nbins]
   const float* gtab;     // k_mid_sq: [H][ncol][N] gate table (scale, truncation, mirror folded
                          // in), or null for a single-level plan, which reads gate directly
+  int gate_kind;         // GateKind of gate (gtab: binary32 pairs for a complex gate)
   int ncol;              // columns per batch element, L1 * L2
   int tiled;             // k_mid_sq: in[] laid out [b][column][CP2 / 4][N][4] (see k_strided_split)
   const float2* twN;     // twN[e] = exp(-2 pi i e / N), e < N
@@ -630,13 +666,13 @@ __global__ __launch_bounds__(512) void k_mid(MidParams p) {
         const int se_col = pr.se == 0 ? cols.x : cols.y;
         const int f = se_col % p.L1 + p.L1 * (se_col / p.L1 + p.L2 * pr.ie);
         const int fc = min(f, p.L - f);
-        float ga = 0.f, gb = 0.f;
+        float2 ga = make_float2(0.f, 0.f), gb = ga;
         if (fc < p.keep) {
-          ga = p.gate[(2 * cp) / p.D * p.nbins + fc] * p.scale;
-          gb = p.gate[(2 * cp + 1) / p.D * p.nbins + fc] * p.scale;
+          ga = gate_value(p.gate, p.gate_kind, p.nbins, (2 * cp) / p.D, fc, f, p.L, p.scale);
+          gb = gate_value(p.gate, p.gate_kind, p.nbins, (2 * cp + 1) / p.D, fc, f, p.L, p.scale);
         }
-        const float2 oa = cscale(cmul(sa[i], A), ga);
-        const float2 ob = cscale(cmul(sb[i], Bv), gb);
+        const float2 oa = cmul(cmul(sa[i], A), ga);
+        const float2 ob = cmul(cmul(sb[i], Bv), gb);
         // W[f] = Oa + i Ob, W[L-f] = conj(Oa) + i conj(Ob)
         lds[oe] = make_float2(oa.x - ob.y, oa.y + ob.x);
         lds[om] = make_float2(oa.x + ob.y, ob.x - oa.y);
@@ -700,7 +736,7 @@ __device__ __forceinline__ float2 lane_pull2(float2 v, int src_byte) {
   return make_float2(lane_pull(v.x, src_byte), lane_pull(v.y, src_byte));
 }
 
-template <int R, int IN, bool GL = false>
+template <int R, int IN, bool GL = false, bool CG = false>
 __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
   constexpr int N = R * R;
   constexpr int H2 = R / 2;
@@ -841,23 +877,34 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 #pragma unroll
       for (int u = 0; u <= H2; ++u) {
         const float2 z = v[u], zm = mirror(u);
-        float ga, gb;
+        float2 oa, ob;
+        const float2 pa = cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+        const float2 pb = cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
         if constexpr (GL) {
-          ga = gl[(s2 * (H2 + 1) + u) * R + k1];
-          gb = ga;
+          const float ga = gl[(s2 * (H2 + 1) + u) * R + k1];
+          oa = cscale(pa, ga);
+          ob = cscale(pb, ga);
+        } else if constexpr (IN == IN_C32 && CG) {  // multi-level, complex gate table
+          const float2 ga = reinterpret_cast<const float2*>(p.gtab)[(gta - p.gtab) + R * u];
+          const float2 gb = ha == hb ? ga : reinterpret_cast<const float2*>(p.gtab)[(gtb - p.gtab) + R * u];
+          oa = cmul(pa, ga);
+          ob = cmul(pb, gb);
         } else if constexpr (IN == IN_C32) {  // multi-level: the gate table
-          ga = gta[R * u];
-          gb = ha == hb ? ga : gtb[R * u];
+          const float ga = gta[R * u];
+          const float gb = ha == hb ? ga : gtb[R * u];
+          oa = cscale(pa, ga);
+          ob = cscale(pb, gb);
         } else {  // raw inputs, one column (single level): bin k1 + R u, from the gate itself
           const int f = k1 + R * u;
           const int fc = min(f, p.L - f);
           const bool kept = fc < p.keep;
-          const int gi = kept ? fc : 0;
-          ga = kept ? p.gate[ha * p.nbins + gi] * p.scale : 0.f;
-          gb = kept ? p.gate[hb * p.nbins + gi] * p.scale : 0.f;
+          const float2 ga = kept ? gate_value(p.gate, p.gate_kind, p.nbins, ha, fc, f, p.L, p.scale)
+                                 : make_float2(0.f, 0.f);
+          const float2 gb = kept ? gate_value(p.gate, p.gate_kind, p.nbins, hb, fc, f, p.L, p.scale)
+                                 : make_float2(0.f, 0.f);
+          oa = cmul(pa, ga);
+          ob = cmul(pb, gb);
         }
-        const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), ga);
-        const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), gb);
         sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
         sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
       }
@@ -933,6 +980,7 @@ __device__ __forceinline__ void wait_vmcnt_32() {
   __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | 0x0F70);  // vmcnt(32)
 }
 
+template <bool CG>  // CG: complex gate, read from the table in the product (no LDS copy)
 __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
   constexpr int R = 32, N = R * R, H2 = R / 2, NT = 256, ROW = R * 8 + 1;
   constexpr int kSlot = 4 * N + 16;          // float2 between the slots' blocks
@@ -992,13 +1040,15 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     float2 tv[N / NT];
 #pragma unroll
     for (int r = 0; r < N / NT; ++r) tv[r] = p.twN[tid + NT * r];
-    gate_load(blk, cols, gv);
+    if constexpr (!CG) gate_load(blk, cols, gv);
     copy_block(p.in[0], blk, cols);
 #pragma unroll
     for (int r = 0; r < N / NT; ++r) twl[tid + NT * r] = tv[r];
+    if constexpr (!CG) {
 #pragma unroll
-    for (int r = 0; r < NGR; ++r)
-      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+      for (int r = 0; r < NGR; ++r)
+        if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+    }
   }
   bool first = true;
   float2 v[R];
@@ -1051,7 +1101,9 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
       // the next item's columns (a vector load: the top of the next tensor
       // waits for it), then its gate values, both used at the end of the item
       if (x == 0) ncols_v = p.wgcols[nblk.x];
-      if (x == 1) gate_load(nblk, ncols_v, gv);
+      if constexpr (!CG) {
+        if (x == 1) gate_load(nblk, ncols_v, gv);
+      }
       __syncthreads();  // the blocks are read before the transpose overwrites them
       // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
       dft<R, -1>(v);
@@ -1094,9 +1146,20 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
 #pragma unroll
         for (int u = 0; u <= H2; ++u) {
           const float2 z = v[u], zm = mirror(u);
-          const float g = gl[(s2 * (H2 + 1) + u) * R + k1];
-          const float2 oa = cscale(cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y)), g);
-          const float2 ob = cscale(cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x)), g);
+          const float2 pa = cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+          const float2 pb = cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
+          float2 oa, ob;
+          if constexpr (CG) {
+            const int c2 = s2 == 0 ? cols.x : cols.y;
+            const float2 g = reinterpret_cast<const float2*>(p.gtab)
+                [((int64_t)((2 * blk.y * 4) / p.D) * p.ncol + (c2 >= 0 ? c2 : 0)) * N + k1 + R * u];
+            oa = cmul(pa, g);
+            ob = cmul(pb, g);
+          } else {
+            const float g = gl[(s2 * (H2 + 1) + u) * R + k1];
+            oa = cscale(pa, g);
+            ob = cscale(pb, g);
+          }
           sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
           sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
         }
@@ -1120,9 +1183,11 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
 #pragma unroll
     for (int n = 0; n < R; ++n) lds[k1 * ROW + n * 8 + col2] = v[n];
     // the next item's gate values (every wave has read this item's)
+    if constexpr (!CG) {
 #pragma unroll
-    for (int r = 0; r < NGR; ++r)
-      if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+      for (int r = 0; r < NGR; ++r)
+        if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
+    }
     // output twiddle w^-(m3 tw_mul), w = w_L, for m3 = t1 + R i, i = 4 a + j:
     // the seeds w^(t1 + R j), j < 4, times (w^(4 R))^a; loaded before the
     // next item's copy so that waiting for them does not wait for it
@@ -1216,7 +1281,8 @@ constexpr int ilog2(int r) { return r <= 1 ? 0 : 1 + ilog2(r / 2); }
 // R-point DFT gives tokens t = n1 M + m.  With FUSE the workgroup is exactly
 // the CP2 pairs of one (b, m), so every token's H*D channels are in the
 // workgroup: residual add, two-pass mean / variance over the channels, affine,
-// store.  Without FUSE it stores y (binary32) for a separate LayerNorm pass.
+// store (PRE: the statistics of y alone, and x added after the affine step).
+// Without FUSE it stores y (binary32) for a separate LayerNorm pass.
 
 struct FinalParams {
   const float2* U;
@@ -1230,7 +1296,7 @@ struct FinalParams {
   float eps;
 };
 
-template <int R, int DT, bool FUSE>
+template <int R, int DT, bool FUSE, bool PRE = false>
 __global__ __launch_bounds__(256) void k_final(FinalParams p) {
   constexpr int Rp = next_pow2(R);
   // fused: one workgroup per (b, m) with exactly CP2 threads; else a flat grid
@@ -1263,8 +1329,10 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
+    if constexpr (!PRE) {  // post-norm: the statistics are those of x + y
 #pragma unroll
-    for (int r = 0; r < R; ++r) z[r] = cadd(z[r], load_pair<DT>(p.x, obase + r * ostep));
+      for (int r = 0; r < R; ++r) z[r] = cadd(z[r], load_pair<DT>(p.x, obase + r * ostep));
+    }
 
     float t[Rp];
     float mean[R], rstd[R];
@@ -1312,8 +1380,9 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
     const float b0 = p.beta[2 * cp], b1 = p.beta[2 * cp + 1];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float2 o = make_float2((z[r].x - mean[r]) * rstd[r] * g0 + b0,
-                                   (z[r].y - mean[r]) * rstd[r] * g1 + b1);
+      float2 o = make_float2((z[r].x - mean[r]) * rstd[r] * g0 + b0,
+                             (z[r].y - mean[r]) * rstd[r] * g1 + b1);
+      if constexpr (PRE) o = cadd(o, load_pair<DT>(p.x, obase + r * ostep));  // x + LN(y)
       store_pair<DT>(p.out, obase + r * ostep, o);
     }
   }
@@ -1328,7 +1397,7 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
 // waves per CU.  Token sums: recursive halving over the 32 lanes of a half
 // (lane c ends with the half-wave total of slot c), then the waves' totals
 // meet in LDS.  Needs CP2 % 32 == 0 and CP2 <= 256.
-template <int R, int DT>
+template <int R, int DT, bool PRE = false>
 __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   constexpr int R2 = R / 2;
   constexpr int T2 = next_pow2(R2);  // 32: token slots per half
@@ -1361,11 +1430,13 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   auto toff = [&](int j) { return (int64_t)(j < Q ? j : j + Q) * ostep; };  // tok(j) - Q h
   // residual, loaded in groups of 8 so that the loads in flight fit the
   // register budget of four waves per SIMD
+  if constexpr (!PRE) {  // post-norm: the statistics are those of x + y
 #pragma unroll
-  for (int g = 0; g < R2; g += 8) {
+    for (int g = 0; g < R2; g += 8) {
 #pragma unroll
-    for (int j = g; j < g + 8 && j < R2; ++j) z[j] = cadd(z[j], load_pair<DT>(p.x, obase + toff(j)));
-    asm volatile("" ::: "memory");
+      for (int j = g; j < g + 8 && j < R2; ++j) z[j] = cadd(z[j], load_pair<DT>(p.x, obase + toff(j)));
+      asm volatile("" ::: "memory");
+    }
   }
 
   // per-token sums over the workgroup's pairs: lane c ends with slot c's total
@@ -1405,7 +1476,8 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
 #pragma unroll
   for (int n = 0; n < R2; ++n) {
     const float mu = s_mean[tok(n)], rs = s_rstd[tok(n)];
-    const float2 o = make_float2((z[n].x - mu) * rs * g0 + b0, (z[n].y - mu) * rs * g1 + b1);
+    float2 o = make_float2((z[n].x - mu) * rs * g0 + b0, (z[n].y - mu) * rs * g1 + b1);
+    if constexpr (PRE) o = cadd(o, load_pair<DT>(p.x, obase + toff(n)));  // x + LN(y)
     store_pair<DT>(p.out, obase + toff(n), o);
   }
 }
@@ -1414,7 +1486,8 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
 //
 // One wave per token: lanes stride over the token's channel pairs (up to 32
 // pairs per lane, H*D <= 4096), z = x + y kept in registers, two-pass
-// statistics with wave butterflies, affine, store.
+// statistics with wave butterflies, affine, store (PRE: z = y, and x is added
+// after the affine step).
 
 struct NormParams {
   const float2* y;
@@ -1426,7 +1499,7 @@ struct NormParams {
   float inv_c, eps;
 };
 
-template <int DT>
+template <int DT, bool PRE = false>
 __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
   constexpr int MAXIT = 32;
   const int lane = threadIdx.x & 63;
@@ -1439,7 +1512,8 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
   for (int it = 0; it < MAXIT; ++it) {
     const int64_t c = lane + 64 * it;
     if (c < p.CP2) {
-      z[it] = cadd(load_nt(p.y + base + c), load_pair<DT>(p.x, base + c));
+      z[it] = load_nt(p.y + base + c);
+      if constexpr (!PRE) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
   }
@@ -1458,8 +1532,9 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
   for (int it = 0; it < MAXIT; ++it) {
     const int64_t c = lane + 64 * it;
     if (c < p.CP2) {
-      const float2 o = make_float2((z[it].x - mean) * rstd * p.gamma[2 * c] + p.beta[2 * c],
-                                   (z[it].y - mean) * rstd * p.gamma[2 * c + 1] + p.beta[2 * c + 1]);
+      float2 o = make_float2((z[it].x - mean) * rstd * p.gamma[2 * c] + p.beta[2 * c],
+                             (z[it].y - mean) * rstd * p.gamma[2 * c + 1] + p.beta[2 * c + 1]);
+      if constexpr (PRE) o = cadd(o, load_pair<DT>(p.x, base + c));  // x + LN(y)
       store_pair<DT>(p.out, base + c, o);
     }
   }

@@ -341,12 +341,18 @@ struct Shape {
   int64_t keep;
   int dtype;
   size_t esz;
+  int gate_kind;   // spectre_gate_kind
+  int norm_order;  // spectre_norm_order
 };
 
 int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, Shape& s,
-                Plan& pl) {
+                Plan& pl, int gate_kind = SPECTRE_GATE_REAL, int norm_order = SPECTRE_NORM_POST) {
   if (B < 1 || H < 1 || D < 1 || L < 2) return SPECTRE_EINVAL;
   if (dtype != SPECTRE_F32 && dtype != SPECTRE_BF16) return SPECTRE_EINVAL;
+  if (gate_kind != SPECTRE_GATE_REAL && gate_kind != SPECTRE_GATE_LOGIT &&
+      gate_kind != SPECTRE_GATE_COMPLEX)
+    return SPECTRE_EINVAL;
+  if (norm_order != SPECTRE_NORM_POST && norm_order != SPECTRE_NORM_PRE) return SPECTRE_EINVAL;
   if (L % 2 != 0) return SPECTRE_EINVAL;
   if (keep < 0 || keep > L / 2 + 1) return SPECTRE_EINVAL;
   if (H > kMaxC || D > kMaxC || H * D > kMaxC) return SPECTRE_EUNSUPPORTED;
@@ -366,6 +372,8 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   s.keep = keep;
   s.dtype = dtype;
   s.esz = dtype == SPECTRE_F32 ? 4 : 2;
+  s.gate_kind = gate_kind;
+  s.norm_order = norm_order;
   return SPECTRE_OK;
 }
 
@@ -395,9 +403,11 @@ size_t spectra_bytes(const Shape& s, const Plan& pl, bool want_fwd) {
 }
 
 // Bytes of the gate table the square B kernel of a multi-level plan reads
-// (H * L binary32 values, in its own bin order), else 0.
+// (H * L binary32 values, or pairs for a complex gate, in its own bin order),
+// else 0.
 size_t gate_table_bytes(const Shape& s, const Plan& pl) {
-  return pl.sq && !is_single(pl) ? (size_t)4 * s.H * s.L : 0;
+  const size_t per = s.gate_kind == SPECTRE_GATE_COMPLEX ? 8 : 4;
+  return pl.sq && !is_single(pl) ? per * s.H * s.L : 0;
 }
 
 size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
@@ -507,19 +517,21 @@ int launch_mid_p(const MidParams& p, dim3 grid, int threads, hipStream_t st) {
   return SPECTRE_OK;
 }
 
-template <int R, int IN>
-int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
+template <int R, int IN, bool CG>
+int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
   const int ncols = p.nslot * p.cpt;
-  // gate values in LDS when every workgroup's channel pairs lie in one head
-  const bool gl = IN == IN_C32 && p.gtab != nullptr && p.D % 2 == 0 && (p.D / 2) % p.cpt == 0;
+  // real gate values in LDS when every workgroup's channel pairs lie in one head
+  const bool one_head = p.D % 2 == 0 && (p.D / 2) % p.cpt == 0;
+  const bool gl = IN == IN_C32 && !CG && p.gtab != nullptr && one_head;
   const size_t lds = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
                      (gl ? (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float) : 0);
-  // tiled input, two slots of 4 pairs, R = 32: the persistent kernel that
-  // copies its input blocks to LDS asynchronously
-  if (IN == IN_C32 && gl && R == 32 && p.tiled && p.nslot == 2 && p.cpt == 4) {
+  // tiled input, two slots of 4 pairs, R = 32, pairs of one head: the kernel
+  // that copies its input blocks to LDS asynchronously
+  if (IN == IN_C32 && p.gtab != nullptr && one_head && R == 32 && p.tiled && p.nslot == 2 &&
+      p.cpt == 4) {
     static bool dma_attr = false;  // guarded by g_mu
     if (!dma_attr) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_dma),
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_dma<CG>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
         return SPECTRE_EHIP;
       dma_attr = true;
@@ -548,30 +560,36 @@ int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
       wgs = ((ntile + items - 1) / items + 31) / 32 * 32;
       if (wgs > ntile) wgs = ntile;
     }
-    hipLaunchKernelGGL(k_mid_dma, dim3((unsigned)wgs), dim3(256), lds, st, q);
+    const size_t lds_dma = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
+                           (CG ? 0 : (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float));
+    hipLaunchKernelGGL(k_mid_dma<CG>, dim3((unsigned)wgs), dim3(256), lds_dma, st, q);
     SPECTRE_LAUNCH_CHECK("B_mid_lds");
     return SPECTRE_OK;
   }
   static bool attr_set[2] = {false, false};  // guarded by g_mu
-  const void* fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, false>);
-  if constexpr (IN == IN_C32) {
-    if (gl) fn = reinterpret_cast<const void*>(&k_mid_sq<R, IN, true>);
-  }
+  const void* fn = gl ? reinterpret_cast<const void*>(&k_mid_sq<R, IN, true, CG>)
+                      : reinterpret_cast<const void*>(&k_mid_sq<R, IN, false, CG>);
   if (!attr_set[gl]) {
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return SPECTRE_EHIP;
     attr_set[gl] = true;
   }
-  if constexpr (IN == IN_C32) {
-    if (gl)
-      hipLaunchKernelGGL((k_mid_sq<R, IN, true>), grid, dim3(R * ncols), lds, st, p);
-    else
-      hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
-  } else {
-    hipLaunchKernelGGL((k_mid_sq<R, IN, false>), grid, dim3(R * ncols), lds, st, p);
-  }
+  if (gl)
+    hipLaunchKernelGGL((k_mid_sq<R, IN, true, CG>), grid, dim3(R * ncols), lds, st, p);
+  else
+    hipLaunchKernelGGL((k_mid_sq<R, IN, false, CG>), grid, dim3(R * ncols), lds, st, p);
   SPECTRE_LAUNCH_CHECK("B_mid_lds");
   return SPECTRE_OK;
+}
+
+// The gate table holds complex values for a complex gate (multi-level);
+// single-level kernels read the gate itself, whatever its kind.
+template <int R, int IN>
+int launch_mid_sq(const MidParams& p, dim3 grid, hipStream_t st) {
+  if constexpr (IN == IN_C32) {
+    if (p.gate_kind == GATE_COMPLEX) return launch_mid_sq_k<R, IN, true>(p, grid, st);
+  }
+  return launch_mid_sq_k<R, IN, false>(p, grid, st);
 }
 
 template <int IN>
@@ -595,18 +613,24 @@ int launch_mid(int P, const MidParams& p, dim3 grid, int threads, hipStream_t st
 }
 
 template <int R, int DT>
-int launch_final_r(const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
+int launch_final_r(const FinalParams& p, bool fuse, bool pre, int64_t B, hipStream_t st) {
   if constexpr (R == 48 || R == 64) {
     if (fuse && p.CP2 % 32 == 0) {  // CP2 <= 256 holds whenever fuse does
-      hipLaunchKernelGGL((k_final_split<R, DT>), dim3((unsigned)(B * p.M)), dim3((unsigned)(2 * p.CP2)),
-                         0, st, p);
+      const dim3 grid((unsigned)(B * p.M)), block((unsigned)(2 * p.CP2));
+      if (pre)
+        hipLaunchKernelGGL((k_final_split<R, DT, true>), grid, block, 0, st, p);
+      else
+        hipLaunchKernelGGL((k_final_split<R, DT, false>), grid, block, 0, st, p);
       SPECTRE_LAUNCH_CHECK("C1_inv_norm");
       return SPECTRE_OK;
     }
   }
   if (fuse) {
     dim3 grid((unsigned)(B * p.M));
-    hipLaunchKernelGGL((k_final<R, DT, true>), grid, dim3((unsigned)p.CP2), 0, st, p);
+    if (pre)
+      hipLaunchKernelGGL((k_final<R, DT, true, true>), grid, dim3((unsigned)p.CP2), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_final<R, DT, true, false>), grid, dim3((unsigned)p.CP2), 0, st, p);
   } else {
     dim3 grid((unsigned)((p.lines + 255) / 256));
     hipLaunchKernelGGL((k_final<R, DT, false>), grid, dim3(256), 0, st, p);
@@ -616,28 +640,35 @@ int launch_final_r(const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
 }
 
 template <int DT>
-int launch_final(int64_t R, const FinalParams& p, bool fuse, int64_t B, hipStream_t st) {
+int launch_final(int64_t R, const FinalParams& p, bool fuse, bool pre, int64_t B, hipStream_t st) {
   switch (R) {
-    case 2: return launch_final_r<2, DT>(p, fuse, B, st);
-    case 4: return launch_final_r<4, DT>(p, fuse, B, st);
-    case 6: return launch_final_r<6, DT>(p, fuse, B, st);
-    case 8: return launch_final_r<8, DT>(p, fuse, B, st);
-    case 12: return launch_final_r<12, DT>(p, fuse, B, st);
-    case 16: return launch_final_r<16, DT>(p, fuse, B, st);
-    case 24: return launch_final_r<24, DT>(p, fuse, B, st);
-    case 32: return launch_final_r<32, DT>(p, fuse, B, st);
-    case 48: return launch_final_r<48, DT>(p, fuse, B, st);
-    case 64: return launch_final_r<64, DT>(p, fuse, B, st);
+    case 2: return launch_final_r<2, DT>(p, fuse, pre, B, st);
+    case 4: return launch_final_r<4, DT>(p, fuse, pre, B, st);
+    case 6: return launch_final_r<6, DT>(p, fuse, pre, B, st);
+    case 8: return launch_final_r<8, DT>(p, fuse, pre, B, st);
+    case 12: return launch_final_r<12, DT>(p, fuse, pre, B, st);
+    case 16: return launch_final_r<16, DT>(p, fuse, pre, B, st);
+    case 24: return launch_final_r<24, DT>(p, fuse, pre, B, st);
+    case 32: return launch_final_r<32, DT>(p, fuse, pre, B, st);
+    case 48: return launch_final_r<48, DT>(p, fuse, pre, B, st);
+    case 64: return launch_final_r<64, DT>(p, fuse, pre, B, st);
     default: return SPECTRE_EUNSUPPORTED;
   }
 }
 
-int launch_norm(const NormParams& p, int dtype, hipStream_t st) {
+int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
   dim3 grid((unsigned)((p.ntok + 3) / 4));
-  if (dtype == SPECTRE_F32)
-    hipLaunchKernelGGL((k_layernorm<IN_F32>), grid, dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_layernorm<IN_BF16>), grid, dim3(256), 0, st, p);
+  if (dtype == SPECTRE_F32) {
+    if (pre)
+      hipLaunchKernelGGL((k_layernorm<IN_F32, true>), grid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_layernorm<IN_F32, false>), grid, dim3(256), 0, st, p);
+  } else {
+    if (pre)
+      hipLaunchKernelGGL((k_layernorm<IN_BF16, true>), grid, dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_layernorm<IN_BF16, false>), grid, dim3(256), 0, st, p);
+  }
   SPECTRE_LAUNCH_CHECK("LN_norm");
   return SPECTRE_OK;
 }
@@ -688,6 +719,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     g.keep = s.keep;
     g.total = s.H * s.L;
     g.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
+    g.kind = s.gate_kind;
   }
   const bool gate_in_a1 = g.gtab != nullptr;  // multi-level square B: A1 builds the table
 
@@ -739,6 +771,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
       m.tiled = tiled || tiled3 ? 1 : 0;
     }
     m.gate = gate;
+    m.gate_kind = s.gate_kind;
     m.gtab = g.gtab;
     m.ncol = (int)(pl.L1 * pl.L2);
     m.twN = tab->twN;
@@ -782,6 +815,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
 
   const float inv_c = (float)(1.0 / (double)s.C);
   const float eps = 1e-5f;
+  const bool pre = s.norm_order == SPECTRE_NORM_PRE;
   if (single) {
     if (!want_out) return SPECTRE_OK;
     NormParams n{};
@@ -794,7 +828,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     n.CP2 = CP2;
     n.inv_c = inv_c;
     n.eps = eps;
-    return launch_norm(n, s.dtype, st);
+    return launch_norm(n, s.dtype, pre, st);
   }
 
   // ---- inverse strided passes
@@ -826,11 +860,11 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   float* ybuf = want_out ? reinterpret_cast<float*>(T + pairs) : y;
   if (fuse) {
     f.out = out;
-    return s.dtype == SPECTRE_F32 ? launch_final<IN_F32>(pl.L1, f, true, s.B, st)
-                                  : launch_final<IN_BF16>(pl.L1, f, true, s.B, st);
+    return s.dtype == SPECTRE_F32 ? launch_final<IN_F32>(pl.L1, f, true, pre, s.B, st)
+                                  : launch_final<IN_BF16>(pl.L1, f, true, pre, s.B, st);
   }
   f.out = ybuf;
-  rc = launch_final<IN_F32>(pl.L1, f, false, s.B, st);
+  rc = launch_final<IN_F32>(pl.L1, f, false, false, s.B, st);
   if (rc || !want_out) return rc;
   NormParams n{};
   n.y = reinterpret_cast<const float2*>(ybuf);
@@ -842,7 +876,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   n.CP2 = CP2;
   n.inv_c = inv_c;
   n.eps = eps;
-  return launch_norm(n, s.dtype, st);
+  return launch_norm(n, s.dtype, pre, st);
 }
 
 }  // namespace
@@ -852,13 +886,14 @@ using namespace spectre;
 
 extern "C" {
 
-int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x, const float* gate,
-                    const float* gamma, const float* beta, void* out, int64_t B, int64_t H,
-                    int64_t L, int64_t D, int64_t keep_bins, int dtype, hipStream_t stream) {
+int spectre_mix_fwd_ex(const void* q, const void* k, const void* v, const void* x,
+                       const float* gate, const float* gamma, const float* beta, void* out,
+                       int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                       int gate_kind, int norm_order, hipStream_t stream) {
   if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
   Shape s;
   Plan pl;
-  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl, gate_kind, norm_order);
   if (rc) return rc;
   const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
   for (const void* p : ptrs)
@@ -869,13 +904,20 @@ int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x, 
   return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream);
 }
 
-int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate, float* y,
-                  int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
-                  hipStream_t stream) {
+int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x, const float* gate,
+                    const float* gamma, const float* beta, void* out, int64_t B, int64_t H,
+                    int64_t L, int64_t D, int64_t keep_bins, int dtype, hipStream_t stream) {
+  return spectre_mix_fwd_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, dtype,
+                            SPECTRE_GATE_REAL, SPECTRE_NORM_POST, stream);
+}
+
+int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* gate, float* y,
+                     int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                     int gate_kind, hipStream_t stream) {
   if (!q || !k || !v || !gate || !y) return SPECTRE_EINVAL;
   Shape s;
   Plan pl;
-  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl, gate_kind, SPECTRE_NORM_POST);
   if (rc) return rc;
   const void* ptrs[] = {q, k, v, gate, y};
   for (const void* p : ptrs)
@@ -886,11 +928,24 @@ int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate
   return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream);
 }
 
-size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype) {
+int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate, float* y,
+                  int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                  hipStream_t stream) {
+  return spectre_mix_y_ex(q, k, v, gate, y, B, H, L, D, keep_bins, dtype, SPECTRE_GATE_REAL,
+                          stream);
+}
+
+size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D, int dtype,
+                                      int gate_kind) {
   Shape s;
   Plan pl;
-  if (check_shape(B, H, L, D, 0, dtype, s, pl) != SPECTRE_OK) return 0;
+  if (check_shape(B, H, L, D, 0, dtype, s, pl, gate_kind, SPECTRE_NORM_POST) != SPECTRE_OK)
+    return 0;
   return workspace_for(s, pl, true);
+}
+
+size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype) {
+  return spectre_mix_workspace_bytes_ex(B, H, L, D, dtype, SPECTRE_GATE_REAL);
 }
 
 int spectre_mix_plan(int64_t L, int64_t* l1, int64_t* l2, int64_t* l3) {

@@ -65,6 +65,37 @@ extern "C" {
 
 typedef enum { SPECTRE_F32 = 0, SPECTRE_BF16 = 1 } spectre_dtype;
 
+/*
+ * How the gate array is read (the *_ex entry points; the others use REAL).
+ *  SPECTRE_GATE_REAL:    gate [H][L/2+1] f32, the real multiplier G[h][f]
+ *                        (the article's section 2.2, a learnable G(f)).
+ *  SPECTRE_GATE_LOGIT:   gate [H][L/2+1] f32 holds logits a; the multiplier is
+ *                        the logistic sigmoid 1 / (1 + exp(-a)), computed in
+ *                        binary32 (section 3.1 recommends a sigmoid gate).
+ *  SPECTRE_GATE_COMPLEX: gate [H][L/2+1][2] f32, the real and imaginary parts
+ *                        of a complex multiplier (section 2.4 carries relative
+ *                        position as a frequency-dependent rotation factor in
+ *                        G(f)).  Bins above L/2 use its conjugate (the output
+ *                        stays real), and at bins 0 and L/2 only its real part
+ *                        acts, as the inverse real FFT reads only the real
+ *                        part of those bins.
+ */
+typedef enum {
+  SPECTRE_GATE_REAL = 0,
+  SPECTRE_GATE_LOGIT = 1,
+  SPECTRE_GATE_COMPLEX = 2
+} spectre_gate_kind;
+
+/*
+ * Where the LayerNorm sits (the *_ex entry points; the others use POST).
+ *  SPECTRE_NORM_POST: out = LayerNorm(x + y)   (section 2.2's pseudocode)
+ *  SPECTRE_NORM_PRE:  out = x + LayerNorm(y)   (the order section 3.3 settles
+ *                     on: the inverse FFT output is normalised, then added
+ *                     to x), the same LayerNorm (eps 1e-5, biased variance,
+ *                     gamma, beta) applied to y alone.
+ */
+typedef enum { SPECTRE_NORM_POST = 0, SPECTRE_NORM_PRE = 1 } spectre_norm_order;
+
 typedef enum {
   SPECTRE_OK = 0,
   SPECTRE_EINVAL = -1,       /* a null/misaligned pointer, bad size, dtype or keep_bins, aliasing */
@@ -95,10 +126,35 @@ int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate
                   hipStream_t stream);
 
 /*
+ * The mix with a chosen gate kind and norm order (spectre_gate_kind,
+ * spectre_norm_order above); every other argument as for spectre_mix_fwd.
+ * gate is [H][L/2+1] f32, or [H][L/2+1][2] f32 for SPECTRE_GATE_COMPLEX.
+ * spectre_mix_fwd(...) is spectre_mix_fwd_ex(..., SPECTRE_GATE_REAL,
+ * SPECTRE_NORM_POST, stream).  An unknown gate_kind or norm_order returns
+ * SPECTRE_EINVAL (nothing enqueued).
+ */
+int spectre_mix_fwd_ex(const void* q, const void* k, const void* v, const void* x,
+                       const float* gate, const float* gamma, const float* beta, void* out,
+                       int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                       int dtype, int gate_kind, int norm_order, hipStream_t stream);
+
+/*
+ * spectre_mix_y with a chosen gate kind (y does not depend on the norm order).
+ */
+int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* gate, float* y,
+                     int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins, int dtype,
+                     int gate_kind, hipStream_t stream);
+
+/*
  * Device workspace bytes a spectre_mix_fwd call of this shape uses (0 if the
  * shape is invalid or unsupported).  Pure host arithmetic; no device call.
  */
 size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype);
+
+/* The same for a spectre_mix_fwd_ex call with this gate kind (a complex gate
+ * doubles the gate table of multi-level plans). */
+size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D, int dtype,
+                                      int gate_kind);
 
 /*
  * Transform plan for length L, for inspection: the sequence length factors

@@ -67,6 +67,17 @@ class DeviceInputs:
         return sm.spectre_mix_y(self.q, self.k, self.v, self.gate, y, w.B, w.H, w.L, w.D, keep,
                                 w.dtype, stream)
 
+    def fwd_ex(self, out, gate_kind, norm_order, stream=None):
+        w = self.w
+        return sm.spectre_mix_fwd_ex(self.q, self.k, self.v, self.x, self.gate, self.gamma,
+                                     self.beta, out, w.B, w.H, w.L, w.D, w.keep_bins, w.dtype,
+                                     gate_kind, norm_order, stream)
+
+    def y_ex(self, y, gate_kind, stream=None):
+        w = self.w
+        return sm.spectre_mix_y_ex(self.q, self.k, self.v, self.gate, y, w.B, w.H, w.L, w.D,
+                                   w.keep_bins, w.dtype, gate_kind, stream)
+
 
 def run_out(w, inp, keep=None):
     """out of the GPU path as float64 host array [B, L, H, D]."""

@@ -74,6 +74,30 @@ def test_fwd_rejects_before_device(kw, expect):
     assert fwd(**kw) == expect
 
 
+def fwd_ex(gate_kind, norm_order, **kw):
+    a = dict(q=GOOD, k=GOOD + 0x1000000, v=GOOD + 0x2000000, x=GOOD + 0x3000000,
+             gate=GOOD + 0x4000000, gamma=GOOD + 0x5000000, beta=GOOD + 0x6000000,
+             out=GOOD + 0x70000000, B=1, H=8, L=65536, D=64, keep_bins=32769, dtype=0)
+    a.update(kw)
+    return sm.spectre_mix_fwd_ex(a["q"], a["k"], a["v"], a["x"], a["gate"], a["gamma"], a["beta"],
+                                 a["out"], a["B"], a["H"], a["L"], a["D"], a["keep_bins"],
+                                 a["dtype"], gate_kind, norm_order, 0)
+
+
+@pytest.mark.parametrize("gate_kind,norm_order", [(3, 0), (-1, 0), (0, 2), (2, -1)])
+def test_fwd_ex_rejects_unknown_variant(gate_kind, norm_order):
+    assert fwd_ex(gate_kind, norm_order) == sm.SPECTRE_EINVAL
+    assert sm.spectre_mix_y_ex(GOOD, GOOD + 0x1000000, GOOD + 0x2000000, GOOD + 0x4000000,
+                               GOOD + 0x70000000, 1, 8, 65536, 64, 32769, 0, 3, 0) == \
+        sm.SPECTRE_EINVAL
+
+
+def test_fwd_ex_checks_shapes_like_fwd():
+    assert fwd_ex(2, 1, L=65535, keep_bins=1) == sm.SPECTRE_EINVAL
+    assert fwd_ex(1, 0, L=5 * 4096, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED
+    assert fwd_ex(2, 1, q=GOOD + 8) == sm.SPECTRE_EINVAL
+
+
 def test_y_rejects_before_device():
     assert sm.spectre_mix_y(0, GOOD, GOOD, GOOD, GOOD, 1, 8, 4096, 64, 2049, 0, 0) == \
         sm.SPECTRE_EINVAL
@@ -133,6 +157,13 @@ def test_workspace_bytes():
     # L = 256: single level, square kernel reading the gate itself (no table)
     assert sm.spectre_mix_workspace_bytes(1, 2, 256, 16, 0) == 4 * 256 * 32
     assert sm.spectre_mix_workspace_bytes(1, 8, 65535, 64, 0) == 0
+    # a complex gate doubles the gate table of multi-level plans; the others keep it
+    assert sm.spectre_mix_workspace_bytes_ex(1, 8, 65536, 64, 0, 2) == \
+        sm.spectre_mix_workspace_bytes(1, 8, 65536, 64, 0) + 4 * 8 * 65536
+    assert sm.spectre_mix_workspace_bytes_ex(1, 8, 65536, 64, 0, 1) == \
+        sm.spectre_mix_workspace_bytes(1, 8, 65536, 64, 0)
+    assert sm.spectre_mix_workspace_bytes_ex(1, 2, 256, 16, 0, 2) == 4 * 256 * 32
+    assert sm.spectre_mix_workspace_bytes_ex(1, 8, 65536, 64, 0, 5) == 0
 
 
 def test_release_without_device_is_clean():

@@ -207,6 +207,31 @@ def make_inputs(w: Workload) -> dict:
     return r
 
 
+# gate kinds of the variant entry points (the same numbers as the C ABI)
+GATE_REAL, GATE_LOGIT, GATE_COMPLEX = 0, 1, 2
+_GATE_LOGIT_SEED, _GATE_RE_SEED, _GATE_IM_SEED = 51, 52, 53
+
+
+def make_gate(w: Workload, gate_kind: int) -> np.ndarray:
+    """The gate array for a gate kind: the workload's own gate (real), logits
+    ~ N(0, 2^2) (their sigmoids spread over (0, 1)), or a complex gate with
+    real and imaginary parts ~ U(-1, 1), laid out [H, L//2 + 1, 2].  Bins at
+    or above keep_bins are zeroed when the workload asks for that."""
+    if gate_kind == GATE_REAL:
+        return make_inputs(w)["gate"]
+    if gate_kind == GATE_LOGIT:
+        g = 2.0 * normal(w.seed(_GATE_LOGIT_SEED), (w.H, w.nbins))
+        if w.gate_zero_above_keep:
+            g[:, w.keep_bins:] = -30.0
+        return g.astype(np.float32)
+    re = uniform(w.seed(_GATE_RE_SEED), (w.H, w.nbins), -1.0, 1.0)
+    im = uniform(w.seed(_GATE_IM_SEED), (w.H, w.nbins), -1.0, 1.0)
+    g = np.stack([re, im], -1)
+    if w.gate_zero_above_keep:
+        g[:, w.keep_bins:] = 0.0
+    return np.ascontiguousarray(g, dtype=np.float32)
+
+
 def sample_tokens(w: Workload, count: int, seed: int = 99) -> np.ndarray:
     """Flat token ids b*L + t to check at full size: the first and last token,
     the tokens on either side of each batch boundary, and a seeded spread."""
