@@ -58,20 +58,22 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(name: str, w) -> int:
+def kernel_bytes(name: str, w, gate_kind: int = 0) -> int:
     """Algorithmic HBM bytes of one launch of a pass: every tensor element the
     pass must read or write once (inputs, the spectra it exchanges, outputs,
-    the kept gate bins)."""
+    the kept gate bins).  A complex gate has 8 bytes per bin, so its gate and
+    gate-table bytes double."""
     N = w.N
     s = w.elem_bytes
     spec = 4 * N  # one tensor's spectrum as binary32 complex channel pairs
-    gate = 4 * w.H * min(w.keep_bins, w.nbins)
+    gb = 8 if gate_kind == 2 else 4  # bytes per gate value
+    gate = gb * w.H * min(w.keep_bins, w.nbins)
     if name == "A1_fwd_strided":
         import efficient_attention_fft_amd as sm
         _, (l1, l2, l3) = sm.spectre_mix_plan(w.L)
         folded = 0
         if l3 in (256, 1024):  # multi-level square B kernel: this launch also builds the gate table
-            folded = 4 * w.H * min(w.keep_bins, w.nbins) + 4 * w.H * w.L
+            folded = gate + gb * w.H * w.L
         return 3 * N * s + 3 * spec + folded
     if name == "A2_fwd_strided":
         return 6 * spec
@@ -81,7 +83,7 @@ def kernel_bytes(name: str, w) -> int:
         if l1 == 1 and l2 == 1:  # single level: the kept gate bins themselves
             return 3 * N * s + spec + gate
         if l3 in (256, 1024):
-            gate = 4 * w.H * w.L  # the gate table A1's launch writes
+            gate = gb * w.H * w.L  # the gate table A1's launch writes
         return 3 * spec + spec + gate
     if name == "C2_inv_strided":
         return 2 * spec
@@ -108,12 +110,13 @@ def model_bytes(w) -> int:
     return m_min + extra
 
 
-def cpu_baseline(w, inp):
+def cpu_baseline(w, inp, gate_kind=0, norm_order=0):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
     oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
-                       inp["beta"], w.keep_bins, dtype=w.dtype, nthreads=threads)
+                       inp["beta"], w.keep_bins, dtype=w.dtype, nthreads=threads,
+                       gate_kind=gate_kind, norm_order=norm_order)
     dt = time.perf_counter() - t0
     return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
             "kind": "oracle", "sample": "the whole workload once: %d columns x %d tokens, "
@@ -145,6 +148,9 @@ def run_bench(args):
     w = workloads.WORKLOADS[args.workload]
     print("bench: workload %s, generating inputs" % w.name, file=sys.stderr, flush=True)
     inp = workloads.make_inputs(w)
+    gk, no = args.gate_kind, args.norm_order
+    if gk != 0:
+        inp["gate"] = workloads.make_gate(w, gk)
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -157,8 +163,11 @@ def run_bench(args):
     stream = torch.cuda.current_stream()
 
     def step():
-        return sm.spectre_mix_fwd(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
-                                  w.keep_bins, w.dtype, stream)
+        if gk == 0 and no == 0:
+            return sm.spectre_mix_fwd(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
+                                      w.keep_bins, w.dtype, stream)
+        return sm.spectre_mix_fwd_ex(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
+                                     w.keep_bins, w.dtype, gk, no, stream)
 
     for _ in range(args.warmup):
         sm.check(step())
@@ -193,10 +202,10 @@ def run_bench(args):
           file=sys.stderr, flush=True)
     dom = max(per_kernel, key=per_kernel.get)
     nl = launches[dom]
-    dom_bytes = kernel_bytes(dom, w) / nl  # per launch
+    dom_bytes = kernel_bytes(dom, w, gk) / nl  # per launch
     avg_ms = per_kernel[dom] / nl
     achieved = dom_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = traffic_for(dom, w)
+    traffic = traffic_for(dom, w) if gk == 0 and no == 0 else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
@@ -229,13 +238,15 @@ def run_bench(args):
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == workloads.F32 else "bf16",
         "data": "synthetic",
-        "config": dict(w.describe(), parallelism="single GPU"),
+        "config": dict(w.describe(), parallelism="single GPU",
+                       **({"gate_kind": ["real", "logit", "complex"][gk],
+                           "norm": ["post", "pre"][no]} if (gk or no) else {})),
         "roofline": roofline,
         "whole_call": whole,
     }
     if not args.profile_run and not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, inp)
+        res["cpu_baseline"] = cpu_baseline(w, inp, gk, no)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
@@ -360,6 +371,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate-kind", type=int, default=0, choices=[0, 1, 2],
+                    help="0 real gate, 1 logit gate (sigmoid in the kernels), 2 complex gate")
+    ap.add_argument("--norm-order", type=int, default=0, choices=[0, 1],
+                    help="0 out = LN(x + y), 1 out = x + LN(y)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
