@@ -60,6 +60,9 @@ def _bind(lib):
                                           ci, ci, ci, vp, vp, ci]
     lib.oracle_spectre_mix_tokens_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                                  i64, i64, ci, ci, ci, vp, i64, vp, vp, ci]
+    lib.oracle_spectre_mix_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                               i64, i64, i64, i64, ci, vp, vp, ci]
+    lib.oracle_spectre_mix_chunked.restype = ci
     for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
               lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads,
               lib.oracle_spectre_y_ex, lib.oracle_layernorm_residual_ex,
@@ -205,3 +208,28 @@ def spectre_mix_tokens(q, k, v, x, gate, gamma, beta, keep_bins: int, tokens,
                                                 tokens.ctypes.data, n, out.ctypes.data,
                                                 y.ctypes.data, nthreads))
     return out, y
+
+
+def spectre_mix_chunked(q, k, v, x, gate, gate_blocks, gamma, beta, fft_len: int,
+                        keep_bins: int, keep_blocks: int, dtype: int = 0, nthreads: int = 0,
+                        want_y: bool = False):
+    """The chunked mix: blocks of fft_len tokens mixed on their own (gate
+    [H, fft_len//2 + 1]), plus the mix of the block means over the block axis
+    (gate_blocks [H, nb//2 + 1], nb = L // fft_len) added to every token of
+    its block, then LN(x + y).  Returns out (and y if want_y), float64."""
+    B, L, H, D = q.shape
+    q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
+    nb = L // fft_len
+    gate = _c(gate, np.float32)
+    gate_blocks = _c(gate_blocks, np.float32)
+    assert gate.shape == (H, fft_len // 2 + 1) and gate_blocks.shape == (H, nb // 2 + 1)
+    gamma, beta = (_c(t, np.float32) for t in (gamma, beta))
+    out = np.empty((B, L, H, D), np.float64)
+    y = np.empty((B, L, H, D), np.float64) if want_y else None
+    _check(_load().oracle_spectre_mix_chunked(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                              x.ctypes.data, gate.ctypes.data,
+                                              gate_blocks.ctypes.data, gamma.ctypes.data,
+                                              beta.ctypes.data, B, H, L, D, fft_len, keep_bins,
+                                              keep_blocks, dtype, out.ctypes.data,
+                                              y.ctypes.data if want_y else None, nthreads))
+    return (out, y) if want_y else out

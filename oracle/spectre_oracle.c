@@ -53,6 +53,15 @@
  *  - norm order 0 (post-norm, section 2.2's pseudocode): out = LN(x + y);
  *    norm order 1 (pre-norm, the order section 3.3 settles on): out =
  *    x + LN(y), the same LayerNorm applied to y alone.
+ *
+ * Chunked mix (oracle_spectre_mix_chunked; section 3.2's fft_len below L:
+ * an FFT inside 4096-token blocks, then one more low-frequency interaction
+ * between blocks, whose form the article leaves open).  Reading: the
+ * sequence is cut into nb = L / F blocks of F tokens and each block is mixed
+ * on its own (gate [H][F/2 + 1], keep_bins); then the block means of q, k, v
+ * (per column, nb values each) are mixed by the same operation over the
+ * block axis (gate_blocks [H][nb/2 + 1], keep_blocks), and that result is
+ * added to every token of its block; then the residual and the LayerNorm.
  */
 #include <math.h>
 #include <pthread.h>
@@ -267,6 +276,7 @@ int oracle_fft(int64_t n, const double *re_in, const double *im_in, double *re_o
 
 static inline double load_elem(const void *base, int dtype, int64_t i) {
   if (dtype == 0) return (double)((const float *)base)[i];
+  if (dtype == 2) return ((const double *)base)[i]; /* internal: the chunked mix's block means */
   uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -617,6 +627,72 @@ int oracle_spectre_mix_tokens(const void *q, const void *k, const void *v, const
                               double *out_tok, double *y_tok, int nthreads) {
   return oracle_spectre_mix_tokens_ex(q, k, v, x, gate, gamma, beta, B, H, L, D, keep, dtype,
                                       0, 0, tokens, ntok, out_tok, y_tok, nthreads);
+}
+
+/* The chunked mix (see the header): out and optionally y, for every token. */
+int oracle_spectre_mix_chunked(const void *q, const void *k, const void *v, const void *x,
+                               const float *gate, const float *gate_blocks, const float *gamma,
+                               const float *beta, int64_t B, int64_t H, int64_t L, int64_t D,
+                               int64_t F, int64_t keep, int64_t keep_blocks, int dtype,
+                               double *out, double *y_out, int nthreads) {
+  if (!q || !k || !v || !x || !gate || !gate_blocks || !gamma || !beta || !out)
+    return ORACLE_EINVAL;
+  if (F < 1 || L < 1 || L % F != 0) return ORACLE_EINVAL;
+  const int64_t nb = L / F;
+  int s = check_dims(B, H, L, D, 0, dtype);
+  if (!s) s = check_dims(B * nb, H, F, D, keep, dtype);
+  if (!s && (keep_blocks < 0 || keep_blocks > nb / 2 + 1)) s = ORACLE_EINVAL;
+  if (s) return s;
+  const int64_t C = H * D, ntok = B * L;
+  double *y = y_out ? y_out : (double *)malloc(sizeof(double) * (size_t)(ntok * C));
+  double *means = (double *)malloc(sizeof(double) * (size_t)(3 * B * nb * C));
+  double *y2 = (double *)malloc(sizeof(double) * (size_t)(B * nb * C));
+  if (!y || !means || !y2) {
+    if (!y_out) free(y);
+    free(means);
+    free(y2);
+    return ORACLE_ENOMEM;
+  }
+  /* each block on its own: [B, L, H, D] read as [B * nb, F, H, D] */
+  s = oracle_spectre_y_ex(q, k, v, gate, B * nb, H, F, D, keep, dtype, 0, y, nthreads);
+  if (s == ORACLE_OK) {
+    /* block means of q, k, v: [3][B][nb][C] */
+    const void *src[3] = {q, k, v};
+    for (int a = 0; a < 3; ++a)
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < nb; ++j)
+          for (int64_t c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < F; ++t)
+              acc += load_elem(src[a], dtype, (b * L + j * F + t) * C + c);
+            means[((a * B + b) * nb + j) * C + c] = acc / (double)F;
+          }
+    /* the same mix over the block axis, on the double block means */
+    mix_job J;
+    memset(&J, 0, sizeof J);
+    J.q = means;
+    J.k = means + B * nb * C;
+    J.v = means + 2 * B * nb * C;
+    J.gate = gate_blocks;
+    J.B = B;
+    J.H = H;
+    J.L = nb;
+    J.D = D;
+    J.keep = keep_blocks;
+    J.dtype = 2;
+    J.y = y2;
+    s = run_mix(&J, nthreads);
+  }
+  if (s == ORACLE_OK) {
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t t = 0; t < L; ++t)
+        for (int64_t c = 0; c < C; ++c) y[(b * L + t) * C + c] += y2[(b * nb + t / F) * C + c];
+    layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, 0, out);
+  }
+  if (!y_out) free(y);
+  free(means);
+  free(y2);
+  return s;
 }
 
 /* Number of threads a call with `nthreads` would use (0 = all online CPUs). */

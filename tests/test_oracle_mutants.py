@@ -30,6 +30,10 @@ MUTANTS = {
                               "o[c] = load_elem(x, dtype, xr * C + c) + yr[c];"),
     "pre_norm_residual_dropped": ("if (pre) o[c] += load_elem(x, dtype, xr * C + c);",
                                   "if (pre) o[c] += 0.0;"),
+    "chunk_mean_scale": ("means[((a * B + b) * nb + j) * C + c] = acc / (double)F;",
+                         "means[((a * B + b) * nb + j) * C + c] = acc;"),
+    "chunk_block_index": ("y2[(b * nb + t / F) * C + c]", "y2[(b * nb + (t / F + 1) % nb) * C + c]"),
+    "chunk_block_gate": ("J.gate = gate_blocks;", "J.gate = gate;"),
     "inverse_scale_dropped": ("double re = bufq[t].re * invL, im = bufq[t].im * invL;",
                               "double re = bufq[t].re, im = bufq[t].im * invL;"),
     "truncation_inclusive": ("if (f < J->keep) {", "if (f <= J->keep) {"),
@@ -129,6 +133,19 @@ def _pins_pass() -> bool:
         out = oracle.spectre_mix(q, k, v, x, np.ones((H, nb), np.float32),
                                  np.ones(H * 2, np.float32), beta, 0, norm_order=1)
         if np.abs(out - (x.astype(np.float64) + beta.reshape(H, 2))).max() > 0.0:
+            return False
+        # chunked mix: piecewise-constant inputs, no in-block gate
+        B, H, D, F, nb = 1, 2, 2, 16, 12
+        cq, ck, cv = (rng.standard_normal((B, nb, H, D)).astype(np.float32) for _ in range(3))
+        qq, kk, vv = (np.repeat(c, F, axis=1) for c in (cq, ck, cv))
+        xx = rng.standard_normal((B, F * nb, H, D)).astype(np.float32)
+        gb = rng.uniform(0.1, 1, (H, nb // 2 + 1)).astype(np.float32)
+        ones, zeros = np.ones(H * D, np.float32), np.zeros(H * D, np.float32)
+        _, y = oracle.spectre_mix_chunked(qq, kk, vv, xx, np.zeros((H, F // 2 + 1), np.float32),
+                                          gb, ones, zeros, F, F // 2 + 1, 5, want_y=True)
+        ref = np.repeat(closed_form_y(*(c.astype(np.float64) for c in (cq, ck, cv)), gb, 5), F,
+                        axis=1)
+        if np.abs(y - ref).max() > 1e-10:
             return False
     except oracle.OracleError:
         return False

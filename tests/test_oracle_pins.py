@@ -489,3 +489,74 @@ def test_variant_arguments_rejected():
     with pytest.raises(oracle.OracleError):
         oracle.spectre_mix(q, q, q, q, g, np.ones(2, np.float32), np.zeros(2, np.float32), 5,
                            norm_order=2)
+
+
+# ---------------------------------------------------------------- chunked mix
+#
+# Section 3.2's fft_len below L: blocks mixed on their own, plus the block
+# means mixed over the block axis and added back to every token of a block.
+
+def _chunk_inputs(rng, B, L, H, D):
+    q, k, v, x = (rng.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    gamma = rng.uniform(0.5, 1.5, H * D).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(H * D)).astype(np.float32)
+    return q, k, v, x, gamma, beta
+
+
+def test_chunked_without_block_gate_mixes_blocks_alone():
+    B, L, H, D, F = 2, 96, 2, 2, 24
+    rng = np.random.default_rng(21)
+    q, k, v, x, gamma, beta = _chunk_inputs(rng, B, L, H, D)
+    g = rng.uniform(0, 1, (H, F // 2 + 1)).astype(np.float32)
+    gb = np.zeros((H, L // F // 2 + 1), np.float32)
+    _, y = oracle.spectre_mix_chunked(q, k, v, x, g, gb, gamma, beta, F, 9, 3, want_y=True)
+    for j in range(L // F):
+        sl = slice(j * F, (j + 1) * F)
+        ref = oracle.spectre_y(q[:, sl], k[:, sl], v[:, sl], g, 9)
+        assert np.abs(y[:, sl] - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max())
+
+
+def test_chunked_block_term_on_piecewise_constant_inputs():
+    """With no in-block gate, y is the mix of the block values over the block
+    axis, repeated over each block's tokens."""
+    B, H, D, F, nb = 1, 2, 2, 16, 12
+    L = F * nb
+    rng = np.random.default_rng(22)
+    cq, ck, cv = (rng.standard_normal((B, nb, H, D)).astype(np.float32) for _ in range(3))
+    q, k, v = (np.repeat(c, F, axis=1) for c in (cq, ck, cv))
+    x = rng.standard_normal((B, L, H, D)).astype(np.float32)
+    g = np.zeros((H, F // 2 + 1), np.float32)
+    gb = rng.uniform(0, 1, (H, nb // 2 + 1)).astype(np.float32)
+    ones, zeros = np.ones(H * D, np.float32), np.zeros(H * D, np.float32)
+    out, y = oracle.spectre_mix_chunked(q, k, v, x, g, gb, ones, zeros, F, F // 2 + 1, 5,
+                                        want_y=True)
+    ref = np.repeat(closed_form_y(cq.astype(np.float64), ck.astype(np.float64),
+                                  cv.astype(np.float64), gb, 5), F, axis=1)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    assert np.abs(out - oracle.layernorm_residual(ref, x, ones, zeros)).max() <= 1e-9
+
+
+def test_chunked_single_block_adds_product_of_means():
+    """fft_len = L: one block, the plain mix, plus the length-1 mix of the
+    means, G_b[h][0] * mean(q) * mean(k) * mean(v) per column."""
+    B, L, H, D = 2, 64, 2, 3
+    rng = np.random.default_rng(23)
+    q, k, v, x, gamma, beta = _chunk_inputs(rng, B, L, H, D)
+    g = rng.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gb = rng.uniform(0, 1, (H, 1)).astype(np.float32)
+    _, y = oracle.spectre_mix_chunked(q, k, v, x, g, gb, gamma, beta, L, 20, 1, want_y=True)
+    plain = oracle.spectre_y(q, k, v, g, 20)
+    m = [t.astype(np.float64).mean(axis=1, keepdims=True) for t in (q, k, v)]
+    term = gb[:, 0].astype(np.float64).reshape(1, 1, H, 1) * m[0] * m[1] * m[2]
+    assert np.abs(y - (plain + term)).max() <= 1e-12 * max(1.0, np.abs(y).max())
+
+
+def test_chunked_rejects_bad_block_sizes():
+    q = np.zeros((1, 48, 1, 2), np.float32)
+    ones, zeros = np.ones(2, np.float32), np.zeros(2, np.float32)
+    with pytest.raises(oracle.OracleError):  # 48 is not a multiple of 10
+        oracle.spectre_mix_chunked(q, q, q, q, np.ones((1, 6), np.float32),
+                                   np.ones((1, 3), np.float32), ones, zeros, 10, 6, 3)
+    with pytest.raises(oracle.OracleError):  # keep_blocks above nb/2 + 1
+        oracle.spectre_mix_chunked(q, q, q, q, np.ones((1, 7), np.float32),
+                                   np.ones((1, 3), np.float32), ones, zeros, 12, 7, 4)
