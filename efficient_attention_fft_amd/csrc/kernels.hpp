@@ -457,6 +457,12 @@ struct MidParams {
   int rad[8];            // Stockham radices, product N
   float scale;           // 1 / (8 L^2): the mix's 1/L, the inverse's 1/L, the (1/2)^3 of the split
   int gx, gy, gz;        // k_mid_dma: the work items (column pairs, channel-pair blocks, batch)
+  // chunked mix: bin 0 of column (0, 0) -- the column sums of each block --
+  // times dc_scale = 1 / L goes to dc[x * dc_stride + b * CP2 + pair] (the
+  // block means of q, k, v); null otherwise
+  float2* dc;
+  int64_t dc_stride;
+  float dc_scale;
 };
 
 // One Stockham autosort pass of radix R over the LDS-resident columns.
@@ -640,6 +646,8 @@ __global__ __launch_bounds__(512) void k_mid(MidParams p) {
     }
     __syncthreads();  // LDS free: the previous tensor's product step is done
     fft_columns<P, -1>(v, lds, p, tc, col, ncols);
+    if (p.dc != nullptr && my_col == 0 && tc == 0)  // bin 0 of column (0, 0)
+      p.dc[x * p.dc_stride + (int64_t)b * p.CP2 + cp] = cscale(v[0], p.dc_scale);
 #pragma unroll
     for (int i = 0; i < P; ++i) lds[(tc + p.Tc * i) * ncols + col] = v[i];
     __syncthreads();
@@ -847,6 +855,8 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 #pragma unroll
     for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * ncols + col2];
     dft<R, -1>(v);
+    if (p.dc != nullptr && special)  // bin 0 of column (0, 0)
+      p.dc[x * p.dc_stride + (int64_t)b * p.CP2 + cp2] = cscale(v[0], p.dc_scale);
 
     // ---- split the packed spectra and accumulate / finish the product.
     // The mirror bin of this lane's k2 = u < R/2 is the partner lane's
@@ -1120,6 +1130,8 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
         copy_block(p.in[x + 1], blk, cols);
       }
       dft<R, -1>(v);
+      if (p.dc != nullptr && special)  // bin 0 of column (0, 0)
+        p.dc[x * p.dc_stride + (int64_t)blk.z * p.CP2 + blk.y * 4 + j2] = cscale(v[0], p.dc_scale);
 
       // ---- split the packed spectra and accumulate / finish the product
       // (the same arithmetic as k_mid_sq)
@@ -1294,6 +1306,7 @@ struct FinalParams {
   int64_t lines;  // B * M * CP2
   float inv_c;
   float eps;
+  const float2* yblk;  // chunked mix: [B][CP2] term added to every token of batch (block) b, or null
 };
 
 template <int R, int DT, bool FUSE, bool PRE = false>
@@ -1313,6 +1326,11 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
 #pragma unroll
   for (int r = 0; r < R; ++r) z[r] = load_nt(p.U + ubase + (int64_t)r * p.M * p.CP2);
   dft<R, +1>(z);
+  if (p.yblk != nullptr) {  // chunked mix: the block term, the same for the R tokens
+    const float2 yb = p.yblk[b * p.CP2 + cp];
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[r] = cadd(z[r], yb);
+  }
 
   // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
   const int64_t obase = (b * p.L + m) * p.CP2 + cp;
@@ -1397,7 +1415,7 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
 // waves per CU.  Token sums: recursive halving over the 32 lanes of a half
 // (lane c ends with the half-wave total of slot c), then the waves' totals
 // meet in LDS.  Needs CP2 % 32 == 0 and CP2 <= 256.
-template <int R, int DT, bool PRE = false>
+template <int R, int DT, bool PRE = false, bool BLK = false>
 __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   constexpr int R2 = R / 2;
   constexpr int T2 = next_pow2(R2);  // 32: token slots per half
@@ -1421,6 +1439,11 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   }
   dft<R2, +1>(z);
   join_swap<R, +1>(z, h);
+  if constexpr (BLK) {  // chunked mix: the block term, the same for every token here
+    const float2 yb = p.yblk[b * p.CP2 + cp];
+#pragma unroll
+    for (int a = 0; a < R2; ++a) z[a] = cadd(z[a], yb);
+  }
   // slot j of half h holds token n1 = tok(j) (join_swap's output order);
   // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
   constexpr int Q = R / 4;
@@ -1497,6 +1520,8 @@ struct NormParams {
   void* out;
   int64_t ntok, CP2;
   float inv_c, eps;
+  const float2* yblk;  // chunked mix: [ntok / Lb][CP2] block term added to y, or null
+  int64_t Lb;          // tokens per block
 };
 
 template <int DT, bool PRE = false>
@@ -1513,6 +1538,7 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
     const int64_t c = lane + 64 * it;
     if (c < p.CP2) {
       z[it] = load_nt(p.y + base + c);
+      if (p.yblk != nullptr) z[it] = cadd(z[it], p.yblk[(tok / p.Lb) * p.CP2 + c]);
       if constexpr (!PRE) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
@@ -1538,6 +1564,14 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
       store_pair<DT>(p.out, base + c, o);
     }
   }
+}
+
+// Chunked mix, y only, single-level blocks: y[b][t][pair] += yblk[b][pair]
+// over nb blocks of Lb tokens (b = the block).
+__global__ __launch_bounds__(256) void k_block_add(float2* y, const float2* yblk, int64_t n,
+                                                   int64_t Lb, int64_t CP2) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    y[i] = cadd(y[i], yblk[(i / (Lb * CP2)) * CP2 + i % CP2]);
 }
 
 }  // namespace spectre

@@ -345,6 +345,15 @@ struct Shape {
   int norm_order;  // spectre_norm_order
 };
 
+// Chunked mix (blocks of L tokens of the blockwise shape, nb per batch
+// element): the block-axis step's gate and kept bins.
+struct Chunk {
+  const float* gate_blocks;  // [H][nb/2 + 1]
+  int64_t nb;                // blocks per batch element
+  int64_t keep_blocks;
+  int64_t B;                 // batch elements (the blockwise shape has B * nb)
+};
+
 int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, Shape& s,
                 Plan& pl, int gate_kind = SPECTRE_GATE_REAL, int norm_order = SPECTRE_NORM_POST) {
   if (B < 1 || H < 1 || D < 1 || L < 2) return SPECTRE_EINVAL;
@@ -413,6 +422,13 @@ size_t gate_table_bytes(const Shape& s, const Plan& pl) {
 size_t workspace_for(const Shape& s, const Plan& pl, bool want_fwd) {
   const size_t a = (spectra_bytes(s, pl, want_fwd) + 255) & ~(size_t)255;
   return a + gate_table_bytes(s, pl);
+}
+
+// Extra workspace of a chunked mix, after the rest (256-byte aligned): the
+// block means of q, k, v and the block term, 4 x B x CP2 pairs of the
+// blockwise shape (one row of pairs per block).
+size_t chunk_bytes(const Shape& s, const Chunk* ch) {
+  return ch ? 256 + 4 * (size_t)s.B * s.CP2 * sizeof(float2) : 0;
 }
 
 // ------------------------------------------------------------ launching
@@ -617,7 +633,9 @@ int launch_final_r(const FinalParams& p, bool fuse, bool pre, int64_t B, hipStre
   if constexpr (R == 48 || R == 64) {
     if (fuse && p.CP2 % 32 == 0) {  // CP2 <= 256 holds whenever fuse does
       const dim3 grid((unsigned)(B * p.M)), block((unsigned)(2 * p.CP2));
-      if (pre)
+      if (p.yblk != nullptr)  // chunked mix (post-norm only)
+        hipLaunchKernelGGL((k_final_split<R, DT, false, true>), grid, block, 0, st, p);
+      else if (pre)
         hipLaunchKernelGGL((k_final_split<R, DT, true>), grid, block, 0, st, p);
       else
         hipLaunchKernelGGL((k_final_split<R, DT, false>), grid, block, 0, st, p);
@@ -673,11 +691,90 @@ int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
   return SPECTRE_OK;
 }
 
+// B, the LDS pass, for shape s / plan pl: the column transforms, the
+// spectral product and the inverse.  in[] are the raw tensors (single level,
+// in_kind their storage) or the spectra (IN_C32); out gets y (single level)
+// or U; gtab is the gate table of a multi-level square kernel, else null;
+// dc (chunked mix) receives the block means.
+int launch_b(const Shape& s, const Plan& pl, const LenTables* tab, const void* const in[3],
+             int in_kind, float2* out, const float* gate, const float* gtab, int tiled,
+             float2* dc, hipStream_t st) {
+  const bool single = is_single(pl);
+  const int64_t CP2 = s.CP2;
+  MidParams m{};
+  const int nslot = single ? 1 : 2;
+  const int cpt = pl.sq ? choose_cpt_sq(pl.sq, CP2, nslot) : choose_cpt(pl, CP2, nslot);
+  for (int t = 0; t < 3; ++t) m.in[t] = in[t];
+  m.out = out;
+  m.tiled = tiled;
+  m.gate = gate;
+  m.gate_kind = s.gate_kind;
+  m.gtab = gtab;
+  m.ncol = (int)(pl.L1 * pl.L2);
+  m.twN = tab->twN;
+  m.twL = tab->twL;
+  m.wgcols = tab->wgcols;
+  m.L = (int)s.L;
+  m.L1 = (int)pl.L1;
+  m.L2 = (int)pl.L2;
+  m.N = (int)pl.L3;
+  m.M = (int)(pl.L2 * pl.L3);
+  m.CP2 = (int)CP2;
+  m.D = (int)s.D;
+  m.keep = (int)s.keep;
+  m.nbins = (int)(s.L / 2 + 1);
+  m.nslot = nslot;
+  m.cpt = cpt;
+  m.Tc = pl.Tc;
+  m.selfwg = tab->selfwg;
+  m.nrad = pl.nrad;
+  for (int i = 0; i < 8; ++i) m.rad[i] = pl.rad[i];
+  m.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
+  m.dc = dc;
+  m.dc_stride = s.B * CP2;
+  m.dc_scale = (float)(1.0 / (double)s.L);
+  dim3 grid((unsigned)tab->nwg, (unsigned)(CP2 / cpt), (unsigned)s.B);
+  const int threads = pl.Tc * nslot * cpt;
+  if (pl.sq) {
+    if (in_kind == IN_F32) return launch_mid_square<IN_F32>(pl.sq, m, grid, st);
+    if (in_kind == IN_BF16) return launch_mid_square<IN_BF16>(pl.sq, m, grid, st);
+    return launch_mid_square<IN_C32>(pl.sq, m, grid, st);
+  }
+  if (in_kind == IN_F32) return launch_mid<IN_F32>(pl.P, m, grid, threads, st);
+  if (in_kind == IN_BF16) return launch_mid<IN_BF16>(pl.P, m, grid, threads, st);
+  return launch_mid<IN_C32>(pl.P, m, grid, threads, st);
+}
+
+// The chunked mix's inter-block step: the block means dc ([3][B][nb][pairs],
+// binary32) mixed over the block axis -- a single-level mix of length nb
+// with gate_blocks -- into yblk ([B][nb][pairs]).
+int launch_block_mix(int dev, const Shape& s, const Chunk& ch, const float2* dc, float2* yblk,
+                     hipStream_t st) {
+  Shape sb = s;
+  sb.B = ch.B;
+  sb.L = ch.nb;
+  sb.N = ch.B * ch.nb * s.C;
+  sb.keep = ch.keep_blocks;
+  sb.dtype = SPECTRE_F32;
+  sb.esz = 4;
+  sb.gate_kind = SPECTRE_GATE_REAL;
+  Plan pb;
+  int rc = make_plan(ch.nb, pb);
+  if (rc) return rc;
+  if (!is_single(pb)) return SPECTRE_EUNSUPPORTED;
+  LenTables* tb = nullptr;
+  rc = get_tables(dev, pb, &tb);
+  if (rc) return rc;
+  const int64_t per = ch.B * ch.nb * s.CP2;  // pairs per tensor of block means
+  const void* ins[3] = {dc, dc + per, dc + 2 * per};
+  return launch_b(sb, pb, tb, ins, IN_F32, yblk, ch.gate_blocks, nullptr, 0, nullptr, st);
+}
+
 // The spectral part into `y` (pairs, binary32), and optionally the fused
 // residual + LayerNorm into `out`.
 int run(const void* q, const void* k, const void* v, const void* x, const float* gate,
         const float* gamma, const float* beta, void* out, float* y, const Shape& s,
-        const Plan& pl, hipStream_t st) {
+        const Plan& pl, hipStream_t st, const Chunk* chunk = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
   std::lock_guard<std::mutex> lock(g_mu);
@@ -686,11 +783,16 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   if (rc) return rc;
   const bool want_out = out != nullptr;
   void* ws = nullptr;
-  const size_t wsb = workspace_for(s, pl, want_out);
+  const size_t wsb = workspace_for(s, pl, want_out) + chunk_bytes(s, chunk);
   if (wsb) {
     rc = get_workspace(dev, wsb, &ws);
     if (rc) return rc;
   }
+  // chunked mix: the block means of q, k, v and the block term, after the rest
+  float2* dc = chunk ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
+                                                 ((workspace_for(s, pl, want_out) + 255) & ~(size_t)255))
+                     : nullptr;
+  float2* yblk = chunk ? dc + 3 * s.B * s.CP2 : nullptr;
   trace_call_begin(st);
   const int64_t CP2 = s.CP2;
   const int64_t pairs = s.B * s.L * CP2;  // complex elements per tensor
@@ -757,60 +859,28 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
 
   // ---- B: LDS transform, spectral product, inverse
   {
-    MidParams m{};
-    const int nslot = single ? 1 : 2;
-    const int cpt = pl.sq ? choose_cpt_sq(pl.sq, CP2, nslot) : choose_cpt(pl, CP2, nslot);
-    if (single) {
-      m.in[0] = q;
-      m.in[1] = k;
-      m.in[2] = v;
-      m.out = want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y);
-    } else {
-      for (int t = 0; t < 3; ++t) m.in[t] = S + t * pairs;
-      m.out = U;  // row layout: q's spectrum in place, workgroup by workgroup, unless tiled
-      m.tiled = tiled || tiled3 ? 1 : 0;
-    }
-    m.gate = gate;
-    m.gate_kind = s.gate_kind;
-    m.gtab = g.gtab;
-    m.ncol = (int)(pl.L1 * pl.L2);
-    m.twN = tab->twN;
-    m.twL = tab->twL;
-    m.wgcols = tab->wgcols;
-    m.L = (int)s.L;
-    m.L1 = (int)pl.L1;
-    m.L2 = (int)pl.L2;
-    m.N = (int)pl.L3;
-    m.M = (int)(pl.L2 * pl.L3);
-    m.CP2 = (int)CP2;
-    m.D = (int)s.D;
-    m.keep = (int)s.keep;
-    m.nbins = (int)(s.L / 2 + 1);
-    m.nslot = nslot;
-    m.cpt = cpt;
-    m.Tc = pl.Tc;
-    m.selfwg = tab->selfwg;
-    m.nrad = pl.nrad;
-    for (int i = 0; i < 8; ++i) m.rad[i] = pl.rad[i];
-    m.scale = (float)(1.0 / (8.0 * (double)s.L * (double)s.L));
-    dim3 grid((unsigned)tab->nwg, (unsigned)(CP2 / cpt), (unsigned)s.B);
-    const int threads = pl.Tc * nslot * cpt;
-    const int kind = single ? in_kind : IN_C32;
-    if (pl.sq) {
-      if (kind == IN_F32)
-        rc = launch_mid_square<IN_F32>(pl.sq, m, grid, st);
-      else if (kind == IN_BF16)
-        rc = launch_mid_square<IN_BF16>(pl.sq, m, grid, st);
-      else
-        rc = launch_mid_square<IN_C32>(pl.sq, m, grid, st);
-    } else if (kind == IN_F32) {
-      rc = launch_mid<IN_F32>(pl.P, m, grid, threads, st);
-    } else if (kind == IN_BF16) {
-      rc = launch_mid<IN_BF16>(pl.P, m, grid, threads, st);
-    } else {
-      rc = launch_mid<IN_C32>(pl.P, m, grid, threads, st);
-    }
+    const void* ins[3] = {q, k, v};
+    if (!single)
+      for (int t = 0; t < 3; ++t) ins[t] = S + t * pairs;
+    float2* bout = single ? (want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y))
+                          : U;  // row layout: q's spectrum in place, unless tiled
+    rc = launch_b(s, pl, tab, ins, single ? in_kind : IN_C32, bout, gate, g.gtab,
+                  tiled || tiled3 ? 1 : 0, chunk ? dc : nullptr, st);
     if (rc) return rc;
+  }
+
+  // ---- chunked mix: the block means, mixed over the block axis, into yblk
+  if (chunk) {
+    rc = launch_block_mix(dev, s, *chunk, dc, yblk, st);
+    if (rc) return rc;
+    if (single && !want_out) {  // y only, written by B: add the block term here
+      const int64_t n = s.B * s.L * CP2;
+      const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
+      hipLaunchKernelGGL(k_block_add, dim3((unsigned)blocks), dim3(256), 0, st,
+                         reinterpret_cast<float2*>(y), yblk, n, s.L, CP2);
+      SPECTRE_LAUNCH_CHECK("block_add");
+      return SPECTRE_OK;
+    }
   }
 
   const float inv_c = (float)(1.0 / (double)s.C);
@@ -828,6 +898,8 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     n.CP2 = CP2;
     n.inv_c = inv_c;
     n.eps = eps;
+    n.yblk = yblk;  // chunked mix: the block term joins y here
+    n.Lb = s.L;
     return launch_norm(n, s.dtype, pre, st);
   }
 
@@ -856,6 +928,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   f.lines = s.B * f.M * CP2;
   f.inv_c = inv_c;
   f.eps = eps;
+  f.yblk = yblk;  // chunked mix: the block term joins y in C1
   // y for a separate LayerNorm: k's spectrum region is free once B has run
   float* ybuf = want_out ? reinterpret_cast<float*>(T + pairs) : y;
   if (fuse) {
@@ -877,6 +950,27 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   n.inv_c = inv_c;
   n.eps = eps;
   return launch_norm(n, s.dtype, pre, st);
+}
+
+// Validates a chunked call: the blockwise shape (B * nb batches of fft_len
+// tokens) and the block axis (nb = L / fft_len, even, one-level plan).
+int check_chunked(int64_t B, int64_t H, int64_t L, int64_t D, int64_t fft_len, int64_t keep_bins,
+                  int64_t keep_blocks, int dtype, Shape& s, Plan& pl, Chunk& ch) {
+  if (B < 1 || L < 2 || fft_len < 2) return SPECTRE_EINVAL;
+  if (L % fft_len != 0) return SPECTRE_EINVAL;
+  const int64_t nb = L / fft_len;
+  if (nb % 2 != 0 || keep_blocks < 0 || keep_blocks > nb / 2 + 1) return SPECTRE_EINVAL;
+  if (B > (int64_t(1) << 40) / L) return SPECTRE_EUNSUPPORTED;
+  int rc = check_shape(B * nb, H, fft_len, D, keep_bins, dtype, s, pl);
+  if (rc) return rc;
+  Plan pb;
+  rc = make_plan(nb, pb);
+  if (rc) return rc;
+  if (!is_single(pb)) return SPECTRE_EUNSUPPORTED;
+  ch.nb = nb;
+  ch.keep_blocks = keep_blocks;
+  ch.B = B;
+  return SPECTRE_OK;
 }
 
 }  // namespace
@@ -933,6 +1027,48 @@ int spectre_mix_y(const void* q, const void* k, const void* v, const float* gate
                   hipStream_t stream) {
   return spectre_mix_y_ex(q, k, v, gate, y, B, H, L, D, keep_bins, dtype, SPECTRE_GATE_REAL,
                           stream);
+}
+
+int spectre_mix_fwd_chunked(const void* q, const void* k, const void* v, const void* x,
+                            const float* gate, const float* gate_blocks, const float* gamma,
+                            const float* beta, void* out, int64_t B, int64_t H, int64_t L, int64_t D,
+                            int64_t fft_len, int64_t keep_bins, int64_t keep_blocks, int dtype,
+                            hipStream_t stream) {
+  if (!q || !k || !v || !x || !gate || !gate_blocks || !gamma || !beta || !out)
+    return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  Chunk ch{};
+  int rc = check_chunked(B, H, L, D, fft_len, keep_bins, keep_blocks, dtype, s, pl, ch);
+  if (rc) return rc;
+  ch.gate_blocks = gate_blocks;
+  const void* ptrs[] = {q, k, v, x, gate, gate_blocks, gamma, beta, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v, x})
+    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
+  return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream, &ch);
+}
+
+int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const float* gate,
+                          const float* gate_blocks, float* y, int64_t B, int64_t H, int64_t L,
+                          int64_t D, int64_t fft_len, int64_t keep_bins, int64_t keep_blocks,
+                          int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !gate || !gate_blocks || !y) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  Chunk ch{};
+  int rc = check_chunked(B, H, L, D, fft_len, keep_bins, keep_blocks, dtype, s, pl, ch);
+  if (rc) return rc;
+  ch.gate_blocks = gate_blocks;
+  const void* ptrs[] = {q, k, v, gate, gate_blocks, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v})
+    if (overlaps(y, (size_t)s.N * 4, p, tb)) return SPECTRE_EINVAL;
+  return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream, &ch);
 }
 
 size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D, int dtype,

@@ -146,6 +146,37 @@ int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* g
                      int gate_kind, hipStream_t stream);
 
 /*
+ * Chunked (blockwise) mix, for fft_len below L (the article's section 3.2:
+ * an FFT inside fixed-size blocks, e.g. 4096 tokens, then one more
+ * low-frequency interaction between the blocks, whose form the article
+ * leaves open).  This library's reading:
+ *   - each of the nb = L / fft_len blocks of fft_len tokens is mixed on its
+ *     own: y_blk = the mix of the top of this file with length fft_len, gate
+ *     [H][fft_len/2+1] and keep_bins <= fft_len/2 + 1;
+ *   - the block means of q, k, v (nb values per column) are mixed by the same
+ *     operation over the block axis: gate_blocks [H][nb/2+1] f32,
+ *     keep_blocks <= nb/2 + 1; the result is added to every token of its
+ *     block;
+ *   - then out = LayerNorm(x + y) as for spectre_mix_fwd.
+ * Shapes: fft_len a supported length (see above), L a multiple of it, nb
+ * even with nb = 2^a * 3^b <= 2048 (else SPECTRE_EINVAL / EUNSUPPORTED).
+ * Everything else (layouts, ownership, stream, errors) as spectre_mix_fwd.
+ * The block means are the transform's bin 0 of each block, taken from the
+ * forward pass; the block-axis mix runs between the transform and the norm.
+ */
+int spectre_mix_fwd_chunked(const void* q, const void* k, const void* v, const void* x,
+                            const float* gate, const float* gate_blocks, const float* gamma,
+                            const float* beta, void* out, int64_t B, int64_t H, int64_t L,
+                            int64_t D, int64_t fft_len, int64_t keep_bins, int64_t keep_blocks,
+                            int dtype, hipStream_t stream);
+
+/* y of the chunked mix (binary32 [B, L, H, D]), the test hook's counterpart. */
+int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const float* gate,
+                          const float* gate_blocks, float* y, int64_t B, int64_t H, int64_t L,
+                          int64_t D, int64_t fft_len, int64_t keep_bins, int64_t keep_blocks,
+                          int dtype, hipStream_t stream);
+
+/*
  * Device workspace bytes a spectre_mix_fwd call of this shape uses (0 if the
  * shape is invalid or unsupported).  Pure host arithmetic; no device call.
  */

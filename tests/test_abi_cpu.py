@@ -98,6 +98,25 @@ def test_fwd_ex_checks_shapes_like_fwd():
     assert fwd_ex(2, 1, q=GOOD + 8) == sm.SPECTRE_EINVAL
 
 
+def test_chunked_rejects_before_device():
+    args = dict(B=1, H=8, L=65536, D=64, F=4096, keep=2049, keepb=9)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return sm.spectre_mix_fwd_chunked(GOOD, GOOD + 0x1000000, GOOD + 0x2000000,
+                                          GOOD + 0x3000000, GOOD + 0x4000000, GOOD + 0x4100000,
+                                          GOOD + 0x5000000, GOOD + 0x6000000, GOOD + 0x70000000,
+                                          a["B"], a["H"], a["L"], a["D"], a["F"], a["keep"],
+                                          a["keepb"], 0, 0)
+    assert call(F=3000) == sm.SPECTRE_EINVAL            # L not a multiple of fft_len
+    assert call(L=3 * 4096) == sm.SPECTRE_EINVAL        # odd block count
+    assert call(keepb=10) == sm.SPECTRE_EINVAL          # keep_blocks above nb/2 + 1
+    assert call(keep=2050) == sm.SPECTRE_EINVAL         # keep_bins above fft_len/2 + 1
+    assert call(F=2, L=16384, keep=2, keepb=1) == sm.SPECTRE_EUNSUPPORTED  # nb = 8192: too long
+    assert call(F=5 * 1024, L=10 * 1024, keepb=1) == sm.SPECTRE_EUNSUPPORTED  # fft_len: factor 5
+
+
 def test_y_rejects_before_device():
     assert sm.spectre_mix_y(0, GOOD, GOOD, GOOD, GOOD, 1, 8, 4096, 64, 2049, 0, 0) == \
         sm.SPECTRE_EINVAL

@@ -232,6 +232,17 @@ def make_gate(w: Workload, gate_kind: int) -> np.ndarray:
     return np.ascontiguousarray(g, dtype=np.float32)
 
 
+_GATE_BLOCK_SEED, _GATE_BLOCKS_SEED = 54, 55
+
+
+def make_chunk_gates(w: Workload, fft_len: int):
+    """Gates of the chunked mix: the in-block gate [H, fft_len//2 + 1] and the
+    block-axis gate [H, nb//2 + 1] (nb = L // fft_len), both ~ U[0, 1)."""
+    nb = w.L // fft_len
+    return (uniform(w.seed(_GATE_BLOCK_SEED), (w.H, fft_len // 2 + 1)),
+            uniform(w.seed(_GATE_BLOCKS_SEED), (w.H, nb // 2 + 1)))
+
+
 def sample_tokens(w: Workload, count: int, seed: int = 99) -> np.ndarray:
     """Flat token ids b*L + t to check at full size: the first and last token,
     the tokens on either side of each batch boundary, and a seeded spread."""
