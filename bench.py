@@ -32,6 +32,7 @@ Other modes (used to produce the files under profiles/):
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import glob
 import hashlib
 import json
@@ -123,6 +124,19 @@ def cpu_baseline(w, inp, gate_kind=0, norm_order=0):
             "float64, %.2f s wall" % (w.B * w.C, w.L, dt)}
 
 
+def cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.spectre_mix_chunked(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], gate_blocks,
+                               inp["gamma"], inp["beta"], F, keep_blk, keep_axis, dtype=w.dtype,
+                               nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+            "kind": "oracle", "sample": "the whole workload once, chunked (fft_len %d): %d "
+            "columns x %d tokens, float64, %.2f s wall" % (F, w.B * w.C, w.L, dt)}
+
+
 def traffic_for(kernel: str, w):
     """HBM bytes per launch of `kernel` from the committed counters, or None."""
     try:
@@ -151,6 +165,10 @@ def run_bench(args):
     gk, no = args.gate_kind, args.norm_order
     if gk != 0:
         inp["gate"] = workloads.make_gate(w, gk)
+    F = args.fft_len
+    if F:  # chunked mix: blocks of F tokens, every bin kept in both steps
+        inp["gate"], gate_blocks = workloads.make_chunk_gates(w, F)
+        keep_blk, keep_axis = F // 2 + 1, (w.L // F) // 2 + 1
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -162,7 +180,13 @@ def run_bench(args):
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
 
+    if F:
+        gbd = dev(gate_blocks)
+
     def step():
+        if F:
+            return sm.spectre_mix_fwd_chunked(q, k, v, x, gate, gbd, gamma, beta, out, w.B, w.H,
+                                              w.L, w.D, F, keep_blk, keep_axis, w.dtype, stream)
         if gk == 0 and no == 0:
             return sm.spectre_mix_fwd(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
                                       w.keep_bins, w.dtype, stream)
@@ -202,10 +226,12 @@ def run_bench(args):
           file=sys.stderr, flush=True)
     dom = max(per_kernel, key=per_kernel.get)
     nl = launches[dom]
-    dom_bytes = kernel_bytes(dom, w, gk) / nl  # per launch
+    # the chunked mix transforms blocks of F tokens: the passes follow that plan
+    wk = w if not F else dataclasses.replace(w, B=w.B * (w.L // F), L=F, keep_bins=F // 2 + 1)
+    dom_bytes = kernel_bytes(dom, wk, gk) / nl  # per launch
     avg_ms = per_kernel[dom] / nl
     achieved = dom_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = traffic_for(dom, w) if gk == 0 and no == 0 else None
+    traffic = traffic_for(dom, w) if gk == 0 and no == 0 and not F else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
@@ -240,13 +266,15 @@ def run_bench(args):
         "data": "synthetic",
         "config": dict(w.describe(), parallelism="single GPU",
                        **({"gate_kind": ["real", "logit", "complex"][gk],
-                           "norm": ["post", "pre"][no]} if (gk or no) else {})),
+                           "norm": ["post", "pre"][no]} if (gk or no) else {}),
+                       **({"fft_len": F} if F else {})),
         "roofline": roofline,
         "whole_call": whole,
     }
     if not args.profile_run and not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, inp, gk, no)
+        res["cpu_baseline"] = (cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis)
+                               if F else cpu_baseline(w, inp, gk, no))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
@@ -375,6 +403,8 @@ def main():
                     help="0 real gate, 1 logit gate (sigmoid in the kernels), 2 complex gate")
     ap.add_argument("--norm-order", type=int, default=0, choices=[0, 1],
                     help="0 out = LN(x + y), 1 out = x + LN(y)")
+    ap.add_argument("--fft-len", type=int, default=0,
+                    help="chunked mix with blocks of this many tokens (0: one block, the plain mix)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))

@@ -212,6 +212,14 @@ void trace_kernel(const char* name) {
   c.names[c.nk++] = name;
 }
 
+// Renames the current call's last traced kernel (a pass launched through a
+// shared launcher for another role).
+void trace_rename_last(const char* name) {
+  if (!g_trace.active) return;
+  TraceCall& c = g_trace.calls.back();
+  if (c.nk > 0) c.names[c.nk - 1] = name;
+}
+
 // exp(-2 pi i e / n) in double, angle split exactly into a quarter turn and
 // a residual of at most pi/4, then rounded to binary32.
 float2 host_twiddle(int64_t e, int64_t n) {
@@ -873,6 +881,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   if (chunk) {
     rc = launch_block_mix(dev, s, *chunk, dc, yblk, st);
     if (rc) return rc;
+    trace_rename_last("B_block_axis");
     if (single && !want_out) {  // y only, written by B: add the block term here
       const int64_t n = s.B * s.L * CP2;
       const int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
