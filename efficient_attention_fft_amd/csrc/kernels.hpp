@@ -375,19 +375,14 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     e[a] = load_pair_u<IN>(in, (uint32_t)0);
     in += 2 * step * pair_bytes<IN>();
   }
-  // twiddle w^k1 for output k1 = k + R2 h, w = w_L^i (A1) or w_L^(i L1) (A2).
-  // Binary32 inputs: seeds w^(R2 h + j), j < 4, times (w^4)^(k / 4), 5 table
-  // loads per lane.  Bfloat16 inputs: one table load per output, which
-  // measured faster there (the stores then leave at the pace of the loads).
+  // twiddle w^k1 for output k1 = k + R2 h, w = w_L^i (A1) or w_L^(i L1) (A2):
+  // seeds w^(R2 h + j), j < 4, times (w^4)^(k / 4), 5 table loads per lane.
   const int tw_i = TW == TW_A2 ? i * p.L1 : i;
   dft<R2, -1>(e);
-  constexpr bool SEEDS = IN != IN_BF16;
-  float2 tws[4], tw4 = make_float2(1.f, 0.f);
-  if constexpr (SEEDS) {
+  float2 tws[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tws[j] = p.twL[tw_i * (R2 * h + j)];
-    tw4 = p.twL[4 * tw_i];
-  }
+  for (int j = 0; j < 4; ++j) tws[j] = p.twL[tw_i * (R2 * h + j)];
+  const float2 tw4 = p.twL[4 * tw_i];
   float2 stp = make_float2(1.f, 0.f);
   auto output = [&](int k) __attribute__((always_inline)) {
     const float2 mine = e[k];
@@ -395,12 +390,8 @@ __global__ __launch_bounds__(256) void k_strided_split(StridedParams p) {
     const float2 e0 = h ? other : mine;
     const float2 e1 = twiddle_ct<R, -1>(h ? mine : other, k);
     float2 xk = h ? csub(e0, e1) : cadd(e0, e1);
-    if constexpr (SEEDS) {
-      xk = cmul(xk, cmul(tws[k & 3], stp));
-      if ((k & 3) == 3) stp = cmul(stp, tw4);
-    } else {
-      xk = cmul(xk, twiddle_lookup(p.twL, tw_i * (k + R2 * h), false));
-    }
+    xk = cmul(xk, cmul(tws[k & 3], stp));
+    if ((k & 3) == 3) stp = cmul(stp, tw4);
     return xk;
   };
   if constexpr (TILED) {
