@@ -981,7 +981,10 @@ __device__ __forceinline__ void wait_vmcnt_32() {
   __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | 0x0F70);  // vmcnt(32)
 }
 
-template <bool CG>  // CG: complex gate, read from the table in the product (no LDS copy)
+// CG: complex gate, read from the table in the product (no LDS copy).
+// UK: the product runs over k2 = u < UK only (UK = 17: all); the host takes
+// UK from the truncation, so that every bin at u >= UK is truncated.
+template <bool CG, int UK = 17>
 __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
   constexpr int R = 32, N = R * R, H2 = R / 2, NT = 256, ROW = R * 8 + 1;
   constexpr int kSlot = 4 * N + 16;          // float2 between the slots' blocks
@@ -1131,40 +1134,46 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
         const float2 pulled = lane_pull2(v[R - 1 - u], partner_byte);
         return special ? v[(R - u) % R] : pulled;
       };
-      if (x == 0) {
+      {
+        if (x == 0) {
 #pragma unroll
-        for (int u = 0; u <= H2; ++u) {
-          const float2 z = v[u], zm = mirror(u);
-          sa[u] = make_float2(z.x + zm.x, z.y - zm.y);
-          sb[u] = make_float2(z.y + zm.y, zm.x - z.x);
-        }
-      } else if (x == 1) {
-#pragma unroll
-        for (int u = 0; u <= H2; ++u) {
-          const float2 z = v[u], zm = mirror(u);
-          sa[u] = cmulc(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
-          sb[u] = cmulc(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u <= H2; ++u) {
-          const float2 z = v[u], zm = mirror(u);
-          const float2 pa = cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
-          const float2 pb = cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
-          float2 oa, ob;
-          if constexpr (CG) {
-            const int c2 = s2 == 0 ? cols.x : cols.y;
-            const float2 g = reinterpret_cast<const float2*>(p.gtab)
-                [((int64_t)((2 * blk.y * 4) / p.D) * p.ncol + (c2 >= 0 ? c2 : 0)) * N + k1 + R * u];
-            oa = cmul(pa, g);
-            ob = cmul(pb, g);
-          } else {
-            const float g = gl[(s2 * (H2 + 1) + u) * R + k1];
-            oa = cscale(pa, g);
-            ob = cscale(pb, g);
+          for (int u = 0; u < UK; ++u) {
+            const float2 z = v[u], zm = mirror(u);
+            sa[u] = make_float2(z.x + zm.x, z.y - zm.y);
+            sb[u] = make_float2(z.y + zm.y, zm.x - z.x);
           }
-          sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
-          sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
+        } else if (x == 1) {
+#pragma unroll
+          for (int u = 0; u < UK; ++u) {
+            const float2 z = v[u], zm = mirror(u);
+            sa[u] = cmulc(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+            sb[u] = cmulc(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u <= H2; ++u) {
+            if (u >= UK) {  // every bin from here on truncated
+              sa[u] = sb[u] = make_float2(0.f, 0.f);
+              continue;
+            }
+            const float2 z = v[u], zm = mirror(u);
+            const float2 pa = cmul(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
+            const float2 pb = cmul(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
+            float2 oa, ob;
+            if constexpr (CG) {
+              const int c2 = s2 == 0 ? cols.x : cols.y;
+              const float2 g = reinterpret_cast<const float2*>(p.gtab)
+                  [((int64_t)((2 * blk.y * 4) / p.D) * p.ncol + (c2 >= 0 ? c2 : 0)) * N + k1 + R * u];
+              oa = cmul(pa, g);
+              ob = cmul(pb, g);
+            } else {
+              const float g = gl[(s2 * (H2 + 1) + u) * R + k1];
+              oa = cscale(pa, g);
+              ob = cscale(pb, g);
+            }
+            sa[u] = make_float2(oa.x - ob.y, oa.y + ob.x);
+            sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
+          }
         }
       }
     }

@@ -553,12 +553,25 @@ int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
   // that copies its input blocks to LDS asynchronously
   if (IN == IN_C32 && p.gtab != nullptr && one_head && R == 32 && p.tiled && p.nslot == 2 &&
       p.cpt == 4) {
-    static bool dma_attr = false;  // guarded by g_mu
-    if (!dma_attr) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mid_dma<CG>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+    // the product's bound from the truncation: every bin f = column + S (k1 +
+    // 32 u) with u >= uk is truncated (f >= keep, and f stays below L - keep
+    // while u <= 16 unless keep is near L/2, which keeps every u)
+    const int64_t S = (int64_t)p.L1 * p.L2;
+    const int64_t fmax = (S - 1) + S * (31 + 32 * 16);
+    int uk = 17;
+    if (p.L - fmax >= p.keep) {
+      const int64_t need = (p.keep + 32 * S - 1) / (32 * S);
+      uk = need <= 5 ? 5 : need <= 9 ? 9 : 17;
+    }
+    const void* fn = uk == 5 ? reinterpret_cast<const void*>(&k_mid_dma<CG, 5>)
+                   : uk == 9 ? reinterpret_cast<const void*>(&k_mid_dma<CG, 9>)
+                             : reinterpret_cast<const void*>(&k_mid_dma<CG, 17>);
+    static bool dma_attr[3] = {false, false, false};  // guarded by g_mu
+    const int ai = uk == 5 ? 0 : uk == 9 ? 1 : 2;
+    if (!dma_attr[ai]) {
+      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
         return SPECTRE_EHIP;
-      dma_attr = true;
+      dma_attr[ai] = true;
     }
     MidParams q = p;
     q.gx = (int)grid.x;
@@ -586,7 +599,12 @@ int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
     }
     const size_t lds_dma = ((size_t)R * (R * ncols + 1) + (size_t)R * R) * sizeof(float2) +
                            (CG ? 0 : (size_t)p.nslot * (R / 2 + 1) * R * sizeof(float));
-    hipLaunchKernelGGL(k_mid_dma<CG>, dim3((unsigned)wgs), dim3(256), lds_dma, st, q);
+    if (uk == 5)
+      hipLaunchKernelGGL((k_mid_dma<CG, 5>), dim3((unsigned)wgs), dim3(256), lds_dma, st, q);
+    else if (uk == 9)
+      hipLaunchKernelGGL((k_mid_dma<CG, 9>), dim3((unsigned)wgs), dim3(256), lds_dma, st, q);
+    else
+      hipLaunchKernelGGL((k_mid_dma<CG, 17>), dim3((unsigned)wgs), dim3(256), lds_dma, st, q);
     SPECTRE_LAUNCH_CHECK("B_mid_lds");
     return SPECTRE_OK;
   }
