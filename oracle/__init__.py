@@ -63,6 +63,11 @@ def _bind(lib):
     lib.oracle_spectre_mix_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                                i64, i64, i64, i64, ci, vp, vp, ci]
     lib.oracle_spectre_mix_chunked.restype = ci
+    lib.oracle_local_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
+    lib.oracle_local_attention.restype = ci
+    lib.oracle_spectre_mix_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                             i64, i64, ci, vp, vp, ci]
+    lib.oracle_spectre_mix_local.restype = ci
     for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
               lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads,
               lib.oracle_spectre_y_ex, lib.oracle_layernorm_residual_ex,
@@ -232,4 +237,32 @@ def spectre_mix_chunked(q, k, v, x, gate, gate_blocks, gamma, beta, fft_len: int
                                               beta.ctypes.data, B, H, L, D, fft_len, keep_bins,
                                               keep_blocks, dtype, out.ctypes.data,
                                               y.ctypes.data if want_y else None, nthreads))
+    return (out, y) if want_y else out
+
+
+def local_attention(q, k, v, win_left: int, win_right: int, dtype: int = 0) -> np.ndarray:
+    """The sliding-window branch: per head, softmax((q . k) / sqrt(D)) over keys
+    t - win_left .. t + win_right inside the sequence, times v; [B, L, H, D] float64."""
+    B, L, H, D = q.shape
+    q, k, v = (_storage(t, dtype) for t in (q, k, v))
+    y = np.empty((B, L, H, D), np.float64)
+    _check(_load().oracle_local_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, L, D,
+                                          win_left, win_right, dtype, y.ctypes.data))
+    return y
+
+
+def spectre_mix_local(q, k, v, x, gate, gamma, beta, keep_bins: int, win_left: int,
+                      win_right: int, dtype: int = 0, nthreads: int = 0, want_y: bool = False):
+    """The mix with the local branch: out = LN(x + y + y_loc); y (if want_y) is
+    y + y_loc."""
+    B, L, H, D = q.shape
+    q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
+    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
+    out = np.empty((B, L, H, D), np.float64)
+    y = np.empty((B, L, H, D), np.float64) if want_y else None
+    _check(_load().oracle_spectre_mix_local(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                            x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
+                                            beta.ctypes.data, B, H, L, D, keep_bins, win_left,
+                                            win_right, dtype, out.ctypes.data,
+                                            y.ctypes.data if want_y else None, nthreads))
     return (out, y) if want_y else out

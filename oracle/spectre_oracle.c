@@ -62,6 +62,13 @@
  * (per column, nb values each) are mixed by the same operation over the
  * block axis (gate_blocks [H][nb/2 + 1], keep_blocks), and that result is
  * added to every token of its block; then the residual and the LayerNorm.
+ *
+ * Local branch (oracle_local_attention, oracle_spectre_mix_local; section
+ * 3.2's use_local_branch and section 4.3: a sliding-window attention branch
+ * beside the FFT branch, window 128 to 256, the two outputs added).
+ * Reading: for token t of head h, the keys j with t - win_left <= j <= t +
+ * win_right and 0 <= j < L; scores (q_t . k_j) / sqrt(D); softmax over those
+ * keys; y_loc[t] = sum_j p_j v_j.  out = LN(x + y + y_loc).
  */
 #include <math.h>
 #include <pthread.h>
@@ -692,6 +699,75 @@ int oracle_spectre_mix_chunked(const void *q, const void *k, const void *v, cons
   if (!y_out) free(y);
   free(means);
   free(y2);
+  return s;
+}
+
+/* The local branch alone: y_loc [B, L, H, D], double (see the header). */
+int oracle_local_attention(const void *q, const void *k, const void *v, int64_t B, int64_t H,
+                           int64_t L, int64_t D, int64_t win_left, int64_t win_right, int dtype,
+                           double *y) {
+  if (!q || !k || !v || !y) return ORACLE_EINVAL;
+  int s = check_dims(B, H, L, D, 0, dtype);
+  if (s) return s;
+  if (win_left < 0 || win_right < 0) return ORACLE_EINVAL;
+  const int64_t C = H * D;
+  const double scale = 1.0 / sqrt((double)D);
+  double *sc = (double *)malloc(sizeof(double) * (size_t)(win_left + win_right + 1));
+  if (!sc) return ORACLE_ENOMEM;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t j0 = t - win_left < 0 ? 0 : t - win_left;
+        const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;
+        const int64_t qb = (b * L + t) * C + h * D;
+        double mx = -INFINITY;
+        for (int64_t j = j0; j <= j1; ++j) {
+          const int64_t kb = (b * L + j) * C + h * D;
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d) dot += load_elem(q, dtype, qb + d) * load_elem(k, dtype, kb + d);
+          sc[j - j0] = dot * scale;
+          if (sc[j - j0] > mx) mx = sc[j - j0];
+        }
+        double sum = 0.0;
+        for (int64_t j = j0; j <= j1; ++j) {
+          sc[j - j0] = exp(sc[j - j0] - mx);
+          sum += sc[j - j0];
+        }
+        for (int64_t d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int64_t j = j0; j <= j1; ++j) acc += sc[j - j0] * load_elem(v, dtype, (b * L + j) * C + h * D + d);
+          y[qb + d] = acc / sum;
+        }
+      }
+  free(sc);
+  return ORACLE_OK;
+}
+
+/* The mix with the local branch: out = LN(x + y + y_loc), and optionally y + y_loc. */
+int oracle_spectre_mix_local(const void *q, const void *k, const void *v, const void *x,
+                             const float *gate, const float *gamma, const float *beta,
+                             int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
+                             int64_t win_left, int64_t win_right, int dtype, double *out,
+                             double *y_out, int nthreads) {
+  if (!x || !gamma || !beta || !out) return ORACLE_EINVAL;
+  int s = check_dims(B, H, L, D, keep, dtype);
+  if (s) return s;
+  const int64_t C = H * D, ntok = B * L;
+  double *y = y_out ? y_out : (double *)malloc(sizeof(double) * (size_t)(ntok * C));
+  double *yl = (double *)malloc(sizeof(double) * (size_t)(ntok * C));
+  if (!y || !yl) {
+    if (!y_out) free(y);
+    free(yl);
+    return ORACLE_ENOMEM;
+  }
+  s = oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, 0, y, nthreads);
+  if (s == ORACLE_OK) s = oracle_local_attention(q, k, v, B, H, L, D, win_left, win_right, dtype, yl);
+  if (s == ORACLE_OK) {
+    for (int64_t i = 0; i < ntok * C; ++i) y[i] += yl[i];
+    layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, 0, out);
+  }
+  if (!y_out) free(y);
+  free(yl);
   return s;
 }
 

@@ -34,6 +34,10 @@ MUTANTS = {
                          "means[((a * B + b) * nb + j) * C + c] = acc;"),
     "chunk_block_index": ("y2[(b * nb + t / F) * C + c]", "y2[(b * nb + (t / F + 1) % nb) * C + c]"),
     "chunk_block_gate": ("J.gate = gate_blocks;", "J.gate = gate;"),
+    "local_scale_dropped": ("const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0;"),
+    "local_window_right": ("const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;",
+                           "const int64_t j1 = t + win_right + 1 > L - 1 ? L - 1 : t + win_right + 1;"),
+    "local_not_normalised": ("y[qb + d] = acc / sum;", "y[qb + d] = acc;"),
     "inverse_scale_dropped": ("double re = bufq[t].re * invL, im = bufq[t].im * invL;",
                               "double re = bufq[t].re, im = bufq[t].im * invL;"),
     "truncation_inclusive": ("if (f < J->keep) {", "if (f <= J->keep) {"),
@@ -146,6 +150,12 @@ def _pins_pass() -> bool:
         ref = np.repeat(closed_form_y(*(c.astype(np.float64) for c in (cq, ck, cv)), gb, 5), F,
                         axis=1)
         if np.abs(y - ref).max() > 1e-10:
+            return False
+        # local branch against the softmax definition on a tiny case
+        from test_oracle_pins import _brute_window_attention
+        q, k, v = (rng.standard_normal((1, 12, 2, 4)).astype(np.float32) for _ in range(3))
+        ref = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), 3, 2)
+        if np.abs(oracle.local_attention(q, k, v, 3, 2) - ref).max() > 1e-10:
             return False
     except oracle.OracleError:
         return False

@@ -560,3 +560,61 @@ def test_chunked_rejects_bad_block_sizes():
     with pytest.raises(oracle.OracleError):  # keep_blocks above nb/2 + 1
         oracle.spectre_mix_chunked(q, q, q, q, np.ones((1, 7), np.float32),
                                    np.ones((1, 3), np.float32), ones, zeros, 12, 7, 4)
+
+
+# -------------------------------------------------------------- local branch
+#
+# Section 4.3's sliding-window attention beside the FFT branch.
+
+def _brute_window_attention(q, k, v, wl, wr):
+    """Softmax attention by its definition, one query at a time, every key in
+    the window t - wl .. t + wr inside the sequence."""
+    B, L, H, D = q.shape
+    y = np.zeros((B, L, H, D))
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                js = [j for j in range(L) if t - wl <= j <= t + wr]
+                s = np.array([np.dot(q[b, t, h], k[b, j, h]) for j in js]) / np.sqrt(D)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                y[b, t, h] = sum(wj * v[b, j, h] for wj, j in zip(w, js))
+    return y
+
+
+@pytest.mark.parametrize("L,wl,wr", [(1, 0, 0), (7, 2, 3), (16, 15, 0), (16, 4, 4), (9, 20, 20)])
+def test_local_attention_equals_definition(L, wl, wr):
+    B, H, D = 2, 2, 4
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    y = oracle.local_attention(q, k, v, wl, wr)
+    ref = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), wl, wr)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_local_attention_closed_forms():
+    """A one-token window returns v; with k = 0 every score is 0, so y is
+    the plain mean of v over the window; the first token of a causal window
+    sees only itself."""
+    B, L, H, D = 1, 40, 2, 8
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    assert np.abs(oracle.local_attention(q, k, v, 0, 0) - v).max() == 0.0
+    z = np.zeros_like(k)
+    y = oracle.local_attention(q, z, v, 3, 5)
+    v64 = v.astype(np.float64)
+    for t in (0, 2, 20, 36, 39):
+        lo, hi = max(0, t - 3), min(L - 1, t + 5)
+        assert np.abs(y[0, t] - v64[0, lo:hi + 1].mean(axis=0)).max() <= 1e-14
+    yc = oracle.local_attention(q, k, v, 255, 0)
+    assert np.abs(yc[:, 0] - v64[:, 0]).max() == 0.0
+
+
+def test_mix_with_local_branch_adds_the_two_outputs():
+    B, L, H, D = 1, 64, 2, 4
+    q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    ones, zeros = np.ones(H * D, np.float32), np.zeros(H * D, np.float32)
+    out, y = oracle.spectre_mix_local(q, k, v, x, gate, ones, zeros, 20, 16, 15, want_y=True)
+    y_fft = oracle.spectre_y(q, k, v, gate, 20)
+    y_loc = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), 16, 15)
+    assert np.abs(y - (y_fft + y_loc)).max() <= 1e-12
+    assert np.abs(out - oracle.layernorm_residual(y_fft + y_loc, x, ones, zeros)).max() <= 1e-9
