@@ -94,6 +94,8 @@ def kernel_bytes(name: str, w, gate_kind: int = 0) -> int:
         return 2 * spec
     if name == "LN_norm":
         return spec + 2 * N * s + 8 * w.C
+    if name == "L_local":  # q, k, v read once; y (binary32) read and written
+        return 3 * N * s + 8 * N
     raise KeyError(name)
 
 
@@ -135,6 +137,19 @@ def cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis):
     return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
             "kind": "oracle", "sample": "the whole workload once, chunked (fft_len %d): %d "
             "columns x %d tokens, float64, %.2f s wall" % (F, w.B * w.C, w.L, dt)}
+
+
+def cpu_baseline_local(w, inp, wl, wr):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.spectre_mix_local(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
+                             inp["beta"], w.keep_bins, wl, wr, dtype=w.dtype, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+            "kind": "oracle", "sample": "the whole workload once with the local branch (keys "
+            "t-%d..t+%d): %d columns x %d tokens, float64, %.2f s wall"
+            % (wl, wr, w.B * w.C, w.L, dt)}
 
 
 def traffic_for(kernel: str, w):
@@ -183,7 +198,13 @@ def run_bench(args):
     if F:
         gbd = dev(gate_blocks)
 
+    win = args.window
+    wl = wr = win // 2
+
     def step():
+        if win:
+            return sm.spectre_mix_fwd_local(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
+                                            w.keep_bins, wl, wr, w.dtype, stream)
         if F:
             return sm.spectre_mix_fwd_chunked(q, k, v, x, gate, gbd, gamma, beta, out, w.B, w.H,
                                               w.L, w.D, F, keep_blk, keep_axis, w.dtype, stream)
@@ -231,7 +252,7 @@ def run_bench(args):
     dom_bytes = kernel_bytes(dom, wk, gk) / nl  # per launch
     avg_ms = per_kernel[dom] / nl
     achieved = dom_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = traffic_for(dom, w) if gk == 0 and no == 0 and not F else None
+    traffic = traffic_for(dom, w) if gk == 0 and no == 0 and not F and not win else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
@@ -267,14 +288,19 @@ def run_bench(args):
         "config": dict(w.describe(), parallelism="single GPU",
                        **({"gate_kind": ["real", "logit", "complex"][gk],
                            "norm": ["post", "pre"][no]} if (gk or no) else {}),
-                       **({"fft_len": F} if F else {})),
+                       **({"fft_len": F} if F else {}),
+                       **({"local_window": [wl, wr]} if win else {})),
         "roofline": roofline,
         "whole_call": whole,
     }
     if not args.profile_run and not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = (cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis)
-                               if F else cpu_baseline(w, inp, gk, no))
+        if win:
+            res["cpu_baseline"] = cpu_baseline_local(w, inp, wl, wr)
+        elif F:
+            res["cpu_baseline"] = cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis)
+        else:
+            res["cpu_baseline"] = cpu_baseline(w, inp, gk, no)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
@@ -310,6 +336,8 @@ def _short(name: str) -> str:
         return "C1_inv_norm" if args[2] == "true" else "C1_inv"
     if kern == "k_layernorm":
         return "LN_norm"
+    if kern == "k_local_attn":
+        return "L_local"
     return name[:60]
 
 
@@ -405,6 +433,8 @@ def main():
                     help="0 out = LN(x + y), 1 out = x + LN(y)")
     ap.add_argument("--fft-len", type=int, default=0,
                     help="chunked mix with blocks of this many tokens (0: one block, the plain mix)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="add the local branch: keys t - W/2 .. t + W/2 (0: no local branch)")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -416,6 +446,10 @@ def main():
         text, _, _ = summarize(args.summarize)
         print(text)
         return 0
+    if args.window and (args.window % 2 or args.fft_len or args.gate_kind or args.norm_order):
+        print("--window takes an even W and the plain mix (real gate, post-norm, no fft_len)",
+              file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested; run with --gpus 1)" % args.gpus, file=sys.stderr)

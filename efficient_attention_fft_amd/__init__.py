@@ -31,7 +31,8 @@ SPECTRE_NORM_PRE = 1
 EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "spectre_mix_plan",
            "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
            "spectre_mix_strerror", "spectre_mix_fwd_ex", "spectre_mix_y_ex",
-           "spectre_mix_workspace_bytes_ex", "spectre_mix_fwd_chunked", "spectre_mix_y_chunked")
+           "spectre_mix_workspace_bytes_ex", "spectre_mix_fwd_chunked", "spectre_mix_y_chunked",
+           "spectre_mix_fwd_local", "spectre_mix_local_attention")
 
 
 class SpectreError(RuntimeError):
@@ -87,6 +88,12 @@ def _load():
     lib.spectre_mix_y_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                           i64, ci, vp]
     lib.spectre_mix_y_chunked.restype = ci
+    lib.spectre_mix_fwd_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          i64, i64, ci, vp]
+    lib.spectre_mix_fwd_local.restype = ci
+    lib.spectre_mix_local_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                                                vp]
+    lib.spectre_mix_local_attention.restype = ci
     lib.spectre_mix_plan.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]
     lib.spectre_mix_plan.restype = ci
@@ -169,6 +176,19 @@ def spectre_mix_y_chunked(q, k, v, gate, gate_blocks, y, B, H, L, D, fft_len, ke
     return _lib.spectre_mix_y_chunked(_addr(q), _addr(k), _addr(v), _addr(gate),
                                       _addr(gate_blocks), _addr(y), B, H, L, D, fft_len,
                                       keep_bins, keep_blocks, dtype, _stream(stream))
+
+
+def spectre_mix_fwd_local(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, win_left,
+                          win_right, dtype, stream=None) -> int:
+    return _lib.spectre_mix_fwd_local(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
+                                      _addr(gamma), _addr(beta), _addr(out), B, H, L, D, keep_bins,
+                                      win_left, win_right, dtype, _stream(stream))
+
+
+def spectre_mix_local_attention(q, k, v, y, B, H, L, D, win_left, win_right, dtype,
+                                stream=None) -> int:
+    return _lib.spectre_mix_local_attention(_addr(q), _addr(k), _addr(v), _addr(y), B, H, L, D,
+                                            win_left, win_right, dtype, _stream(stream))
 
 
 def spectre_mix_workspace_bytes(B, H, L, D, dtype) -> int:

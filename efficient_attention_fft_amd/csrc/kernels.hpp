@@ -1566,6 +1566,222 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
   }
 }
 
+// ------------------------------------------- local branch: windowed attention
+//
+// The sliding-window attention branch (SPECTRE article, section 3.2's
+// use_local_branch and section 4.3): for token t of head h, the keys j with
+// t - WL <= j <= t + WR inside the sequence, scores (q_t . k_j) / sqrt(D),
+// softmax over those keys, y_loc[t] = sum_j p_j v_j.
+//
+// One wave per (32-query tile, head, batch element).  Both products run on
+// MFMA (v_mfma_f32_32x32x16_bf16, binary32 accumulation):
+//   S^T (32 keys x 32 queries) = K_tile (keys x D) . Q_tile^T (D x queries):
+//     lane l supplies K[key l % 32][8 (l / 32) + e + 16 kc] and
+//     Q[query l % 32][the same dims], e < 8, for the D / 16 chunks kc;
+//     lane l receives the scores of query l % 32 for the keys
+//     (v % 4) + 8 (v / 4) + 4 (l / 32), v < 16 -- so a query's softmax needs
+//     only its own lane and lane l ^ 32;
+//   O (32 queries x D) += P (queries x keys) . V (keys x D), per 32-dim tile:
+//     the lane's 16 probabilities are already the A operand of the two
+//     16-key chunks (key order within the contraction is free), and lane l
+//     supplies V[key][dim l % 32] for the same key order.
+// Binary32 storage uses split bfloat16 (x = hi + lo, both bfloat16; the
+// three products hi.hi + hi.lo + lo.hi), which keeps the products to about
+// 2^-16 relative; bfloat16 storage needs only hi.  Softmax in two passes
+// over the key tiles: the running max and sum per query, then the
+// normalised probabilities and the PV product, so O is never rescaled.
+
+struct LocalParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* y;        // [B][L][H][D] binary32
+  int64_t B, L;
+  int H, C;        // C = H * D
+  int64_t WL, WR;  // window: keys t - WL .. t + WR
+  float scale;     // 1 / sqrt(D)
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int DT>
+__device__ __forceinline__ float load_elem_f(const void* base, int64_t i) {
+  if constexpr (DT == IN_BF16) {
+    const uint32_t u = (uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16;
+    return __uint_as_float(u);
+  } else {
+    return reinterpret_cast<const float*>(base)[i];
+  }
+}
+
+// 8 consecutive elements at base[i .. i+8) (i a multiple of 8) as bfloat16
+// hi (and lo = the rounding remainder for binary32 storage); zero when !ok.
+template <int DT>
+__device__ __forceinline__ void load8_split(const void* base, int64_t i, bool ok, bf16x8_t& hi,
+                                            bf16x8_t& lo) {
+  float f[8];
+  if (ok) {
+    if constexpr (DT == IN_BF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + i);
+      const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(a[e] << 16);
+        f[2 * e + 1] = __uint_as_float(a[e] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
+      const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i + 4);
+      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+      f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (__bf16)f[e];
+    lo[e] = (__bf16)(f[e] - (float)hi[e]);
+  }
+}
+
+// ACC: y += the branch (y already holds the spectral mix), else y = it.
+// D % 16 == 0, D <= 128; dims at or above D in the last 32-dim tile are
+// zero operands and are not stored.
+template <int DT, int D, bool ACC>
+__global__ __launch_bounds__(64) void k_local_attn(LocalParams p) {
+  constexpr bool F32 = DT != IN_BF16;  // split the stored operands too
+  constexpr int KC = D / 16;           // contraction chunks of the score product
+  constexpr int DTL = (D + 31) / 32;   // 32-dim output tiles
+  const int lane = threadIdx.x;
+  const int half = lane >> 5, c32 = lane & 31;
+  // work item: 32-query tile fastest, then head, then batch element; the
+  // workgroups one XCD runs (every 8th) take a contiguous run of items, so
+  // the overlapping key windows of neighbouring tiles meet in one L2
+  const int64_t ntq = (p.L + 31) / 32;
+  const int64_t nitem = ntq * p.H * p.B;
+  int64_t w = blockIdx.x;
+  if (nitem % 8 == 0) w = (w % 8) * (nitem / 8) + w / 8;
+  const int64_t t0 = (w % ntq) * 32;
+  const int h = (int)((w / ntq) % p.H);
+  const int64_t b = w / (ntq * p.H);
+  const int64_t rowbase = b * p.L;  // token row of t = 0
+  const int hoff = h * D;
+
+  // Q^T operand: query t0 + c32, dims 16 kc + 8 half + e
+  const int64_t tq = t0 + c32;
+  bf16x8_t qh[KC], ql[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    load8_split<DT>(p.q, (rowbase + tq) * p.C + hoff + 16 * kc + 8 * half, tq < p.L, qh[kc], ql[kc]);
+
+  const int64_t jlo = t0 - p.WL < 0 ? 0 : t0 - p.WL;
+  const int64_t jend = t0 + 31 + p.WR < p.L - 1 ? t0 + 31 + p.WR : p.L - 1;
+  const int nt = (int)((jend - jlo + 32) / 32);
+
+  // scores of key tile n for this lane's query: element v is key
+  // jlo + 32 n + (v % 4) + 8 (v / 4) + 4 half; keys outside the query's
+  // window or the sequence -> -inf
+  auto scores = [&](int n, float (&s)[16]) __attribute__((always_inline)) {
+    const int64_t kt = jlo + 32 * n + c32;  // this lane's key row for the K operand
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      bf16x8_t kh, kl;
+      load8_split<DT>(p.k, (rowbase + kt) * p.C + hoff + 16 * kc + 8 * half, kt <= jend, kh, kl);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kc], acc, 0, 0, 0);
+      if constexpr (F32) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kc], acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t key = jlo + 32 * n + (v & 3) + 8 * (v >> 2) + 4 * half;
+      const bool ok = key <= jend && key >= tq - p.WL && key <= tq + p.WR;
+      s[v] = ok ? acc[v] * p.scale : -INFINITY;
+    }
+  };
+
+  // pass 1: running max and sum of exp over this lane's keys, then the halves
+  float m = -INFINITY, l = 0.f;
+#pragma unroll 1
+  for (int n = 0; n < nt; ++n) {
+    float s[16];
+    scores(n, s);
+    float tm = m;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tm = fmaxf(tm, s[v]);
+    if (tm != -INFINITY) {
+      l *= __expf(m - tm);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) l += __expf(s[v] - tm);
+      m = tm;
+    }
+  }
+  {
+    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+    const float mm = fmaxf(m, mo);
+    l = (m == -INFINITY ? 0.f : l * __expf(m - mm)) + (mo == -INFINITY ? 0.f : lo * __expf(mo - mm));
+    m = mm;
+  }
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+
+  // pass 2: probabilities (split hi + lo) and O += P V
+  f32x16_t o[DTL];
+#pragma unroll
+  for (int dt = 0; dt < DTL; ++dt) o[dt] = f32x16_t{};
+#pragma unroll 1
+  for (int n = 0; n < nt; ++n) {
+    float s[16];
+    scores(n, s);
+    bf16x8_t ph[2], pl[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float pv = s[v] == -INFINITY ? 0.f : __expf(s[v] - m) * inv_l;
+      const __bf16 hi = (__bf16)pv;
+      ph[v >> 3][v & 7] = hi;
+      pl[v >> 3][v & 7] = (__bf16)(pv - (float)hi);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < DTL; ++dt) {
+        // V operand: dim 32 dt + c32, keys (e % 4) + 8 (e / 4) + 16 c + 4 half
+        const int dim = 32 * dt + c32;
+        bf16x8_t vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t key = jlo + 32 * n + (e & 3) + 8 * (e >> 2) + 16 * c + 4 * half;
+          const float f = key <= jend && dim < D ? load_elem_f<DT>(p.v, (rowbase + key) * p.C + hoff + dim)
+                                                 : 0.f;
+          vh[e] = (__bf16)f;
+          vl[e] = (__bf16)(f - (float)vh[e]);
+        }
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
+        if constexpr (F32) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
+      }
+    }
+  }
+  // O element v of lane (dim 32 dt + c32, half): query (v % 4) + 8 (v / 4) + 4 half
+#pragma unroll
+  for (int dt = 0; dt < DTL; ++dt) {
+    const int dim = 32 * dt + c32;
+    if (dim >= D) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t t = t0 + (v & 3) + 8 * (v >> 2) + 4 * half;
+      if (t < p.L) {
+        float* yp = p.y + (rowbase + t) * p.C + hoff + dim;
+        *yp = ACC ? *yp + o[dt][v] : o[dt][v];
+      }
+    }
+  }
+}
+
 // Chunked mix, y only, single-level blocks: y[b][t][pair] += yblk[b][pair]
 // over nb blocks of Lb tokens (b = the block).
 __global__ __launch_bounds__(256) void k_block_add(float2* y, const float2* yblk, int64_t n,

@@ -362,6 +362,11 @@ struct Chunk {
   int64_t B;                 // batch elements (the blockwise shape has B * nb)
 };
 
+// Local branch: keys t - wl .. t + wr of token t (clipped to the sequence).
+struct Local {
+  int64_t wl, wr;
+};
+
 int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, Shape& s,
                 Plan& pl, int gate_kind = SPECTRE_GATE_REAL, int norm_order = SPECTRE_NORM_POST) {
   if (B < 1 || H < 1 || D < 1 || L < 2) return SPECTRE_EINVAL;
@@ -717,6 +722,50 @@ int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
   return SPECTRE_OK;
 }
 
+// The windowed-attention branch over q, k, v of shape s into y (binary32
+// [B][L][H][D]); acc adds it to what y holds.
+template <int DT, bool ACC>
+int launch_local_d(const LocalParams& p, int64_t D, dim3 grid, hipStream_t st) {
+  switch (D) {
+    case 16: hipLaunchKernelGGL((k_local_attn<DT, 16, ACC>), grid, dim3(64), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_local_attn<DT, 32, ACC>), grid, dim3(64), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_local_attn<DT, 64, ACC>), grid, dim3(64), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((k_local_attn<DT, 128, ACC>), grid, dim3(64), 0, st, p); break;
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+  SPECTRE_LAUNCH_CHECK("L_local");
+  return SPECTRE_OK;
+}
+
+bool local_shape_ok(const Shape& s) {
+  if (s.D != 16 && s.D != 32 && s.D != 64 && s.D != 128) return false;
+  const int64_t nitem = (s.L + 31) / 32 * s.H * s.B;
+  return nitem <= (int64_t)(UINT32_MAX / 64);
+}
+
+int launch_local(const void* q, const void* k, const void* v, float* y, const Shape& s,
+                 const Local& lw, bool acc, hipStream_t st) {
+  if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
+  LocalParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.y = y;
+  p.B = s.B;
+  p.L = s.L;
+  p.H = (int)s.H;
+  p.C = (int)s.C;
+  p.WL = std::min<int64_t>(lw.wl, s.L - 1);
+  p.WR = std::min<int64_t>(lw.wr, s.L - 1);
+  p.scale = (float)(1.0 / std::sqrt((double)s.D));
+  const dim3 grid((unsigned)((s.L + 31) / 32 * s.H * s.B));
+  if (s.dtype == SPECTRE_F32)
+    return acc ? launch_local_d<IN_F32, true>(p, s.D, grid, st)
+               : launch_local_d<IN_F32, false>(p, s.D, grid, st);
+  return acc ? launch_local_d<IN_BF16, true>(p, s.D, grid, st)
+             : launch_local_d<IN_BF16, false>(p, s.D, grid, st);
+}
+
 // B, the LDS pass, for shape s / plan pl: the column transforms, the
 // spectral product and the inverse.  in[] are the raw tensors (single level,
 // in_kind their storage) or the spectra (IN_C32); out gets y (single level)
@@ -800,7 +849,8 @@ int launch_block_mix(int dev, const Shape& s, const Chunk& ch, const float2* dc,
 // residual + LayerNorm into `out`.
 int run(const void* q, const void* k, const void* v, const void* x, const float* gate,
         const float* gamma, const float* beta, void* out, float* y, const Shape& s,
-        const Plan& pl, hipStream_t st, const Chunk* chunk = nullptr) {
+        const Plan& pl, hipStream_t st, const Chunk* chunk = nullptr,
+        const Local* local = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
   std::lock_guard<std::mutex> lock(g_mu);
@@ -927,6 +977,10 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     n.eps = eps;
     n.yblk = yblk;  // chunked mix: the block term joins y here
     n.Lb = s.L;
+    if (local) {  // local branch: added to y before the norm
+      rc = launch_local(q, k, v, reinterpret_cast<float*>(ws), s, *local, true, st);
+      if (rc) return rc;
+    }
     return launch_norm(n, s.dtype, pre, st);
   }
 
@@ -943,7 +997,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     rc = strided_inv(pl.L2, c2, st);
     if (rc) return rc;
   }
-  const bool fuse = want_out && fused_norm_ok(CP2);
+  const bool fuse = want_out && fused_norm_ok(CP2) && !local;
   FinalParams f{};
   f.U = U;
   f.x = x;
@@ -966,6 +1020,10 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   f.out = ybuf;
   rc = launch_final<IN_F32>(pl.L1, f, false, false, s.B, st);
   if (rc || !want_out) return rc;
+  if (local) {  // local branch: added to y before the norm
+    rc = launch_local(q, k, v, ybuf, s, *local, true, st);
+    if (rc) return rc;
+  }
   NormParams n{};
   n.y = reinterpret_cast<const float2*>(ybuf);
   n.x = x;
@@ -1096,6 +1154,57 @@ int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const flo
   for (const void* p : {q, k, v})
     if (overlaps(y, (size_t)s.N * 4, p, tb)) return SPECTRE_EINVAL;
   return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream, &ch);
+}
+
+int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,
+                          const float* gate, const float* gamma, const float* beta, void* out,
+                          int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                          int64_t win_left, int64_t win_right, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
+  if (win_left < 0 || win_right < 0) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  if (rc) return rc;
+  if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
+  const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v, x})
+    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
+  const Local lw{win_left, win_right};
+  return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream, nullptr, &lw);
+}
+
+int spectre_mix_local_attention(const void* q, const void* k, const void* v, float* y, int64_t B,
+                                int64_t H, int64_t L, int64_t D, int64_t win_left,
+                                int64_t win_right, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !y) return SPECTRE_EINVAL;
+  if (win_left < 0 || win_right < 0) return SPECTRE_EINVAL;
+  if (B < 1 || H < 1 || D < 1 || L < 1) return SPECTRE_EINVAL;
+  if (dtype != SPECTRE_F32 && dtype != SPECTRE_BF16) return SPECTRE_EINVAL;
+  if (H > kMaxC || D > kMaxC || H * D > kMaxC) return SPECTRE_EUNSUPPORTED;
+  if (L > (int64_t(1) << 40) / (B * H * D)) return SPECTRE_EUNSUPPORTED;
+  Shape s{};
+  s.B = B;
+  s.H = H;
+  s.L = L;
+  s.D = D;
+  s.C = H * D;
+  s.N = B * L * H * D;
+  s.dtype = dtype;
+  s.esz = dtype == SPECTRE_F32 ? 4 : 2;
+  if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
+  const void* ptrs[] = {q, k, v, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v})
+    if (overlaps(y, (size_t)s.N * 4, p, tb)) return SPECTRE_EINVAL;
+  std::lock_guard<std::mutex> lock(g_mu);
+  trace_call_begin(stream);
+  return launch_local(q, k, v, y, s, Local{win_left, win_right}, false, stream);
 }
 
 size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D, int dtype,

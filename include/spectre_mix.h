@@ -177,6 +177,39 @@ int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const flo
                           int dtype, hipStream_t stream);
 
 /*
+ * The mix with the local branch (SPECTRE article, section 3.2's
+ * use_local_branch and section 4.3: a sliding-window attention branch beside
+ * the FFT branch, the two outputs added before the residual):
+ *   out = LayerNorm_{H*D}(x + y + y_loc),
+ * y the spectral mix of spectre_mix_fwd (real gate), and y_loc of head h at
+ * token t the softmax over the keys j, t - win_left <= j <= t + win_right and
+ * 0 <= j < L, of (q_t . k_j) / sqrt(D), applied to v_j (see
+ * spectre_mix_local_attention).  Arguments, layout, ownership and errors as
+ * spectre_mix_fwd, plus win_left, win_right >= 0 (else SPECTRE_EINVAL; a
+ * window longer than the sequence is clipped to it), and D must be 16, 32,
+ * 64 or 128 (else SPECTRE_EUNSUPPORTED).  The workspace is that of
+ * spectre_mix_fwd (spectre_mix_workspace_bytes).
+ */
+int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,
+                          const float* gate, const float* gamma, const float* beta, void* out,
+                          int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                          int64_t win_left, int64_t win_right, int dtype, hipStream_t stream);
+
+/*
+ * The local branch alone, the test hook of spectre_mix_fwd_local:
+ * y[b, t, h, :] = sum_j p_j v[b, j, h, :], with p the softmax over the keys
+ * j in [t - win_left, t + win_right] and [0, L) of (q[b,t,h,:] . k[b,j,h,:])
+ * / sqrt(D).  q, k, v: [B, L, H, D] in `dtype` storage; y: binary32
+ * [B, L, H, D], written whole, not overlapping q, k or v.  Any L >= 1;
+ * D 16, 32, 64 or 128 (else SPECTRE_EUNSUPPORTED); pointers 16-byte
+ * aligned, win_left, win_right >= 0 (else SPECTRE_EINVAL).  Uses no
+ * workspace.  Asynchronous on `stream`.
+ */
+int spectre_mix_local_attention(const void* q, const void* k, const void* v, float* y, int64_t B,
+                                int64_t H, int64_t L, int64_t D, int64_t win_left,
+                                int64_t win_right, int dtype, hipStream_t stream);
+
+/*
  * Device workspace bytes a spectre_mix_fwd call of this shape uses (0 if the
  * shape is invalid or unsupported).  Pure host arithmetic; no device call.
  */

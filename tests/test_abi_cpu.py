@@ -117,6 +117,35 @@ def test_chunked_rejects_before_device():
     assert call(F=5 * 1024, L=10 * 1024, keepb=1) == sm.SPECTRE_EUNSUPPORTED  # fft_len: factor 5
 
 
+def test_local_rejects_before_device():
+    def mix(**kw):
+        a = dict(B=1, H=8, L=65536, D=64, keep=32769, wl=64, wr=64, dt=0, out=GOOD + 0x70000000)
+        a.update(kw)
+        return sm.spectre_mix_fwd_local(GOOD, GOOD + 0x1000000, GOOD + 0x2000000,
+                                        GOOD + 0x3000000, GOOD + 0x4000000, GOOD + 0x5000000,
+                                        GOOD + 0x6000000, a["out"], a["B"], a["H"], a["L"],
+                                        a["D"], a["keep"], a["wl"], a["wr"], a["dt"], 0)
+    assert mix(wl=-1) == sm.SPECTRE_EINVAL
+    assert mix(wr=-5) == sm.SPECTRE_EINVAL
+    assert mix(D=48, H=8) == sm.SPECTRE_EUNSUPPORTED     # head size the kernel lacks
+    assert mix(L=65535, keep=1) == sm.SPECTRE_EINVAL      # checked like spectre_mix_fwd
+    assert mix(out=GOOD + 0x3000000) == sm.SPECTRE_EINVAL  # out == x
+
+    def attn(**kw):
+        a = dict(B=1, H=2, L=100, D=64, wl=3, wr=3, dt=0, y=GOOD + 0x1000000, q=GOOD)
+        a.update(kw)
+        return sm.spectre_mix_local_attention(a["q"], GOOD + 0x400000, GOOD + 0x800000, a["y"],
+                                              a["B"], a["H"], a["L"], a["D"], a["wl"], a["wr"],
+                                              a["dt"], 0)
+    assert attn(L=0) == sm.SPECTRE_EINVAL
+    assert attn(wl=-1) == sm.SPECTRE_EINVAL
+    assert attn(dt=2) == sm.SPECTRE_EINVAL
+    assert attn(D=24) == sm.SPECTRE_EUNSUPPORTED
+    assert attn(q=GOOD + 4) == sm.SPECTRE_EINVAL          # misaligned
+    assert attn(y=GOOD + 0x400000 + 64) == sm.SPECTRE_EINVAL  # y overlaps k
+    assert attn(q=0) == sm.SPECTRE_EINVAL
+
+
 def test_y_rejects_before_device():
     assert sm.spectre_mix_y(0, GOOD, GOOD, GOOD, GOOD, 1, 8, 4096, 64, 2049, 0, 0) == \
         sm.SPECTRE_EINVAL

@@ -1,0 +1,165 @@
+"""The local branch on the GPU against the oracle: the sliding-window
+attention alone (spectre_mix_local_attention) and the mix with it
+(spectre_mix_fwd_local, out = LN(x + y + y_loc)), the SPECTRE article's
+use_local_branch (section 3.2) and its FFT-plus-window hybrid (section 4.3).
+
+Tolerances: out max-abs 1e-4 (binary32 storage), 2e-2 (bfloat16 storage), as
+for the plain mix; y_loc within 1e-4 * max(1, max|y_loc|).  The MFMA products
+run on split bfloat16 operands (hi + lo), about 2^-16 relative per product,
+well inside 1e-4.
+
+Windows: 128 and 256 keys (the article's sizes), one-sided (wr = 0),
+asymmetric, a window of one key (y_loc = v), one longer than the sequence
+(full attention); lengths with a ragged last 32-query tile, L = 1, and every
+head size the kernel takes (16, 32, 64, 128).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import dev, empty_like_storage, oracle_threads, to_host_f64, tol, torch, y_tol
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_local(sm, inp, w, wl, wr):
+    t = torch()
+    q, k, v = (dev(inp[n]) for n in "qkv")
+    y = t.full((w.N,), float("nan"), dtype=t.float32, device="cuda")
+    sm.check(sm.spectre_mix_local_attention(q, k, v, y, w.B, w.H, w.L, w.D, wl, wr, w.dtype))
+    t.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64).reshape(w.B, w.L, w.H, w.D)
+
+
+ATTN_CASES = [
+    # (B, L, H, D, dtype, win_left, win_right)
+    (1, 256, 2, 16, 0, 64, 64),       # window 128 on the tiny shape
+    (2, 300, 2, 64, 0, 20, 5),        # ragged last tile, asymmetric
+    (1, 1000, 4, 32, 1, 127, 0),      # one-sided (causal-style) window, bfloat16
+    (1, 97, 1, 128, 0, 500, 500),     # window longer than the sequence: full attention
+    (1, 1, 1, 16, 0, 3, 3),           # one token
+    (2, 4096, 8, 64, 0, 64, 64),      # 4096-token shape, window 128
+    (1, 4096, 8, 64, 1, 128, 128),    # window 256, bfloat16
+    (3, 33, 3, 32, 0, 0, 40),         # B * tiles * H not a multiple of 8, look-ahead only
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,wl,wr", ATTN_CASES)
+def test_local_attention_against_oracle(B, L, H, D, dt, wl, wr):
+    import efficient_attention_fft_amd as sm
+    w = workloads.custom(600 + L % 97, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=L // 2 + 1)
+    say("case", w.describe(), "window", wl, wr)
+    inp = workloads.make_inputs(w)
+    ref = oracle.local_attention(inp["q"], inp["k"], inp["v"], wl, wr, dtype=dt)
+    got = run_local(sm, inp, w, wl, wr)
+    err = np.abs(got - ref).max()
+    say("  y_loc max-abs err %.3g (tol %.3g)" % (err, y_tol(ref)))
+    assert np.all(np.isfinite(got)) and err <= y_tol(ref)
+
+
+def test_window_of_one_key_is_v():
+    """win_left = win_right = 0: each query sees only itself, so y_loc = v, to
+    the split-bfloat16 representation of v (hi + lo carries 16 significant
+    bits; 2^-16 relative bounds it)."""
+    import efficient_attention_fft_amd as sm
+    w = workloads.custom(611, B=1, L=200, H=2, D=64, dtype=0, keep_bins=101)
+    inp = workloads.make_inputs(w)
+    got = run_local(sm, inp, w, 0, 0)
+    v = inp["v"].astype(np.float64).reshape(got.shape)
+    err = np.abs(got - v).max()
+    say("  one-key window: max |y_loc - v| %.3g" % err)
+    assert err <= 2.0 ** -16 * np.abs(v).max()
+
+
+def test_local_attention_full_size_sampled():
+    """The 65536-token shape (B=1, H=8, D=64, binary32), window 128: the
+    oracle computes sampled tokens from the sub-sequence their window covers
+    (a token's output depends only on the keys in its window)."""
+    import efficient_attention_fft_amd as sm
+    w = workloads.WORKLOADS[3]
+    inp = workloads.make_inputs(w)
+    wl = wr = 64
+    got = run_local(sm, inp, w, wl, wr)
+    toks = [0, 1, 31, 32, 63, 64, 65, 1000, 32767, 32768, 65471, 65472, 65503, 65504, 65535]
+    toks += list(np.random.default_rng(5).integers(0, w.L, 17))
+    worst = 0.0
+    for t in toks:
+        lo, hi = max(0, t - wl), min(w.L, t + wr + 1)
+        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[:, lo:hi] for n in "qkv"}
+        ref = oracle.local_attention(sub["q"], sub["k"], sub["v"], wl, wr)[:, t - lo]
+        worst = max(worst, np.abs(got[:, t] - ref).max())
+    say("  sampled y_loc max-abs err %.3g over %d tokens" % (worst, len(toks)))
+    assert worst <= 1e-4
+
+
+MIX_CASES = [
+    # (B, L, H, D, dtype, keep_bins, win_left, win_right)
+    (1, 256, 2, 16, 0, 129, 64, 64),       # single-level square kernel
+    (2, 4096, 8, 64, 0, 2049, 64, 64),     # single-level generic LDS kernel, window 128
+    (1, 16384, 2, 32, 0, 3000, 128, 128),  # two-level plan, window 256
+    (1, 16384, 8, 64, 1, 4097, 64, 63),    # bfloat16, LDS-copy B kernel
+    (1, 98304, 1, 32, 0, 49153, 100, 0),   # three-level plan (32 x 3 x 1024), one-sided
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep,wl,wr", MIX_CASES)
+def test_mix_with_local_branch_against_oracle(B, L, H, D, dt, keep, wl, wr):
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.custom(620 + L % 89, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=keep, affine=True)
+    say("case", w.describe(), "window", wl, wr)
+    inp = workloads.make_inputs(w)
+    ref = oracle.spectre_mix_local(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
+                                   inp["gamma"], inp["beta"], keep, wl, wr, dtype=dt,
+                                   nthreads=oracle_threads())
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, gam, bet = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
+    _, out = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_local(q, k, v, x, g, gam, bet, out, B, H, L, D, keep, wl, wr, dt))
+    t.cuda.synchronize()
+    got = to_host_f64(out, dt).reshape(ref.shape)
+    err = np.abs(got - ref).max()
+    say("  out max-abs err %.3g (tol %.1g)" % (err, tol(w)))
+    assert np.all(np.isfinite(got)) and err <= tol(w)
+
+
+def test_mix_with_local_branch_full_size_sampled():
+    """The 65536-token shape (binary32), window 128, in the launch
+    configuration the benchmark times: at sampled tokens the oracle's
+    spectral y, plus its windowed attention over each token's sub-sequence,
+    through its residual LayerNorm."""
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.WORKLOADS[3]
+    inp = workloads.make_inputs(w)
+    wl = wr = 64
+    toks = np.array(sorted(set([0, 5, 64, 65535, 32768] +
+                               list(np.random.default_rng(7).integers(0, w.L, 27)))), np.int64)
+    _, ref_y = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
+                                         inp["gamma"], inp["beta"], w.keep_bins, toks,
+                                         dtype=w.dtype, nthreads=oracle_threads())
+    yl = np.empty_like(ref_y)
+    for i, tk in enumerate(toks):
+        lo, hi = max(0, tk - wl), min(w.L, tk + wr + 1)
+        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[:, lo:hi] for n in "qkv"}
+        yl[i] = oracle.local_attention(sub["q"], sub["k"], sub["v"], wl, wr, dtype=w.dtype)[0, tk - lo]
+    xs = inp["x"].reshape(w.L, w.H, w.D)[toks]
+    ref = oracle.layernorm_residual(ref_y + yl, xs, inp["gamma"], inp["beta"], dtype=w.dtype)
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, gam, bet = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
+    _, out = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_local(q, k, v, x, g, gam, bet, out, w.B, w.H, w.L, w.D,
+                                      w.keep_bins, wl, wr, w.dtype))
+    t.cuda.synchronize()
+    got = to_host_f64(out.view(w.L, w.C)[t.from_numpy(toks).cuda()], w.dtype).reshape(ref.shape)
+    err = np.abs(got - ref).max()
+    say("  out max-abs err %.3g over %d tokens" % (err, len(toks)))
+    assert err <= tol(w)
