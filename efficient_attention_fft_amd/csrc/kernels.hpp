@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dft.hpp"
 
 namespace spectre {
@@ -1307,6 +1309,7 @@ struct FinalParams {
   float inv_c;
   float eps;
   const float2* yblk;  // chunked mix: [B][CP2] term added to every token of batch (block) b, or null
+  const float2* yloc;  // local branch: [B][L][CP2] term added to y, or null
 };
 
 template <int R, int DT, bool FUSE, bool PRE = false>
@@ -1335,6 +1338,10 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
   // token t = n1 M + m of batch b sits at pair offset ((b L) + t) CP2 + cp
   const int64_t obase = (b * p.L + m) * p.CP2 + cp;
   const int64_t ostep = p.M * p.CP2;
+  if (p.yloc != nullptr) {  // local branch: its output joins y
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[r] = cadd(z[r], load_nt(p.yloc + obase + r * ostep));
+  }
   if constexpr (!FUSE) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1415,7 +1422,8 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
 // waves per CU.  Token sums: recursive halving over the 32 lanes of a half
 // (lane c ends with the half-wave total of slot c), then the waves' totals
 // meet in LDS.  Needs CP2 % 32 == 0 and CP2 <= 256.
-template <int R, int DT, bool PRE = false, bool BLK = false>
+// ADD: 0 nothing more, 1 the chunked mix's block term, 2 the local branch.
+template <int R, int DT, bool PRE = false, int ADD = 0>
 __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   constexpr int R2 = R / 2;
   constexpr int T2 = next_pow2(R2);  // 32: token slots per half
@@ -1439,7 +1447,7 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   }
   dft<R2, +1>(z);
   join_swap<R, +1>(z, h);
-  if constexpr (BLK) {  // chunked mix: the block term, the same for every token here
+  if constexpr (ADD == 1) {  // chunked mix: the block term, the same for every token here
     const float2 yb = p.yblk[b * p.CP2 + cp];
 #pragma unroll
     for (int a = 0; a < R2; ++a) z[a] = cadd(z[a], yb);
@@ -1451,6 +1459,14 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   const int64_t ostep = p.M * p.CP2;
   const int64_t obase = (b * p.L + m) * p.CP2 + cp + (int64_t)(Q * h) * ostep;
   auto toff = [&](int j) { return (int64_t)(j < Q ? j : j + Q) * ostep; };  // tok(j) - Q h
+  if constexpr (ADD == 2) {  // local branch: its output joins y
+#pragma unroll
+    for (int g = 0; g < R2; g += 8) {
+#pragma unroll
+      for (int j = g; j < g + 8 && j < R2; ++j) z[j] = cadd(z[j], load_nt(p.yloc + obase + toff(j)));
+      asm volatile("" ::: "memory");
+    }
+  }
   // residual, loaded in groups of 8 so that the loads in flight fit the
   // register budget of four waves per SIMD
   if constexpr (!PRE) {  // post-norm: the statistics are those of x + y
@@ -1522,6 +1538,7 @@ struct NormParams {
   float inv_c, eps;
   const float2* yblk;  // chunked mix: [ntok / Lb][CP2] block term added to y, or null
   int64_t Lb;          // tokens per block
+  const float2* yloc;  // local branch: [ntok][CP2] term added to y, or null
 };
 
 template <int DT, bool PRE = false>
@@ -1539,6 +1556,7 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
     if (c < p.CP2) {
       z[it] = load_nt(p.y + base + c);
       if (p.yblk != nullptr) z[it] = cadd(z[it], p.yblk[(tok / p.Lb) * p.CP2 + c]);
+      if (p.yloc != nullptr) z[it] = cadd(z[it], load_nt(p.yloc + base + c));
       if constexpr (!PRE) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
@@ -1573,213 +1591,337 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
 // t - WL <= j <= t + WR inside the sequence, scores (q_t . k_j) / sqrt(D),
 // softmax over those keys, y_loc[t] = sum_j p_j v_j.
 //
-// One wave per (32-query tile, head, batch element).  Both products run on
-// MFMA (v_mfma_f32_32x32x16_bf16, binary32 accumulation):
+// One wave per (32-query tile, head, batch element), one pass over the key
+// tiles of 32 with the running-max softmax.  Both products run on MFMA
+// (v_mfma_f32_32x32x16_bf16, binary32 accumulation):
 //   S^T (32 keys x 32 queries) = K_tile (keys x D) . Q_tile^T (D x queries):
-//     lane l supplies K[key l % 32][8 (l / 32) + e + 16 kc] and
+//     lane l supplies K[key l % 32][16 kc + 8 (l / 32) + e] and
 //     Q[query l % 32][the same dims], e < 8, for the D / 16 chunks kc;
 //     lane l receives the scores of query l % 32 for the keys
-//     (v % 4) + 8 (v / 4) + 4 (l / 32), v < 16 -- so a query's softmax needs
-//     only its own lane and lane l ^ 32;
+//     (v % 4) + 8 (v / 4) + 4 (l / 32), v < 16 -- so a query's max and sum
+//     need only its own lane and lane l ^ 32;
 //   O (32 queries x D) += P (queries x keys) . V (keys x D), per 32-dim tile:
 //     the lane's 16 probabilities are already the A operand of the two
 //     16-key chunks (key order within the contraction is free), and lane l
-//     supplies V[key][dim l % 32] for the same key order.
-// Binary32 storage uses split bfloat16 (x = hi + lo, both bfloat16; the
-// three products hi.hi + hi.lo + lo.hi), which keeps the products to about
-// 2^-16 relative; bfloat16 storage needs only hi.  Softmax in two passes
-// over the key tiles: the running max and sum per query, then the
-// normalised probabilities and the PV product, so O is never rescaled.
+//     supplies V[key][dim l % 32] for the same key order; O's element v of
+//     lane l is query (v % 4) + 8 (v / 4) + 4 (l / 32), dim l % 32, so the
+//     per-query rescale and the final 1 / sum reach O through 32 floats of
+//     LDS.
+// Binary32 storage splits every operand into bfloat16 hi + lo (hi the
+// rounded value, lo the rounded remainder: 16 significant bits) and sums the
+// products hi.hi + hi.lo + lo.hi; bfloat16 storage is exact in hi, and only
+// the probabilities are split.  The next key tile's loads are issued before
+// the current tile's arithmetic (two register sets, rows clamped into the
+// sequence so that every load is unconditional; clamped keys are masked).
 
 struct LocalParams {
   const void* q;
   const void* k;
   const void* v;
   float* y;        // [B][L][H][D] binary32
-  int64_t B, L;
-  int H, C;        // C = H * D
-  int64_t WL, WR;  // window: keys t - WL .. t + WR
-  float scale;     // 1 / sqrt(D)
+  int64_t L;
+  int B, H, C;     // C = H * D
+  int WL, WR;      // window: keys t - WL .. t + WR (each below L)
+  float scale2;    // log2(e) / sqrt(D): scores in base-2 exponent units
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int DT>
-__device__ __forceinline__ float load_elem_f(const void* base, int64_t i) {
-  if constexpr (DT == IN_BF16) {
-    const uint32_t u = (uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16;
-    return __uint_as_float(u);
-  } else {
-    return reinterpret_cast<const float*>(base)[i];
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// hi = f rounded to bfloat16 (pairs converted together), lo = the remainder
+// f - hi (exact in binary32) rounded to bfloat16.
+__device__ __forceinline__ void split8(const float (&f)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t a = {f[2 * i], f[2 * i + 1]};
+    h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
+    const f32x2_t r = {f[2 * i] - __uint_as_float(h[i] << 16),
+                       f[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u)};
+    l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
   }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
-// 8 consecutive elements at base[i .. i+8) (i a multiple of 8) as bfloat16
-// hi (and lo = the rounding remainder for binary32 storage); zero when !ok.
-template <int DT>
-__device__ __forceinline__ void load8_split(const void* base, int64_t i, bool ok, bf16x8_t& hi,
-                                            bf16x8_t& lo) {
-  float f[8];
-  if (ok) {
-    if constexpr (DT == IN_BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + i);
-      const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+// One key tile's raw operands for one lane: K (KTile) and V (VTile).
+template <int DT, int D>
+struct LocalShape {
+  static constexpr bool F32 = DT != IN_BF16;
+  static constexpr int KC = D / 16;
+  static constexpr int DTL = (D + 31) / 32;
+  using E = typename std::conditional<F32, float, uint16_t>::type;
+};
+
+// kt: element (key j0, dim 0) of this head (wave-uniform); keys j0 + r with
+// r > lim are clamped to j0 + lim (the sequence end).  This lane's K row is
+// j0 + c32, dims 16 kc + 8 half + e (two float4, or one uint4 of bfloat16).
+template <int DT, int D>
+struct KTile {
+  using S = LocalShape<DT, D>;
+  float4 kf[S::F32 ? S::KC : 1][2];
+  uint4 kb[S::F32 ? 1 : S::KC];
+  // (byte offsets from the uniform base in 32 bits: the loads take the
+  // scalar-base form)
+  __device__ __forceinline__ void load(const typename S::E* kt, int lim, int C, int half, int c32) {
+    constexpr uint32_t es = sizeof(typename S::E);
+    const char* kb0 = reinterpret_cast<const char*>(kt);
+    const uint32_t kro = (__umul24((uint32_t)(c32 < lim ? c32 : lim), (uint32_t)C) + 8 * half) * es;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[2 * e] = __uint_as_float(a[e] << 16);
-        f[2 * e + 1] = __uint_as_float(a[e] & 0xffff0000u);
+    for (int kc = 0; kc < S::KC; ++kc) {
+      if constexpr (S::F32) {
+        kf[kc][0] = *reinterpret_cast<const float4*>(kb0 + kro + 64 * kc);
+        kf[kc][1] = *reinterpret_cast<const float4*>(kb0 + kro + 64 * kc + 16);
+      } else {
+        kb[kc] = *reinterpret_cast<const uint4*>(kb0 + kro + 32 * kc);
       }
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i);
-      const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + i + 4);
-      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-      f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = 0.f;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    hi[e] = (__bf16)f[e];
-    lo[e] = (__bf16)(f[e] - (float)hi[e]);
-  }
-}
+};
 
-// ACC: y += the branch (y already holds the spectral mix), else y = it.
-// D % 16 == 0, D <= 128; dims at or above D in the last 32-dim tile are
-// zero operands and are not stored.
-template <int DT, int D, bool ACC>
-__global__ __launch_bounds__(64) void k_local_attn(LocalParams p) {
-  constexpr bool F32 = DT != IN_BF16;  // split the stored operands too
-  constexpr int KC = D / 16;           // contraction chunks of the score product
-  constexpr int DTL = (D + 31) / 32;   // 32-dim output tiles
+// vt as kt; this lane's V keys are (e % 4) + 8 (e / 4) + 16 c + 4 half at
+// dim 32 dt + c32 (dims at or above D read dim 0).
+template <int DT, int D>
+struct VTile {
+  using S = LocalShape<DT, D>;
+  typename S::E vv[2][S::DTL][8];
+  __device__ __forceinline__ void load(const typename S::E* vt, int lim, int C, int half, int c32) {
+    using E = typename S::E;
+    constexpr uint32_t es = sizeof(E);
+    const char* vb0 = reinterpret_cast<const char*>(vt);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = (e & 3) + 8 * (e >> 2) + 16 * c + 4 * half;
+        const uint32_t vro = __umul24((uint32_t)(r < lim ? r : lim), (uint32_t)C);
+#pragma unroll
+        for (int dt = 0; dt < S::DTL; ++dt) {
+          const uint32_t dim = 32 * dt + c32 < D ? 32 * dt + c32 : 0;
+          vv[c][dt][e] = *reinterpret_cast<const E*>(vb0 + (vro + dim) * es);
+        }
+      }
+  }
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void local_attn(const LocalParams& p) {
+  using S = LocalShape<DT, D>;
+  using E = typename S::E;
+  constexpr bool F32 = S::F32;
+  constexpr int KC = S::KC;
+  constexpr int DTL = S::DTL;
+  constexpr float NEG = -1e30f;  // running max before any key: exp2 of masked scores stays 0
+  __shared__ float4 bc[8];       // 32 per-query factors, broadcast to O's layout
   const int lane = threadIdx.x;
   const int half = lane >> 5, c32 = lane & 31;
+  const int C = p.C;
   // work item: 32-query tile fastest, then head, then batch element; the
   // workgroups one XCD runs (every 8th) take a contiguous run of items, so
   // the overlapping key windows of neighbouring tiles meet in one L2
-  const int64_t ntq = (p.L + 31) / 32;
-  const int64_t nitem = ntq * p.H * p.B;
-  int64_t w = blockIdx.x;
+  const int ntq = (int)((p.L + 31) / 32);
+  const int nitem = ntq * p.H * p.B;
+  int w = blockIdx.x;
   if (nitem % 8 == 0) w = (w % 8) * (nitem / 8) + w / 8;
-  const int64_t t0 = (w % ntq) * 32;
-  const int h = (int)((w / ntq) % p.H);
-  const int64_t b = w / (ntq * p.H);
-  const int64_t rowbase = b * p.L;  // token row of t = 0
-  const int hoff = h * D;
+  const int64_t t0 = (int64_t)(w % ntq) * 32;
+  const int h = (w / ntq) % p.H;
+  const int b = w / (ntq * p.H);
+  const int64_t base = (int64_t)b * p.L * C + (int64_t)h * D;  // element (b, t = 0, h, 0)
+  const int64_t Lm1 = p.L - 1;
+  const E* qp = reinterpret_cast<const E*>(p.q) + base;
+  const E* kp = reinterpret_cast<const E*>(p.k) + base;
+  const E* vp = reinterpret_cast<const E*>(p.v) + base;
 
-  // Q^T operand: query t0 + c32, dims 16 kc + 8 half + e
+  // Q^T operand: query t0 + c32 (clamped; outputs of clamped queries are not stored)
   const int64_t tq = t0 + c32;
   bf16x8_t qh[KC], ql[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    load8_split<DT>(p.q, (rowbase + tq) * p.C + hoff + 16 * kc + 8 * half, tq < p.L, qh[kc], ql[kc]);
-
-  const int64_t jlo = t0 - p.WL < 0 ? 0 : t0 - p.WL;
-  const int64_t jend = t0 + 31 + p.WR < p.L - 1 ? t0 + 31 + p.WR : p.L - 1;
-  const int nt = (int)((jend - jlo + 32) / 32);
-
-  // scores of key tile n for this lane's query: element v is key
-  // jlo + 32 n + (v % 4) + 8 (v / 4) + 4 half; keys outside the query's
-  // window or the sequence -> -inf
-  auto scores = [&](int n, float (&s)[16]) __attribute__((always_inline)) {
-    const int64_t kt = jlo + 32 * n + c32;  // this lane's key row for the K operand
-    f32x16_t acc = {};
+  {
+    const E* qt = qp + t0 * C;
+    const int lim = (int)(Lm1 - t0);
+    const uint32_t o = (uint32_t)(c32 < lim ? c32 : lim) * (uint32_t)C + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      bf16x8_t kh, kl;
-      load8_split<DT>(p.k, (rowbase + kt) * p.C + hoff + 16 * kc + 8 * half, kt <= jend, kh, kl);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kc], acc, 0, 0, 0);
       if constexpr (F32) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kc], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kc], acc, 0, 0, 0);
+        const float4* src = reinterpret_cast<const float4*>(qt + o + 16 * kc);
+        const float4 a = src[0], c = src[1];
+        const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        split8(f, qh[kc], ql[kc]);
+      } else {
+        qh[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qt + o + 16 * kc));
       }
     }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t key = jlo + 32 * n + (v & 3) + 8 * (v >> 2) + 4 * half;
-      const bool ok = key <= jend && key >= tq - p.WL && key <= tq + p.WR;
-      s[v] = ok ? acc[v] * p.scale : -INFINITY;
-    }
-  };
-
-  // pass 1: running max and sum of exp over this lane's keys, then the halves
-  float m = -INFINITY, l = 0.f;
-#pragma unroll 1
-  for (int n = 0; n < nt; ++n) {
-    float s[16];
-    scores(n, s);
-    float tm = m;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) tm = fmaxf(tm, s[v]);
-    if (tm != -INFINITY) {
-      l *= __expf(m - tm);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) l += __expf(s[v] - tm);
-      m = tm;
-    }
   }
-  {
-    const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
-    const float mm = fmaxf(m, mo);
-    l = (m == -INFINITY ? 0.f : l * __expf(m - mm)) + (mo == -INFINITY ? 0.f : lo * __expf(mo - mm));
-    m = mm;
-  }
-  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
 
-  // pass 2: probabilities (split hi + lo) and O += P V
+  const int64_t jlo = t0 - p.WL < 0 ? 0 : t0 - p.WL;
+  const int64_t jend = t0 + 31 + p.WR < Lm1 ? t0 + 31 + p.WR : Lm1;
+  const int nt = (int)((jend - jlo + 32) / 32);
+  // key j is in this lane's query window iff 0 <= j - tq + WL <= qwin_hi
+  // (for a clamped query tq >= L the test admits any key: its row is not stored)
+  const int qwin_hi = (int)((tq + p.WR < Lm1 ? tq + p.WR : Lm1) - tq + p.WL);
+  const int d0 = (int)(jlo - tq + p.WL) + 4 * half;  // key (v%4)+8(v/4) of tile 0, relative
+
+  float m = NEG, lsum = 0.f;
   f32x16_t o[DTL];
 #pragma unroll
   for (int dt = 0; dt < DTL; ++dt) o[dt] = f32x16_t{};
-#pragma unroll 1
-  for (int n = 0; n < nt; ++n) {
+
+  // tile n: its V loads go out first, then the next tile's K loads (K of
+  // tile n was loaded during tile n - 1); V is needed only after the scores
+  // and the softmax update, so both overlap the arithmetic
+  auto tile_rows = [&](int n, int& lim) __attribute__((always_inline)) {
+    // wave-uniform: kept in scalar registers so the loads take a scalar base
+    const int j0 = __builtin_amdgcn_readfirstlane((int)jlo + 32 * n);
+    lim = __builtin_amdgcn_readfirstlane((int)(Lm1 - j0 < 31 ? Lm1 - j0 : 31));
+    return (int64_t)j0 * C;
+  };
+  auto consume = [&](const KTile<DT, D>& T, const VTile<DT, D>& V, int n)
+                     __attribute__((always_inline)) {
+    // scores
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if constexpr (F32) {
+        const float f[8] = {T.kf[kc][0].x, T.kf[kc][0].y, T.kf[kc][0].z, T.kf[kc][0].w,
+                            T.kf[kc][1].x, T.kf[kc][1].y, T.kf[kc][1].z, T.kf[kc][1].w};
+        bf16x8_t kh, kl;
+        split8(f, kh, kl);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kc], acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, T.kb[kc]),
+                                                      qh[kc], acc, 0, 0, 0);
+      }
+    }
+    // mask (window of this lane's query, and the sequence end), tile max
     float s[16];
-    scores(n, s);
+    float tmax = NEG;
+    const int dn = d0 + 32 * n;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int d = dn + (v & 3) + 8 * (v >> 2);
+      s[v] = (uint32_t)d <= (uint32_t)qwin_hi ? acc[v] * p.scale2 : -INFINITY;
+      tmax = fmaxf(tmax, s[v]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float ps = 0.f;
     bf16x8_t ph[2], pl[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float pv = s[v] == -INFINITY ? 0.f : __expf(s[v] - m) * inv_l;
+      const float pv = __builtin_amdgcn_exp2f(s[v] - mn);
+      ps += pv;
       const __bf16 hi = (__bf16)pv;
       ph[v >> 3][v & 7] = hi;
       pl[v >> 3][v & 7] = (__bf16)(pv - (float)hi);
     }
+    lsum = lsum * alpha + ps;
+    // rescale O by its queries' alpha
+    if (half == 0) reinterpret_cast<float*>(bc)[c32] = alpha;
+    __syncthreads();
+    float4 a4[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int g = 0; g < 4; ++g) a4[g] = bc[2 * g + half];
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < DTL; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        o[dt][4 * g + 0] *= a4[g].x;
+        o[dt][4 * g + 1] *= a4[g].y;
+        o[dt][4 * g + 2] *= a4[g].z;
+        o[dt][4 * g + 3] *= a4[g].w;
+      }
+    // O += P V
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int dt = 0; dt < DTL; ++dt) {
-        // V operand: dim 32 dt + c32, keys (e % 4) + 8 (e / 4) + 16 c + 4 half
-        const int dim = 32 * dt + c32;
-        bf16x8_t vh, vl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t key = jlo + 32 * n + (e & 3) + 8 * (e >> 2) + 16 * c + 4 * half;
-          const float f = key <= jend && dim < D ? load_elem_f<DT>(p.v, (rowbase + key) * p.C + hoff + dim)
-                                                 : 0.f;
-          vh[e] = (__bf16)f;
-          vl[e] = (__bf16)(f - (float)vh[e]);
+        if constexpr (F32) {
+          bf16x8_t vh, vl;
+          split8(V.vv[c][dt], vh, vl);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
+        } else {
+          uint4 u;
+          u.x = V.vv[c][dt][0] | ((uint32_t)V.vv[c][dt][1] << 16);
+          u.y = V.vv[c][dt][2] | ((uint32_t)V.vv[c][dt][3] << 16);
+          u.z = V.vv[c][dt][4] | ((uint32_t)V.vv[c][dt][5] << 16);
+          u.w = V.vv[c][dt][6] | ((uint32_t)V.vv[c][dt][7] << 16);
+          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, u);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
         }
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
-        if constexpr (F32) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
       }
-    }
+  };
+
+  // two K register sets: tile n + 1's K (clamped to the last tile) loads
+  // while tile n computes; one V set
+  auto kload = [&](KTile<DT, D>& T, int n) __attribute__((always_inline)) {
+    int lim;
+    const int64_t o = tile_rows(n, lim);
+    T.load(kp + o, lim, C, half, c32);
+  };
+  auto vload = [&](VTile<DT, D>& V, int n) __attribute__((always_inline)) {
+    int lim;
+    const int64_t o = tile_rows(n, lim);
+    V.load(vp + o, lim, C, half, c32);
+  };
+  KTile<DT, D> KA, KB;
+  VTile<DT, D> V;
+  kload(KA, 0);
+#pragma unroll 1
+  for (int n = 0; n < nt; n += 2) {
+    vload(V, n);
+    kload(KB, n + 1 < nt ? n + 1 : n);
+    consume(KA, V, n);
+    if (n + 1 >= nt) break;
+    vload(V, n + 1);
+    kload(KA, n + 2 < nt ? n + 2 : n + 1);
+    consume(KB, V, n + 1);
   }
+
+  // 1 / sum per query (both halves' partial sums), broadcast like alpha
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  if (half == 0) reinterpret_cast<float*>(bc)[c32] = lt > 0.f ? 1.0f / lt : 0.f;
+  __syncthreads();
+  float4 r4[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) r4[g] = bc[2 * g + half];
   // O element v of lane (dim 32 dt + c32, half): query (v % 4) + 8 (v / 4) + 4 half
+  float* yt = p.y + base + t0 * C;
+  const int nq = (int)(p.L - t0 < 32 ? p.L - t0 : 32);
 #pragma unroll
   for (int dt = 0; dt < DTL; ++dt) {
     const int dim = 32 * dt + c32;
     if (dim >= D) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t t = t0 + (v & 3) + 8 * (v >> 2) + 4 * half;
-      if (t < p.L) {
-        float* yp = p.y + (rowbase + t) * p.C + hoff + dim;
-        *yp = ACC ? *yp + o[dt][v] : o[dt][v];
+    for (int g = 0; g < 4; ++g) {
+      const float rg[4] = {r4[g].x, r4[g].y, r4[g].z, r4[g].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i + 8 * g + 4 * half;
+        if (r < nq) yt[(uint32_t)r * (uint32_t)C + dim] = o[dt][4 * g + i] * rg[i];
       }
     }
   }
+}
+
+// Head sizes up to 64 fit two waves per SIMD in registers; 128 takes one.
+template <int DT, int D>
+__global__ __launch_bounds__(64, 2) void k_local_attn(LocalParams p) {
+  local_attn<DT, D>(p);
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_local_attn_wide(LocalParams p) {
+  local_attn<DT, 128>(p);
 }
 
 // Chunked mix, y only, single-level blocks: y[b][t][pair] += yblk[b][pair]

@@ -665,7 +665,9 @@ int launch_final_r(const FinalParams& p, bool fuse, bool pre, int64_t B, hipStre
     if (fuse && p.CP2 % 32 == 0) {  // CP2 <= 256 holds whenever fuse does
       const dim3 grid((unsigned)(B * p.M)), block((unsigned)(2 * p.CP2));
       if (p.yblk != nullptr)  // chunked mix (post-norm only)
-        hipLaunchKernelGGL((k_final_split<R, DT, false, true>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((k_final_split<R, DT, false, 1>), grid, block, 0, st, p);
+      else if (p.yloc != nullptr)  // local branch (post-norm only)
+        hipLaunchKernelGGL((k_final_split<R, DT, false, 2>), grid, block, 0, st, p);
       else if (pre)
         hipLaunchKernelGGL((k_final_split<R, DT, true>), grid, block, 0, st, p);
       else
@@ -723,47 +725,52 @@ int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
 }
 
 // The windowed-attention branch over q, k, v of shape s into y (binary32
-// [B][L][H][D]); acc adds it to what y holds.
-template <int DT, bool ACC>
+// [B][L][H][D]).
+template <int DT>
 int launch_local_d(const LocalParams& p, int64_t D, dim3 grid, hipStream_t st) {
   switch (D) {
-    case 16: hipLaunchKernelGGL((k_local_attn<DT, 16, ACC>), grid, dim3(64), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((k_local_attn<DT, 32, ACC>), grid, dim3(64), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_local_attn<DT, 64, ACC>), grid, dim3(64), 0, st, p); break;
-    case 128: hipLaunchKernelGGL((k_local_attn<DT, 128, ACC>), grid, dim3(64), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_local_attn<DT, 16>), grid, dim3(64), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_local_attn<DT, 32>), grid, dim3(64), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_local_attn<DT, 64>), grid, dim3(64), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((k_local_attn_wide<DT>), grid, dim3(64), 0, st, p); break;
     default: return SPECTRE_EUNSUPPORTED;
   }
   SPECTRE_LAUNCH_CHECK("L_local");
   return SPECTRE_OK;
 }
 
+// Head sizes the kernel is built for; item counts and offsets that fit its
+// 32-bit arithmetic.
 bool local_shape_ok(const Shape& s) {
   if (s.D != 16 && s.D != 32 && s.D != 64 && s.D != 128) return false;
+  if (s.L > (int64_t(1) << 30)) return false;
   const int64_t nitem = (s.L + 31) / 32 * s.H * s.B;
-  return nitem <= (int64_t)(UINT32_MAX / 64);
+  return nitem <= (int64_t)(INT32_MAX / 64);
 }
 
 int launch_local(const void* q, const void* k, const void* v, float* y, const Shape& s,
-                 const Local& lw, bool acc, hipStream_t st) {
+                 const Local& lw, hipStream_t st) {
   if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
   LocalParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.y = y;
-  p.B = s.B;
   p.L = s.L;
+  p.B = (int)s.B;
   p.H = (int)s.H;
   p.C = (int)s.C;
-  p.WL = std::min<int64_t>(lw.wl, s.L - 1);
-  p.WR = std::min<int64_t>(lw.wr, s.L - 1);
-  p.scale = (float)(1.0 / std::sqrt((double)s.D));
+  p.WL = (int)std::min<int64_t>(lw.wl, s.L - 1);
+  p.WR = (int)std::min<int64_t>(lw.wr, s.L - 1);
+  p.scale2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
   const dim3 grid((unsigned)((s.L + 31) / 32 * s.H * s.B));
-  if (s.dtype == SPECTRE_F32)
-    return acc ? launch_local_d<IN_F32, true>(p, s.D, grid, st)
-               : launch_local_d<IN_F32, false>(p, s.D, grid, st);
-  return acc ? launch_local_d<IN_BF16, true>(p, s.D, grid, st)
-             : launch_local_d<IN_BF16, false>(p, s.D, grid, st);
+  return s.dtype == SPECTRE_F32 ? launch_local_d<IN_F32>(p, s.D, grid, st)
+                                : launch_local_d<IN_BF16>(p, s.D, grid, st);
+}
+
+// Bytes of the local branch's output (binary32 y_loc) in the workspace.
+size_t local_bytes(const Shape& s, const Local* local) {
+  return local ? 256 + (size_t)s.N * 4 : 0;
 }
 
 // B, the LDS pass, for shape s / plan pl: the column transforms, the
@@ -859,17 +866,25 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   if (rc) return rc;
   const bool want_out = out != nullptr;
   void* ws = nullptr;
-  const size_t wsb = workspace_for(s, pl, want_out) + chunk_bytes(s, chunk);
+  const size_t wsb = workspace_for(s, pl, want_out) + chunk_bytes(s, chunk) + local_bytes(s, local);
   if (wsb) {
     rc = get_workspace(dev, wsb, &ws);
     if (rc) return rc;
   }
+  // local branch: y_loc after the rest, computed first and added by the norm
+  float2* yloc = local ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
+                                                   ((workspace_for(s, pl, want_out) + 255) & ~(size_t)255))
+                       : nullptr;
   // chunked mix: the block means of q, k, v and the block term, after the rest
   float2* dc = chunk ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
                                                  ((workspace_for(s, pl, want_out) + 255) & ~(size_t)255))
                      : nullptr;
   float2* yblk = chunk ? dc + 3 * s.B * s.CP2 : nullptr;
   trace_call_begin(st);
+  if (local) {
+    rc = launch_local(q, k, v, reinterpret_cast<float*>(yloc), s, *local, st);
+    if (rc) return rc;
+  }
   const int64_t CP2 = s.CP2;
   const int64_t pairs = s.B * s.L * CP2;  // complex elements per tensor
   const int in_kind = s.dtype == SPECTRE_F32 ? IN_F32 : IN_BF16;
@@ -977,10 +992,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     n.eps = eps;
     n.yblk = yblk;  // chunked mix: the block term joins y here
     n.Lb = s.L;
-    if (local) {  // local branch: added to y before the norm
-      rc = launch_local(q, k, v, reinterpret_cast<float*>(ws), s, *local, true, st);
-      if (rc) return rc;
-    }
+    n.yloc = yloc;  // local branch: joins y here
     return launch_norm(n, s.dtype, pre, st);
   }
 
@@ -997,7 +1009,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     rc = strided_inv(pl.L2, c2, st);
     if (rc) return rc;
   }
-  const bool fuse = want_out && fused_norm_ok(CP2) && !local;
+  const bool fuse = want_out && fused_norm_ok(CP2);
   FinalParams f{};
   f.U = U;
   f.x = x;
@@ -1010,6 +1022,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   f.inv_c = inv_c;
   f.eps = eps;
   f.yblk = yblk;  // chunked mix: the block term joins y in C1
+  f.yloc = fuse ? yloc : nullptr;  // local branch: joins y in the fused C1, else in the norm
   // y for a separate LayerNorm: k's spectrum region is free once B has run
   float* ybuf = want_out ? reinterpret_cast<float*>(T + pairs) : y;
   if (fuse) {
@@ -1020,10 +1033,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   f.out = ybuf;
   rc = launch_final<IN_F32>(pl.L1, f, false, false, s.B, st);
   if (rc || !want_out) return rc;
-  if (local) {  // local branch: added to y before the norm
-    rc = launch_local(q, k, v, ybuf, s, *local, true, st);
-    if (rc) return rc;
-  }
+
   NormParams n{};
   n.y = reinterpret_cast<const float2*>(ybuf);
   n.x = x;
@@ -1034,6 +1044,7 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
   n.CP2 = CP2;
   n.inv_c = inv_c;
   n.eps = eps;
+  n.yloc = yloc;
   return launch_norm(n, s.dtype, pre, st);
 }
 
@@ -1204,7 +1215,7 @@ int spectre_mix_local_attention(const void* q, const void* k, const void* v, flo
     if (overlaps(y, (size_t)s.N * 4, p, tb)) return SPECTRE_EINVAL;
   std::lock_guard<std::mutex> lock(g_mu);
   trace_call_begin(stream);
-  return launch_local(q, k, v, y, s, Local{win_left, win_right}, false, stream);
+  return launch_local(q, k, v, y, s, Local{win_left, win_right}, stream);
 }
 
 size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D, int dtype,

@@ -187,8 +187,10 @@ int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const flo
  * spectre_mix_local_attention).  Arguments, layout, ownership and errors as
  * spectre_mix_fwd, plus win_left, win_right >= 0 (else SPECTRE_EINVAL; a
  * window longer than the sequence is clipped to it), and D must be 16, 32,
- * 64 or 128 (else SPECTRE_EUNSUPPORTED).  The workspace is that of
- * spectre_mix_fwd (spectre_mix_workspace_bytes).
+ * 64 or 128 (else SPECTRE_EUNSUPPORTED).  The library's workspace is that
+ * of spectre_mix_fwd (spectre_mix_workspace_bytes) plus 256 + 4 * B * L * H
+ * * D bytes for y_loc, which the branch writes first and the LayerNorm pass
+ * adds.
  */
 int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,
                           const float* gate, const float* gamma, const float* beta, void* out,

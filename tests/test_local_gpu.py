@@ -107,6 +107,7 @@ MIX_CASES = [
     (1, 16384, 2, 32, 0, 3000, 128, 128),  # two-level plan, window 256
     (1, 16384, 8, 64, 1, 4097, 64, 63),    # bfloat16, LDS-copy B kernel
     (1, 98304, 1, 32, 0, 49153, 100, 0),   # three-level plan (32 x 3 x 1024), one-sided
+    (1, 49152, 8, 64, 1, 12289, 128, 0),   # 48 x 1024: the split fused inverse adds y_loc, bf16
 ]
 
 
