@@ -59,11 +59,12 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(name: str, w, gate_kind: int = 0) -> int:
+def kernel_bytes(name: str, w, gate_kind: int = 0, local: bool = False) -> int:
     """Algorithmic HBM bytes of one launch of a pass: every tensor element the
     pass must read or write once (inputs, the spectra it exchanges, outputs,
     the kept gate bins).  A complex gate has 8 bytes per bin, so its gate and
-    gate-table bytes double."""
+    gate-table bytes double.  With the local branch the pass that normalises
+    also reads y_loc (4 bytes per element)."""
     N = w.N
     s = w.elem_bytes
     spec = 4 * N  # one tensor's spectrum as binary32 complex channel pairs
@@ -88,14 +89,15 @@ def kernel_bytes(name: str, w, gate_kind: int = 0) -> int:
         return 3 * spec + spec + gate
     if name == "C2_inv_strided":
         return 2 * spec
+    yl = 4 * N if local else 0
     if name == "C1_inv_norm":
-        return spec + 2 * N * s + 8 * w.C
+        return spec + 2 * N * s + 8 * w.C + yl
     if name == "C1_inv":
         return 2 * spec
     if name == "LN_norm":
-        return spec + 2 * N * s + 8 * w.C
-    if name == "L_local":  # q, k, v read once; y (binary32) read and written
-        return 3 * N * s + 8 * N
+        return spec + 2 * N * s + 8 * w.C + yl
+    if name == "L_local":  # q, k, v read once; y_loc (binary32) written
+        return 3 * N * s + 4 * N
     raise KeyError(name)
 
 
@@ -249,7 +251,7 @@ def run_bench(args):
     nl = launches[dom]
     # the chunked mix transforms blocks of F tokens: the passes follow that plan
     wk = w if not F else dataclasses.replace(w, B=w.B * (w.L // F), L=F, keep_bins=F // 2 + 1)
-    dom_bytes = kernel_bytes(dom, wk, gk) / nl  # per launch
+    dom_bytes = kernel_bytes(dom, wk, gk, local=bool(win)) / nl  # per launch
     avg_ms = per_kernel[dom] / nl
     achieved = dom_bytes / (avg_ms * 1e-3) / 1e9
     traffic = traffic_for(dom, w) if gk == 0 and no == 0 and not F and not win else None
@@ -258,6 +260,8 @@ def run_bench(args):
                 "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
                 "avg_ms": round(avg_ms, 5), "launches_per_call": nl}
     mb = model_bytes(w)
+    if win:  # the branch reads q, k, v again and sends y_loc through HBM once
+        mb += 3 * w.N * w.elem_bytes + 8 * w.N
     whole = {"model_bytes": mb,
              "model_GBps": round(mb / (ms_per_step * 1e-3) / 1e9, 1),
              "model_frac": round(mb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -1591,8 +1591,13 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
 // t - WL <= j <= t + WR inside the sequence, scores (q_t . k_j) / sqrt(D),
 // softmax over those keys, y_loc[t] = sum_j p_j v_j.
 //
-// One wave per (32-query tile, head, batch element), one pass over the key
-// tiles of 32 with the running-max softmax.  Both products run on MFMA
+// One workgroup of four waves per (128-query block, head, batch element).
+// The block's key range goes through LDS in tiles of 32 keys, each tile
+// loaded once from HBM / L2 by all 256 lanes, converted to bfloat16 once and
+// read by every wave whose queries' windows reach it; the next tile's loads
+// are in flight while the current one is used (two LDS buffers, one barrier
+// per tile).  Each wave (32 queries) makes one pass over its tiles with the
+// running-max softmax.  Both products run on MFMA
 // (v_mfma_f32_32x32x16_bf16, binary32 accumulation):
 //   S^T (32 keys x 32 queries) = K_tile (keys x D) . Q_tile^T (D x queries):
 //     lane l supplies K[key l % 32][16 kc + 8 (l / 32) + e] and
@@ -1602,17 +1607,28 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
 //     need only its own lane and lane l ^ 32;
 //   O (32 queries x D) += P (queries x keys) . V (keys x D), per 32-dim tile:
 //     the lane's 16 probabilities are already the A operand of the two
-//     16-key chunks (key order within the contraction is free), and lane l
-//     supplies V[key][dim l % 32] for the same key order; O's element v of
-//     lane l is query (v % 4) + 8 (v / 4) + 4 (l / 32), dim l % 32, so the
-//     per-query rescale and the final 1 / sum reach O through 32 floats of
-//     LDS.
+//     16-key chunks (the key order inside a contraction is free), so LDS
+//     holds V transposed with its keys in that order (slot 16 c + 8 h + e
+//     is key (e % 4) + 8 (e / 4) + 16 c + 4 h): lane l reads its dim's 8
+//     keys as one 16-byte row piece.  O's element v of lane l is query
+//     (v % 4) + 8 (v / 4) + 4 (l / 32), dim l % 32, so the per-query
+//     rescale and the final 1 / sum reach O through 32 floats of LDS.
 // Binary32 storage splits every operand into bfloat16 hi + lo (hi the
 // rounded value, lo the rounded remainder: 16 significant bits) and sums the
 // products hi.hi + hi.lo + lo.hi; bfloat16 storage is exact in hi, and only
-// the probabilities are split.  The next key tile's loads are issued before
-// the current tile's arithmetic (two register sets, rows clamped into the
-// sequence so that every load is unconditional; clamped keys are masked).
+// the probabilities are split.  Rows past the sequence end are clamped to
+// its last row on load (every load unconditional) and masked in the scores.
+
+// max / sum of a value over lanes l and l ^ 32 (one v_permlane32_swap:
+// each half receives the other half's value)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 
 struct LocalParams {
   const void* q;
@@ -1627,173 +1643,227 @@ struct LocalParams {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// hi = f rounded to bfloat16 (pairs converted together), lo = the remainder
-// f - hi (exact in binary32) rounded to bfloat16.
-__device__ __forceinline__ void split8(const float (&f)[8], bf16x8_t& hi, bf16x8_t& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x2_t a = {f[2 * i], f[2 * i + 1]};
-    h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
-    const f32x2_t r = {f[2 * i] - __uint_as_float(h[i] << 16),
-                       f[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u)};
-    l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-  }
-  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+// Two binary32 values rounded to bfloat16 (one conversion), packed.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// One key tile's raw operands for one lane: K (KTile) and V (VTile).
+// hi = rounded pair, lo = the rounded remainders (f - hi is exact in binary32).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// LDS image of one staged key tile, in bfloat16 elements: PL planes (hi,
+// and lo for binary32 storage) of K [32 keys][KS] and of V^T [D dims][VS].
+// The row strides (16 bytes of padding) make the 16-byte reads of 8
+// consecutive lanes fall on distinct banks; in V^T row d the four 8-slot
+// blocks are rotated by (d / 8) % 4 blocks, which spreads the staging
+// writes of 16 dims that share a slot over the banks (8-way conflicts
+// without it).
 template <int DT, int D>
-struct LocalShape {
-  static constexpr bool F32 = DT != IN_BF16;
-  static constexpr int KC = D / 16;
-  static constexpr int DTL = (D + 31) / 32;
-  using E = typename std::conditional<F32, float, uint16_t>::type;
+struct LocalLds {
+  static constexpr int PL = DT != IN_BF16 ? 2 : 1;
+  static constexpr int KS = D + 8;
+  static constexpr int VS = 40;
+  static constexpr int KPL = 32 * KS;
+  static constexpr int VPL = D * VS;
+  static constexpr int TILE = PL * (KPL + VPL);
+  static constexpr int UNITS = 4 * D;             // staging units per tensor and tile
+  static constexpr int UPT = (UNITS + 255) / 256;  // per thread
+  // element offset of V^T slot `slot` (16 c + 8 h + e) in dim row `dim`
+  __device__ static constexpr int vslot(int dim, int slot) {
+    return dim * VS + ((slot + 8 * (dim >> 3)) & 31);
+  }
 };
 
-// kt: element (key j0, dim 0) of this head (wave-uniform); keys j0 + r with
-// r > lim are clamped to j0 + lim (the sequence end).  This lane's K row is
-// j0 + c32, dims 16 kc + 8 half + e (two float4, or one uint4 of bfloat16).
+// One thread's share of a tile in flight, as raw words: K units (8
+// consecutive dims of a key) and V units (4 consecutive dims of two keys
+// that are neighbours in the V^T slot order).
 template <int DT, int D>
-struct KTile {
-  using S = LocalShape<DT, D>;
-  float4 kf[S::F32 ? S::KC : 1][2];
-  uint4 kb[S::F32 ? 1 : S::KC];
-  // (byte offsets from the uniform base in 32 bits: the loads take the
-  // scalar-base form)
-  __device__ __forceinline__ void load(const typename S::E* kt, int lim, int C, int half, int c32) {
-    constexpr uint32_t es = sizeof(typename S::E);
-    const char* kb0 = reinterpret_cast<const char*>(kt);
-    const uint32_t kro = (__umul24((uint32_t)(c32 < lim ? c32 : lim), (uint32_t)C) + 8 * half) * es;
+struct LocalStage {
+  using LL = LocalLds<DT, D>;
+  static constexpr bool F32 = DT != IN_BF16;
+  static constexpr int KW = F32 ? 2 : 1;  // 16-byte words per K unit
+  uint4 kw[LL::UPT][KW];
+  uint4 vw[LL::UPT][2];  // rows key, key + 1 (bfloat16: .x, .y used)
+
+  // kt, vt: bytes of (key j0, dim 0) of this head; keys j0 + r, r > lim,
+  // read row j0 + lim
+  __device__ __forceinline__ void load(const char* kt, const char* vt, int lim, int C, int tid) {
+    constexpr uint32_t es = F32 ? 4 : 2;
 #pragma unroll
-    for (int kc = 0; kc < S::KC; ++kc) {
-      if constexpr (S::F32) {
-        kf[kc][0] = *reinterpret_cast<const float4*>(kb0 + kro + 64 * kc);
-        kf[kc][1] = *reinterpret_cast<const float4*>(kb0 + kro + 64 * kc + 16);
-      } else {
-        kb[kc] = *reinterpret_cast<const uint4*>(kb0 + kro + 32 * kc);
+    for (int i = 0; i < LL::UPT; ++i) {
+      const int u = tid + 256 * i;
+      if (LL::UNITS % 256 != 0 && u >= LL::UNITS) continue;
+      {
+        const int key = u / (D / 8), c8 = u % (D / 8);
+        const uint32_t o = (__umul24((uint32_t)(key < lim ? key : lim), (uint32_t)C) + 8 * c8) * es;
+#pragma unroll
+        for (int x = 0; x < KW; ++x) kw[i][x] = *reinterpret_cast<const uint4*>(kt + o + 16 * x);
+      }
+      {
+        const int kp = u / (D / 4), quad = u % (D / 4);
+        const int pos = 2 * kp;  // slot 16 c + 8 h + e, e even
+        const int key = (pos & 3) + 8 * ((pos >> 2) & 1) + 16 * (pos >> 4) + 4 * ((pos >> 3) & 1);
+        const int k0 = key < lim ? key : lim, k1 = key + 1 < lim ? key + 1 : lim;
+        const uint32_t o0 = (__umul24((uint32_t)k0, (uint32_t)C) + 4 * quad) * es;
+        const uint32_t o1 = (__umul24((uint32_t)k1, (uint32_t)C) + 4 * quad) * es;
+        if constexpr (F32) {
+          vw[i][0] = *reinterpret_cast<const uint4*>(vt + o0);
+          vw[i][1] = *reinterpret_cast<const uint4*>(vt + o1);
+        } else {
+          const uint2 a = *reinterpret_cast<const uint2*>(vt + o0);
+          const uint2 c = *reinterpret_cast<const uint2*>(vt + o1);
+          vw[i][0] = make_uint4(a.x, a.y, 0u, 0u);
+          vw[i][1] = make_uint4(c.x, c.y, 0u, 0u);
+        }
       }
     }
   }
-};
 
-// vt as kt; this lane's V keys are (e % 4) + 8 (e / 4) + 16 c + 4 half at
-// dim 32 dt + c32 (dims at or above D read dim 0).
-template <int DT, int D>
-struct VTile {
-  using S = LocalShape<DT, D>;
-  typename S::E vv[2][S::DTL][8];
-  __device__ __forceinline__ void load(const typename S::E* vt, int lim, int C, int half, int c32) {
-    using E = typename S::E;
-    constexpr uint32_t es = sizeof(E);
-    const char* vb0 = reinterpret_cast<const char*>(vt);
+  __device__ __forceinline__ void store(uint16_t* t, int tid) const {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = (e & 3) + 8 * (e >> 2) + 16 * c + 4 * half;
-        const uint32_t vro = __umul24((uint32_t)(r < lim ? r : lim), (uint32_t)C);
-#pragma unroll
-        for (int dt = 0; dt < S::DTL; ++dt) {
-          const uint32_t dim = 32 * dt + c32 < D ? 32 * dt + c32 : 0;
-          vv[c][dt][e] = *reinterpret_cast<const E*>(vb0 + (vro + dim) * es);
+    for (int i = 0; i < LL::UPT; ++i) {
+      const int u = tid + 256 * i;
+      if (LL::UNITS % 256 != 0 && u >= LL::UNITS) continue;
+      {
+        const int key = u / (D / 8), c8 = u % (D / 8);
+        uint16_t* kd = t + key * LL::KS + 8 * c8;
+        if constexpr (F32) {
+          const uint4 a = kw[i][0], c = kw[i][1];
+          uint4 h, l;
+          split_pair(__uint_as_float(a.x), __uint_as_float(a.y), h.x, l.x);
+          split_pair(__uint_as_float(a.z), __uint_as_float(a.w), h.y, l.y);
+          split_pair(__uint_as_float(c.x), __uint_as_float(c.y), h.z, l.z);
+          split_pair(__uint_as_float(c.z), __uint_as_float(c.w), h.w, l.w);
+          *reinterpret_cast<uint4*>(kd) = h;
+          *reinterpret_cast<uint4*>(kd + LL::KPL) = l;
+        } else {
+          *reinterpret_cast<uint4*>(kd) = kw[i][0];
         }
       }
+      {
+        const int kp = u / (D / 4), quad = u % (D / 4);
+        // the 4 dims share one 8-dim group, so one rotated slot for all
+        uint16_t* vd = t + LL::PL * LL::KPL + LL::vslot(4 * quad, 2 * kp);
+        const uint4 a = vw[i][0], c = vw[i][1];
+        if constexpr (F32) {
+          const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            uint32_t h, l;
+            split_pair(__uint_as_float(aw[d]), __uint_as_float(cw[d]), h, l);
+            *reinterpret_cast<uint32_t*>(vd + d * LL::VS) = h;
+            *reinterpret_cast<uint32_t*>(vd + d * LL::VS + LL::VPL) = l;
+          }
+        } else {
+          // dims 4 quad + d of keys key, key + 1: low / high halves of the words
+          *reinterpret_cast<uint32_t*>(vd) = (a.x & 0xffffu) | (c.x << 16);
+          *reinterpret_cast<uint32_t*>(vd + LL::VS) = (a.x >> 16) | (c.x & 0xffff0000u);
+          *reinterpret_cast<uint32_t*>(vd + 2 * LL::VS) = (a.y & 0xffffu) | (c.y << 16);
+          *reinterpret_cast<uint32_t*>(vd + 3 * LL::VS) = (a.y >> 16) | (c.y & 0xffff0000u);
+        }
+      }
+    }
   }
 };
 
 template <int DT, int D>
 __device__ __forceinline__ void local_attn(const LocalParams& p) {
-  using S = LocalShape<DT, D>;
-  using E = typename S::E;
-  constexpr bool F32 = S::F32;
-  constexpr int KC = S::KC;
-  constexpr int DTL = S::DTL;
+  using LL = LocalLds<DT, D>;
+  using E = typename std::conditional<DT != IN_BF16, float, uint16_t>::type;
+  constexpr bool F32 = DT != IN_BF16;
+  constexpr int KC = D / 16;
+  constexpr int DTL = (D + 31) / 32;
   constexpr float NEG = -1e30f;  // running max before any key: exp2 of masked scores stays 0
-  __shared__ float4 bc[8];       // 32 per-query factors, broadcast to O's layout
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LL::TILE];
+  __shared__ float4 bc[4][8];  // per wave: 32 per-query factors, broadcast to O's layout
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, c32 = lane & 31;
   const int C = p.C;
-  // work item: 32-query tile fastest, then head, then batch element; the
+  // work item: 128-query block fastest, then head, then batch element; the
   // workgroups one XCD runs (every 8th) take a contiguous run of items, so
-  // the overlapping key windows of neighbouring tiles meet in one L2
-  const int ntq = (int)((p.L + 31) / 32);
-  const int nitem = ntq * p.H * p.B;
+  // the overlapping key ranges of neighbouring blocks meet in one L2
+  const int nblk = (int)((p.L + 127) / 128);
+  const int nitem = nblk * p.H * p.B;
   int w = blockIdx.x;
   if (nitem % 8 == 0) w = (w % 8) * (nitem / 8) + w / 8;
-  const int64_t t0 = (int64_t)(w % ntq) * 32;
-  const int h = (w / ntq) % p.H;
-  const int b = w / (ntq * p.H);
+  const int blk = w % nblk;
+  const int64_t T0 = (int64_t)blk * 128;
+  const int h = (w / nblk) % p.H;
+  const int b = w / (nblk * p.H);
   const int64_t base = (int64_t)b * p.L * C + (int64_t)h * D;  // element (b, t = 0, h, 0)
   const int64_t Lm1 = p.L - 1;
-  const E* qp = reinterpret_cast<const E*>(p.q) + base;
-  const E* kp = reinterpret_cast<const E*>(p.k) + base;
-  const E* vp = reinterpret_cast<const E*>(p.v) + base;
+  const char* kp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.k) + base);
+  const char* vp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.v) + base);
 
-  // Q^T operand: query t0 + c32 (clamped; outputs of clamped queries are not stored)
-  const int64_t tq = t0 + c32;
+  // the block's keys, in tiles of 32 from jlo
+  const int64_t jlo = T0 - p.WL < 0 ? 0 : T0 - p.WL;
+  const int64_t jend = T0 + 127 + p.WR < Lm1 ? T0 + 127 + p.WR : Lm1;
+  const int nt = (int)((jend - jlo + 32) / 32);
+  auto stage_load = [&](LocalStage<DT, D>& st, int n) __attribute__((always_inline)) {
+    const int j0 = (int)jlo + 32 * n;
+    const int lim = (int)(Lm1 - j0 < 31 ? Lm1 - j0 : 31);
+    const int64_t o = (int64_t)j0 * C * (int64_t)sizeof(E);
+    st.load(kp + o, vp + o, lim, C, tid);
+  };
+
+  // this wave's 32 queries and the keys their windows reach
+  const int64_t Tw = T0 + 32 * wave;
+  const bool wave_on = Tw < p.L;
+  const int64_t wlo = Tw - p.WL < 0 ? 0 : Tw - p.WL;
+  const int64_t whi = Tw + 31 + p.WR < Lm1 ? Tw + 31 + p.WR : Lm1;
+  const int64_t tq = Tw + c32;  // this lane's query (clamped on load; not stored past L)
   bf16x8_t qh[KC], ql[KC];
   {
-    const E* qt = qp + t0 * C;
-    const int lim = (int)(Lm1 - t0);
-    const uint32_t o = (uint32_t)(c32 < lim ? c32 : lim) * (uint32_t)C + 8 * half;
+    const int64_t row = tq < Lm1 ? tq : Lm1;
+    const E* qr = reinterpret_cast<const E*>(p.q) + base + row * C + 8 * half;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       if constexpr (F32) {
-        const float4* src = reinterpret_cast<const float4*>(qt + o + 16 * kc);
-        const float4 a = src[0], c = src[1];
-        const float f[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        split8(f, qh[kc], ql[kc]);
+        const float4 a = *reinterpret_cast<const float4*>(qr + 16 * kc);
+        const float4 c = *reinterpret_cast<const float4*>(qr + 16 * kc + 4);
+        uint4 hh, ll;
+        split_pair(a.x, a.y, hh.x, ll.x);
+        split_pair(a.z, a.w, hh.y, ll.y);
+        split_pair(c.x, c.y, hh.z, ll.z);
+        split_pair(c.z, c.w, hh.w, ll.w);
+        qh[kc] = __builtin_bit_cast(bf16x8_t, hh);
+        ql[kc] = __builtin_bit_cast(bf16x8_t, ll);
       } else {
-        qh[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qt + o + 16 * kc));
+        qh[kc] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qr + 16 * kc));
       }
     }
   }
-
-  const int64_t jlo = t0 - p.WL < 0 ? 0 : t0 - p.WL;
-  const int64_t jend = t0 + 31 + p.WR < Lm1 ? t0 + 31 + p.WR : Lm1;
-  const int nt = (int)((jend - jlo + 32) / 32);
   // key j is in this lane's query window iff 0 <= j - tq + WL <= qwin_hi
   // (for a clamped query tq >= L the test admits any key: its row is not stored)
   const int qwin_hi = (int)((tq + p.WR < Lm1 ? tq + p.WR : Lm1) - tq + p.WL);
   const int d0 = (int)(jlo - tq + p.WL) + 4 * half;  // key (v%4)+8(v/4) of tile 0, relative
+  float* bw = reinterpret_cast<float*>(bc[wave]);
 
   float m = NEG, lsum = 0.f;
   f32x16_t o[DTL];
 #pragma unroll
   for (int dt = 0; dt < DTL; ++dt) o[dt] = f32x16_t{};
 
-  // tile n: its V loads go out first, then the next tile's K loads (K of
-  // tile n was loaded during tile n - 1); V is needed only after the scores
-  // and the softmax update, so both overlap the arithmetic
-  auto tile_rows = [&](int n, int& lim) __attribute__((always_inline)) {
-    // wave-uniform: kept in scalar registers so the loads take a scalar base
-    const int j0 = __builtin_amdgcn_readfirstlane((int)jlo + 32 * n);
-    lim = __builtin_amdgcn_readfirstlane((int)(Lm1 - j0 < 31 ? Lm1 - j0 : 31));
-    return (int64_t)j0 * C;
-  };
-  auto consume = [&](const KTile<DT, D>& T, const VTile<DT, D>& V, int n)
-                     __attribute__((always_inline)) {
+  auto compute = [&](const uint16_t* t, int n) __attribute__((always_inline)) {
     // scores
     f32x16_t acc = {};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
+      const uint16_t* kr = t + c32 * LL::KS + 16 * kc + 8 * half;
+      const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(kr);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kc], acc, 0, 0, 0);
       if constexpr (F32) {
-        const float f[8] = {T.kf[kc][0].x, T.kf[kc][0].y, T.kf[kc][0].z, T.kf[kc][0].w,
-                            T.kf[kc][1].x, T.kf[kc][1].y, T.kf[kc][1].z, T.kf[kc][1].w};
-        bf16x8_t kh, kl;
-        split8(f, kh, kl);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[kc], acc, 0, 0, 0);
+        const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(kr + LL::KPL);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[kc], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kc], acc, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, T.kb[kc]),
-                                                      qh[kc], acc, 0, 0, 0);
       }
     }
     // mask (window of this lane's query, and the sequence end), tile max
@@ -1803,124 +1873,147 @@ __device__ __forceinline__ void local_attn(const LocalParams& p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int d = dn + (v & 3) + 8 * (v >> 2);
-      s[v] = (uint32_t)d <= (uint32_t)qwin_hi ? acc[v] * p.scale2 : -INFINITY;
+      s[v] = (uint32_t)d <= (uint32_t)qwin_hi ? acc[v] : -INFINITY;
       tmax = fmaxf(tmax, s[v]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
+    tmax = xhalf_max(tmax) * p.scale2;  // both halves of the query, scaled (scale2 > 0)
+    // The reference max m moves only when a score exceeds it by more than
+    // 2^8 (so p <= 256): O and the sum are rescaled on those tiles only, and
+    // the result, O / sum, does not depend on which m was used.
+    const bool up = tmax > m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;
+      m = up ? tmax : m;
+      lsum *= alpha;
+      // O's queries' alpha through this wave's own LDS slots (the wave's LDS
+      // accesses run in order, so no barrier)
+      if (half == 0) bw[c32] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      float4 a4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) a4[g] = reinterpret_cast<const float4*>(bw)[2 * g + half];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dt = 0; dt < DTL; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          o[dt][4 * g + 0] *= a4[g].x;
+          o[dt][4 * g + 1] *= a4[g].y;
+          o[dt][4 * g + 2] *= a4[g].z;
+          o[dt][4 * g + 3] *= a4[g].w;
+        }
+    }
     float ps = 0.f;
     bf16x8_t ph[2], pl[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float pv = __builtin_amdgcn_exp2f(s[v] - mn);
-      ps += pv;
-      const __bf16 hi = (__bf16)pv;
-      ph[v >> 3][v & 7] = hi;
-      pl[v >> 3][v & 7] = (__bf16)(pv - (float)hi);
-    }
-    lsum = lsum * alpha + ps;
-    // rescale O by its queries' alpha
-    if (half == 0) reinterpret_cast<float*>(bc)[c32] = alpha;
-    __syncthreads();
-    float4 a4[4];
+    for (int c = 0; c < 2; ++c) {
+      uint32_t hp[4], lp[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) a4[g] = bc[2 * g + half];
-    __syncthreads();
-#pragma unroll
-    for (int dt = 0; dt < DTL; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        o[dt][4 * g + 0] *= a4[g].x;
-        o[dt][4 * g + 1] *= a4[g].y;
-        o[dt][4 * g + 2] *= a4[g].z;
-        o[dt][4 * g + 3] *= a4[g].w;
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i], p.scale2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i + 1], p.scale2, -m));
+        ps += p0 + p1;
+        split_pair(p0, p1, hp[i], lp[i]);
       }
+      ph[c] = __builtin_bit_cast(bf16x8_t, make_uint4(hp[0], hp[1], hp[2], hp[3]));
+      pl[c] = __builtin_bit_cast(bf16x8_t, make_uint4(lp[0], lp[1], lp[2], lp[3]));
+    }
+    lsum += ps;
     // O += P V
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int dt = 0; dt < DTL; ++dt) {
-        if constexpr (F32) {
-          bf16x8_t vh, vl;
-          split8(V.vv[c][dt], vh, vl);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
-        } else {
-          uint4 u;
-          u.x = V.vv[c][dt][0] | ((uint32_t)V.vv[c][dt][1] << 16);
-          u.y = V.vv[c][dt][2] | ((uint32_t)V.vv[c][dt][3] << 16);
-          u.z = V.vv[c][dt][4] | ((uint32_t)V.vv[c][dt][5] << 16);
-          u.w = V.vv[c][dt][6] | ((uint32_t)V.vv[c][dt][7] << 16);
-          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, u);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
+        const int dim = 32 * dt + c32;
+        bf16x8_t vh = {}, vl = {};
+        const uint16_t* vr = t + LL::PL * LL::KPL + LL::vslot(dim < D ? dim : 0, 16 * c + 8 * half);
+        if (D % 32 == 0 || dim < D) {
+          vh = *reinterpret_cast<const bf16x8_t*>(vr);
+          if constexpr (F32) vl = *reinterpret_cast<const bf16x8_t*>(vr + LL::VPL);
         }
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vh, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
+        if constexpr (F32) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
       }
   };
 
-  // two K register sets: tile n + 1's K (clamped to the last tile) loads
-  // while tile n computes; one V set
-  auto kload = [&](KTile<DT, D>& T, int n) __attribute__((always_inline)) {
-    int lim;
-    const int64_t o = tile_rows(n, lim);
-    T.load(kp + o, lim, C, half, c32);
+  // Two register sets of staged loads: tile n + 2's loads go out at the
+  // start of iteration n and reach LDS at the end of iteration n + 1, so
+  // two iterations of work cover their latency; two LDS buffers.
+  // Loads and stores are unconditional (tile indices clamped to the last
+  // tile; a store past the last tile fills a buffer nobody reads again), so
+  // the wait before each store counts only the older set.
+  LocalStage<DT, D> sa, sb;
+  // Odd blocks walk their tiles from the last to the first: the tiles a
+  // block shares with its neighbours (half of its range at window 128) are
+  // then read by the two within about two steps of each other, while they
+  // are still in L2 (the softmax does not depend on the order).
+  const bool rev = blk & 1;
+  auto tile_of = [&](int n) { return rev ? nt - 1 - n : n; };
+  stage_load(sa, tile_of(0));
+  stage_load(sb, tile_of(nt > 1 ? 1 : 0));
+  sa.store(lds, tid);
+  __syncthreads();
+  auto iteration = [&](int n, LocalStage<DT, D>& next2, const LocalStage<DT, D>& next1)
+                       __attribute__((always_inline)) {
+    stage_load(next2, tile_of(n + 2 < nt ? n + 2 : nt - 1));
+    const int tn = tile_of(n);
+    const int64_t k0 = jlo + 32 * tn;
+    if (wave_on && k0 <= whi && k0 + 31 >= wlo) compute(lds + (n & 1) * LL::TILE, tn);
+    next1.store(lds + ((n + 1) & 1) * LL::TILE, tid);
+    __syncthreads();
   };
-  auto vload = [&](VTile<DT, D>& V, int n) __attribute__((always_inline)) {
-    int lim;
-    const int64_t o = tile_rows(n, lim);
-    V.load(vp + o, lim, C, half, c32);
-  };
-  KTile<DT, D> KA, KB;
-  VTile<DT, D> V;
-  kload(KA, 0);
 #pragma unroll 1
   for (int n = 0; n < nt; n += 2) {
-    vload(V, n);
-    kload(KB, n + 1 < nt ? n + 1 : n);
-    consume(KA, V, n);
+    iteration(n, sa, sb);  // sa held tile n (stored), now takes tile n + 2; sb holds n + 1
     if (n + 1 >= nt) break;
-    vload(V, n + 1);
-    kload(KA, n + 2 < nt ? n + 2 : n + 1);
-    consume(KB, V, n + 1);
+    iteration(n + 1, sb, sa);
   }
+  if (!wave_on) return;
 
   // 1 / sum per query (both halves' partial sums), broadcast like alpha
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
-  if (half == 0) reinterpret_cast<float*>(bc)[c32] = lt > 0.f ? 1.0f / lt : 0.f;
-  __syncthreads();
+  const float lt = xhalf_sum(lsum);
+  if (half == 0) bw[c32] = lt > 0.f ? 1.0f / lt : 0.f;
+  __builtin_amdgcn_wave_barrier();
   float4 r4[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) r4[g] = bc[2 * g + half];
+  for (int g = 0; g < 4; ++g) r4[g] = reinterpret_cast<const float4*>(bw)[2 * g + half];
   // O element v of lane (dim 32 dt + c32, half): query (v % 4) + 8 (v / 4) + 4 half
-  float* yt = p.y + base + t0 * C;
-  const int nq = (int)(p.L - t0 < 32 ? p.L - t0 : 32);
+  float* yt = p.y + base + Tw * C;
+  const int nq = (int)(p.L - Tw < 32 ? p.L - Tw : 32);
+  auto store = [&](bool full) __attribute__((always_inline)) {
 #pragma unroll
-  for (int dt = 0; dt < DTL; ++dt) {
-    const int dim = 32 * dt + c32;
-    if (dim >= D) continue;
+    for (int dt = 0; dt < DTL; ++dt) {
+      const int dim = 32 * dt + c32;
+      if (D % 32 != 0 && dim >= D) continue;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float rg[4] = {r4[g].x, r4[g].y, r4[g].z, r4[g].w};
+      for (int g = 0; g < 4; ++g) {
+        const float rg[4] = {r4[g].x, r4[g].y, r4[g].z, r4[g].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i + 8 * g + 4 * half;
-        if (r < nq) yt[(uint32_t)r * (uint32_t)C + dim] = o[dt][4 * g + i] * rg[i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = i + 8 * g + 4 * half;
+          if (full || r < nq)
+            *reinterpret_cast<float*>(reinterpret_cast<char*>(yt) + ((uint32_t)r * (uint32_t)C + dim) * 4u) =
+                o[dt][4 * g + i] * rg[i];
+        }
       }
     }
-  }
+  };
+  if (nq == 32)
+    store(true);  // every query of the wave is in the sequence: no per-row test
+  else
+    store(false);
 }
 
-// Head sizes up to 64 fit two waves per SIMD in registers; 128 takes one.
+// Head sizes up to 64 fit three workgroups per CU (registers and LDS);
+// 128 takes what its registers allow.
 template <int DT, int D>
-__global__ __launch_bounds__(64, 2) void k_local_attn(LocalParams p) {
+__global__ __launch_bounds__(256, 3) void k_local_attn(LocalParams p) {
   local_attn<DT, D>(p);
 }
 
 template <int DT>
-__global__ __launch_bounds__(64) void k_local_attn_wide(LocalParams p) {
+__global__ __launch_bounds__(256) void k_local_attn_wide(LocalParams p) {
   local_attn<DT, 128>(p);
 }
 
