@@ -49,6 +49,8 @@ ATTN_CASES = [
     (2, 4096, 8, 64, 0, 64, 64),      # 4096-token shape, window 128
     (1, 4096, 8, 64, 1, 128, 128),    # window 256, bfloat16
     (3, 33, 3, 32, 0, 0, 40),         # B * tiles * H not a multiple of 8, look-ahead only
+    (1, 300, 2, 128, 1, 64, 64),      # head size 128 in bfloat16
+    (2, 520, 4, 16, 1, 200, 31),      # head size 16 in bfloat16, ragged, asymmetric
 ]
 
 
