@@ -1673,33 +1673,35 @@ struct LocalLds {
   static constexpr int KPL = 32 * KS;
   static constexpr int VPL = D * VS;
   static constexpr int TILE = PL * (KPL + VPL);
-  static constexpr int UNITS = 4 * D;             // staging units per tensor and tile
-  static constexpr int UPT = (UNITS + 255) / 256;  // per thread
+  static constexpr int UNITS = 4 * D;  // staging units per tensor and tile
   // element offset of V^T slot `slot` (16 c + 8 h + e) in dim row `dim`
   __device__ static constexpr int vslot(int dim, int slot) {
     return dim * VS + ((slot + 8 * (dim >> 3)) & 31);
   }
 };
 
-// One thread's share of a tile in flight, as raw words: K units (8
-// consecutive dims of a key) and V units (4 consecutive dims of two keys
-// that are neighbours in the V^T slot order).
-template <int DT, int D>
+// One thread's share of a tile in flight, as raw words: K units of 8
+// consecutive dims of one key, V units of 4 consecutive dims of two keys
+// that are neighbours in the V^T slot order.  NT threads stage a tile;
+// units past the last repeat the last one (every load unconditional, so
+// the wait before a store counts only older loads).
+template <int DT, int D, int NT>
 struct LocalStage {
   using LL = LocalLds<DT, D>;
   static constexpr bool F32 = DT != IN_BF16;
   static constexpr int KW = F32 ? 2 : 1;  // 16-byte words per K unit
-  uint4 kw[LL::UPT][KW];
-  uint4 vw[LL::UPT][2];  // rows key, key + 1 (bfloat16: .x, .y used)
+  static constexpr int UPT = (LL::UNITS + NT - 1) / NT;
+  uint4 kw[UPT][KW];
+  uint4 vw[UPT][2];  // rows key, key + 1 (bfloat16: .x, .y used)
 
   // kt, vt: bytes of (key j0, dim 0) of this head; keys j0 + r, r > lim,
   // read row j0 + lim
   __device__ __forceinline__ void load(const char* kt, const char* vt, int lim, int C, int tid) {
     constexpr uint32_t es = F32 ? 4 : 2;
 #pragma unroll
-    for (int i = 0; i < LL::UPT; ++i) {
-      const int u = tid + 256 * i;
-      if (LL::UNITS % 256 != 0 && u >= LL::UNITS) continue;
+    for (int i = 0; i < UPT; ++i) {
+      int u = tid + NT * i;
+      u = u < LL::UNITS ? u : LL::UNITS - 1;
       {
         const int key = u / (D / 8), c8 = u % (D / 8);
         const uint32_t o = (__umul24((uint32_t)(key < lim ? key : lim), (uint32_t)C) + 8 * c8) * es;
@@ -1726,26 +1728,29 @@ struct LocalStage {
     }
   }
 
+  // 8 dims of a row, split (binary32 storage) or copied, into planes at d
+  __device__ static void put_row8(uint16_t* d, uint4 a, uint4 c) {
+    if constexpr (F32) {
+      uint4 h, l;
+      split_pair(__uint_as_float(a.x), __uint_as_float(a.y), h.x, l.x);
+      split_pair(__uint_as_float(a.z), __uint_as_float(a.w), h.y, l.y);
+      split_pair(__uint_as_float(c.x), __uint_as_float(c.y), h.z, l.z);
+      split_pair(__uint_as_float(c.z), __uint_as_float(c.w), h.w, l.w);
+      *reinterpret_cast<uint4*>(d) = h;
+      *reinterpret_cast<uint4*>(d + LL::KPL) = l;
+    } else {
+      *reinterpret_cast<uint4*>(d) = a;
+    }
+  }
+
   __device__ __forceinline__ void store(uint16_t* t, int tid) const {
 #pragma unroll
-    for (int i = 0; i < LL::UPT; ++i) {
-      const int u = tid + 256 * i;
-      if (LL::UNITS % 256 != 0 && u >= LL::UNITS) continue;
+    for (int i = 0; i < UPT; ++i) {
+      int u = tid + NT * i;
+      u = u < LL::UNITS ? u : LL::UNITS - 1;
       {
-        const int key = u / (D / 8), c8 = u % (D / 8);
-        uint16_t* kd = t + key * LL::KS + 8 * c8;
-        if constexpr (F32) {
-          const uint4 a = kw[i][0], c = kw[i][1];
-          uint4 h, l;
-          split_pair(__uint_as_float(a.x), __uint_as_float(a.y), h.x, l.x);
-          split_pair(__uint_as_float(a.z), __uint_as_float(a.w), h.y, l.y);
-          split_pair(__uint_as_float(c.x), __uint_as_float(c.y), h.z, l.z);
-          split_pair(__uint_as_float(c.z), __uint_as_float(c.w), h.w, l.w);
-          *reinterpret_cast<uint4*>(kd) = h;
-          *reinterpret_cast<uint4*>(kd + LL::KPL) = l;
-        } else {
-          *reinterpret_cast<uint4*>(kd) = kw[i][0];
-        }
+        const int row = u / (D / 8), c8 = u % (D / 8);
+        put_row8(t + row * LL::KS + 8 * c8, kw[i][0], kw[i][KW - 1]);
       }
       {
         const int kp = u / (D / 4), quad = u % (D / 4);
@@ -1773,57 +1778,28 @@ struct LocalStage {
   }
 };
 
+// One wave's 32 queries: their Q operands, running max and sum, and O.
 template <int DT, int D>
-__device__ __forceinline__ void local_attn(const LocalParams& p) {
+struct LocalWave {
   using LL = LocalLds<DT, D>;
   using E = typename std::conditional<DT != IN_BF16, float, uint16_t>::type;
-  constexpr bool F32 = DT != IN_BF16;
-  constexpr int KC = D / 16;
-  constexpr int DTL = (D + 31) / 32;
-  constexpr float NEG = -1e30f;  // running max before any key: exp2 of masked scores stays 0
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LL::TILE];
-  __shared__ float4 bc[4][8];  // per wave: 32 per-query factors, broadcast to O's layout
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int half = lane >> 5, c32 = lane & 31;
-  const int C = p.C;
-  // work item: 128-query block fastest, then head, then batch element; the
-  // workgroups one XCD runs (every 8th) take a contiguous run of items, so
-  // the overlapping key ranges of neighbouring blocks meet in one L2
-  const int nblk = (int)((p.L + 127) / 128);
-  const int nitem = nblk * p.H * p.B;
-  int w = blockIdx.x;
-  if (nitem % 8 == 0) w = (w % 8) * (nitem / 8) + w / 8;
-  const int blk = w % nblk;
-  const int64_t T0 = (int64_t)blk * 128;
-  const int h = (w / nblk) % p.H;
-  const int b = w / (nblk * p.H);
-  const int64_t base = (int64_t)b * p.L * C + (int64_t)h * D;  // element (b, t = 0, h, 0)
-  const int64_t Lm1 = p.L - 1;
-  const char* kp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.k) + base);
-  const char* vp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.v) + base);
-
-  // the block's keys, in tiles of 32 from jlo
-  const int64_t jlo = T0 - p.WL < 0 ? 0 : T0 - p.WL;
-  const int64_t jend = T0 + 127 + p.WR < Lm1 ? T0 + 127 + p.WR : Lm1;
-  const int nt = (int)((jend - jlo + 32) / 32);
-  auto stage_load = [&](LocalStage<DT, D>& st, int n) __attribute__((always_inline)) {
-    const int j0 = (int)jlo + 32 * n;
-    const int lim = (int)(Lm1 - j0 < 31 ? Lm1 - j0 : 31);
-    const int64_t o = (int64_t)j0 * C * (int64_t)sizeof(E);
-    st.load(kp + o, vp + o, lim, C, tid);
-  };
-
-  // this wave's 32 queries and the keys their windows reach
-  const int64_t Tw = T0 + 32 * wave;
-  const bool wave_on = Tw < p.L;
-  const int64_t wlo = Tw - p.WL < 0 ? 0 : Tw - p.WL;
-  const int64_t whi = Tw + 31 + p.WR < Lm1 ? Tw + 31 + p.WR : Lm1;
-  const int64_t tq = Tw + c32;  // this lane's query (clamped on load; not stored past L)
+  static constexpr bool F32 = DT != IN_BF16;
+  static constexpr int KC = D / 16;
+  static constexpr int DTL = (D + 31) / 32;
+  static constexpr float NEG = -1e30f;  // max before any key: exp2 of masked scores stays 0
   bf16x8_t qh[KC], ql[KC];
-  {
-    const int64_t row = tq < Lm1 ? tq : Lm1;
-    const E* qr = reinterpret_cast<const E*>(p.q) + base + row * C + 8 * half;
+  float m, lsum;
+  f32x16_t o[DTL];
+
+  __device__ void reset() {
+    m = NEG;
+    lsum = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DTL; ++dt) o[dt] = f32x16_t{};
+  }
+
+  // Q^T operand from global memory: qr = this lane's row at dim 8 half
+  __device__ void q_global(const E* qr) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       if constexpr (F32) {
@@ -1841,18 +1817,14 @@ __device__ __forceinline__ void local_attn(const LocalParams& p) {
       }
     }
   }
-  // key j is in this lane's query window iff 0 <= j - tq + WL <= qwin_hi
-  // (for a clamped query tq >= L the test admits any key: its row is not stored)
-  const int qwin_hi = (int)((tq + p.WR < Lm1 ? tq + p.WR : Lm1) - tq + p.WL);
-  const int d0 = (int)(jlo - tq + p.WL) + 4 * half;  // key (v%4)+8(v/4) of tile 0, relative
-  float* bw = reinterpret_cast<float*>(bc[wave]);
 
-  float m = NEG, lsum = 0.f;
-  f32x16_t o[DTL];
-#pragma unroll
-  for (int dt = 0; dt < DTL; ++dt) o[dt] = f32x16_t{};
-
-  auto compute = [&](const uint16_t* t, int n) __attribute__((always_inline)) {
+  // One staged key tile t.  Element v of the lane's scores is key
+  // (v % 4) + 8 (v / 4) of the tile's keys plus 4 half; it is in the query's
+  // window iff (dn + (v % 4) + 8 (v / 4)) <= qwin as unsigned numbers (the
+  // caller offsets dn so that the window starts at 0).  bw: this wave's 32
+  // floats of LDS.
+  __device__ void step(const uint16_t* t, int dn, uint32_t qwin, float scale2, float* bw, int half,
+                       int c32) {
     // scores
     f32x16_t acc = {};
 #pragma unroll
@@ -1866,17 +1838,16 @@ __device__ __forceinline__ void local_attn(const LocalParams& p) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[kc], acc, 0, 0, 0);
       }
     }
-    // mask (window of this lane's query, and the sequence end), tile max
+    // mask, tile max
     float s[16];
     float tmax = NEG;
-    const int dn = d0 + 32 * n;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int d = dn + (v & 3) + 8 * (v >> 2);
-      s[v] = (uint32_t)d <= (uint32_t)qwin_hi ? acc[v] : -INFINITY;
+      s[v] = (uint32_t)d <= qwin ? acc[v] : -INFINITY;
       tmax = fmaxf(tmax, s[v]);
     }
-    tmax = xhalf_max(tmax) * p.scale2;  // both halves of the query, scaled (scale2 > 0)
+    tmax = xhalf_max(tmax) * scale2;  // both halves of the query, scaled (scale2 > 0)
     // The reference max m moves only when a score exceeds it by more than
     // 2^8 (so p <= 256): O and the sum are rescaled on those tiles only, and
     // the result, O / sum, does not depend on which m was used.
@@ -1910,8 +1881,8 @@ __device__ __forceinline__ void local_attn(const LocalParams& p) {
       uint32_t hp[4], lp[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i], p.scale2, -m));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i + 1], p.scale2, -m));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i], scale2, -m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * i + 1], scale2, -m));
         ps += p0 + p1;
         split_pair(p0, p1, hp[i], lp[i]);
       }
@@ -1935,86 +1906,140 @@ __device__ __forceinline__ void local_attn(const LocalParams& p) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[c], vh, o[dt], 0, 0, 0);
         if constexpr (F32) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[c], vl, o[dt], 0, 0, 0);
       }
+  }
+
+  // O / sum into y: yt = row of the wave's first query (dim 0 of the head),
+  // nq of its 32 queries inside the sequence.
+  __device__ void finish(float* yt, int nq, int C, float* bw, int half, int c32) {
+    const float lt = xhalf_sum(lsum);  // both halves' partial sums
+    if (half == 0) bw[c32] = lt > 0.f ? 1.0f / lt : 0.f;
+    __builtin_amdgcn_wave_barrier();
+    float4 r4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) r4[g] = reinterpret_cast<const float4*>(bw)[2 * g + half];
+    __builtin_amdgcn_wave_barrier();
+    // O element v of lane (dim 32 dt + c32, half): query (v % 4) + 8 (v / 4) + 4 half.
+    // Addresses: a wave-uniform row pointer per (g, i) plus one per-lane
+    // byte offset, so no per-store 64-bit offsets stay live.
+    const uint32_t laneoff = (__umul24(4u * half, (uint32_t)C) + c32) * 4u;
+    auto store = [&](bool full) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float rg[4] = {r4[g].x, r4[g].y, r4[g].z, r4[g].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const char* rowp = reinterpret_cast<const char*>(yt) + (size_t)(i + 8 * g) * C * 4;
+          if (!full && i + 8 * g + 4 * half >= nq) continue;
+#pragma unroll
+          for (int dt = 0; dt < DTL; ++dt) {
+            if (D % 32 != 0 && 32 * dt + c32 >= D) continue;
+            *reinterpret_cast<float*>(const_cast<char*>(rowp) + laneoff + 128 * dt) = o[dt][4 * g + i] * rg[i];
+          }
+        }
+      }
+    };
+    if (nq == 32)
+      store(true);  // every query of the wave is in the sequence: no per-row test
+    else
+      store(false);
+  }
+};
+
+// One workgroup of four waves per (128-query block, head, batch element);
+// the block's key range streams through LDS once.
+template <int DT, int D>
+__device__ __forceinline__ void local_block(const LocalParams& p) {
+  using LL = LocalLds<DT, D>;
+  using E = typename std::conditional<DT != IN_BF16, float, uint16_t>::type;
+  using Stage = LocalStage<DT, D, 256>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * LL::TILE];
+  __shared__ float4 bc[4][8];  // per wave: 32 per-query factors, broadcast to O's layout
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave: uniform
+  const int half = lane >> 5, c32 = lane & 31;
+  const int C = p.C;
+  // work item: 128-query block fastest, then head, then batch element; the
+  // workgroups one XCD runs (every 8th) take a contiguous run of items, so
+  // the overlapping key ranges of neighbouring blocks meet in one L2
+  const int nblk = (int)((p.L + 127) / 128);
+  const int nitem = nblk * p.H * p.B;
+  int w = blockIdx.x;
+  if (nitem % 8 == 0) w = (w % 8) * (nitem / 8) + w / 8;
+  const int blk = w % nblk;
+  const int64_t T0 = (int64_t)blk * 128;
+  const int h = (w / nblk) % p.H;
+  const int b = w / (nblk * p.H);
+  const int64_t base = (int64_t)b * p.L * C + (int64_t)h * D;  // element (b, t = 0, h, 0)
+  const int64_t Lm1 = p.L - 1;
+  const char* kp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.k) + base);
+  const char* vp = reinterpret_cast<const char*>(reinterpret_cast<const E*>(p.v) + base);
+
+  // the block's keys, in tiles of 32 from jlo
+  const int64_t jlo = T0 - p.WL < 0 ? 0 : T0 - p.WL;
+  const int64_t jend = T0 + 127 + p.WR < Lm1 ? T0 + 127 + p.WR : Lm1;
+  const int nt = (int)((jend - jlo + 32) / 32);
+  auto stage_load = [&](Stage& st, int n) __attribute__((always_inline)) {
+    const int j0 = (int)jlo + 32 * n;
+    const int lim = (int)(Lm1 - j0 < 31 ? Lm1 - j0 : 31);
+    const int64_t o = (int64_t)j0 * C * (int64_t)sizeof(E);
+    st.load(kp + o, vp + o, lim, C, tid);
   };
 
-  // Two register sets of staged loads: tile n + 2's loads go out at the
-  // start of iteration n and reach LDS at the end of iteration n + 1, so
-  // two iterations of work cover their latency; two LDS buffers.
-  // Loads and stores are unconditional (tile indices clamped to the last
-  // tile; a store past the last tile fills a buffer nobody reads again), so
-  // the wait before each store counts only the older set.
-  LocalStage<DT, D> sa, sb;
+  // this wave's 32 queries and the keys their windows reach
+  const int64_t Tw = T0 + 32 * wave;
+  const bool wave_on = Tw < p.L;
+  const int64_t wlo = Tw - p.WL < 0 ? 0 : Tw - p.WL;
+  const int64_t whi = Tw + 31 + p.WR < Lm1 ? Tw + 31 + p.WR : Lm1;
+  const int64_t tq = Tw + c32;  // this lane's query (clamped on load; not stored past L)
+  LocalWave<DT, D> W;
+  W.reset();
+  W.q_global(reinterpret_cast<const E*>(p.q) + base + (tq < Lm1 ? tq : Lm1) * C + 8 * half);
+  // key j is in this lane's query window iff 0 <= j - tq + WL <= qwin
+  // (for a clamped query tq >= L the test admits any key: its row is not stored)
+  const uint32_t qwin = (uint32_t)((tq + p.WR < Lm1 ? tq + p.WR : Lm1) - tq + p.WL);
+  const int d0 = (int)(jlo - tq + p.WL) + 4 * half;  // key (v%4)+8(v/4) of tile 0, relative
+  float* bw = reinterpret_cast<float*>(bc[wave]);
+
+  // Tile n + 1's loads go out at the start of iteration n and reach the
+  // other LDS buffer at its end, after the arithmetic on tile n.  Loads and
+  // stores are unconditional (the tile index clamped to the last tile; a
+  // store past the last tile fills a buffer nobody reads again), so the
+  // wait before each store counts only that set.
   // Odd blocks walk their tiles from the last to the first: the tiles a
   // block shares with its neighbours (half of its range at window 128) are
   // then read by the two within about two steps of each other, while they
   // are still in L2 (the softmax does not depend on the order).
   const bool rev = blk & 1;
   auto tile_of = [&](int n) { return rev ? nt - 1 - n : n; };
-  stage_load(sa, tile_of(0));
-  stage_load(sb, tile_of(nt > 1 ? 1 : 0));
-  sa.store(lds, tid);
+  Stage st;
+  stage_load(st, tile_of(0));
+  st.store(lds, tid);
   __syncthreads();
-  auto iteration = [&](int n, LocalStage<DT, D>& next2, const LocalStage<DT, D>& next1)
-                       __attribute__((always_inline)) {
-    stage_load(next2, tile_of(n + 2 < nt ? n + 2 : nt - 1));
+#pragma unroll 1
+  for (int n = 0; n < nt; ++n) {
+    stage_load(st, tile_of(n + 1 < nt ? n + 1 : nt - 1));
     const int tn = tile_of(n);
     const int64_t k0 = jlo + 32 * tn;
-    if (wave_on && k0 <= whi && k0 + 31 >= wlo) compute(lds + (n & 1) * LL::TILE, tn);
-    next1.store(lds + ((n + 1) & 1) * LL::TILE, tid);
+    if (wave_on && k0 <= whi && k0 + 31 >= wlo)
+      W.step(lds + (n & 1) * LL::TILE, d0 + 32 * tn, qwin, p.scale2, bw, half, c32);
+    st.store(lds + ((n + 1) & 1) * LL::TILE, tid);
     __syncthreads();
-  };
-#pragma unroll 1
-  for (int n = 0; n < nt; n += 2) {
-    iteration(n, sa, sb);  // sa held tile n (stored), now takes tile n + 2; sb holds n + 1
-    if (n + 1 >= nt) break;
-    iteration(n + 1, sb, sa);
   }
   if (!wave_on) return;
-
-  // 1 / sum per query (both halves' partial sums), broadcast like alpha
-  const float lt = xhalf_sum(lsum);
-  if (half == 0) bw[c32] = lt > 0.f ? 1.0f / lt : 0.f;
-  __builtin_amdgcn_wave_barrier();
-  float4 r4[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) r4[g] = reinterpret_cast<const float4*>(bw)[2 * g + half];
-  // O element v of lane (dim 32 dt + c32, half): query (v % 4) + 8 (v / 4) + 4 half
-  float* yt = p.y + base + Tw * C;
-  const int nq = (int)(p.L - Tw < 32 ? p.L - Tw : 32);
-  auto store = [&](bool full) __attribute__((always_inline)) {
-#pragma unroll
-    for (int dt = 0; dt < DTL; ++dt) {
-      const int dim = 32 * dt + c32;
-      if (D % 32 != 0 && dim >= D) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float rg[4] = {r4[g].x, r4[g].y, r4[g].z, r4[g].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = i + 8 * g + 4 * half;
-          if (full || r < nq)
-            *reinterpret_cast<float*>(reinterpret_cast<char*>(yt) + ((uint32_t)r * (uint32_t)C + dim) * 4u) =
-                o[dt][4 * g + i] * rg[i];
-        }
-      }
-    }
-  };
-  if (nq == 32)
-    store(true);  // every query of the wave is in the sequence: no per-row test
-  else
-    store(false);
+  W.finish(p.y + base + Tw * C, (int)(p.L - Tw < 32 ? p.L - Tw : 32), C, bw, half, c32);
 }
 
-// Head sizes up to 64 fit three workgroups per CU (registers and LDS);
-// 128 takes what its registers allow.
+// Head sizes up to 64 fit three workgroups per CU in registers and LDS
+// (four with bfloat16 storage, which needs no split of K and V); 128 takes
+// what its registers allow.
 template <int DT, int D>
-__global__ __launch_bounds__(256, 3) void k_local_attn(LocalParams p) {
-  local_attn<DT, D>(p);
+__global__ __launch_bounds__(256, DT == IN_BF16 ? 4 : 3) void k_local_attn(LocalParams p) {
+  local_block<DT, D>(p);
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_local_attn_wide(LocalParams p) {
-  local_attn<DT, 128>(p);
+  local_block<DT, 128>(p);
 }
 
 // Chunked mix, y only, single-level blocks: y[b][t][pair] += yblk[b][pair]

@@ -727,7 +727,8 @@ int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
 // The windowed-attention branch over q, k, v of shape s into y (binary32
 // [B][L][H][D]).
 template <int DT>
-int launch_local_d(const LocalParams& p, int64_t D, dim3 grid, hipStream_t st) {
+int launch_block_d(const LocalParams& p, int64_t D, hipStream_t st) {
+  const dim3 grid((unsigned)((p.L + 127) / 128 * p.H * p.B));
   switch (D) {
     case 16: hipLaunchKernelGGL((k_local_attn<DT, 16>), grid, dim3(256), 0, st, p); break;
     case 32: hipLaunchKernelGGL((k_local_attn<DT, 32>), grid, dim3(256), 0, st, p); break;
@@ -739,13 +740,13 @@ int launch_local_d(const LocalParams& p, int64_t D, dim3 grid, hipStream_t st) {
   return SPECTRE_OK;
 }
 
-// Head sizes the kernel is built for; item counts and offsets that fit its
-// 32-bit arithmetic.
+// Head sizes the kernels are built for; item counts and offsets that fit
+// their 32-bit arithmetic.
 bool local_shape_ok(const Shape& s) {
   if (s.D != 16 && s.D != 32 && s.D != 64 && s.D != 128) return false;
   if (s.L > (int64_t(1) << 30)) return false;
-  const int64_t nitem = (s.L + 127) / 128 * s.H * s.B;
-  return nitem <= (int64_t)(INT32_MAX / 256);
+  const int64_t nitem = (s.L + 31) / 32 * s.H * s.B;
+  return nitem <= (int64_t)(INT32_MAX / 1024);
 }
 
 int launch_local(const void* q, const void* k, const void* v, float* y, const Shape& s,
@@ -763,9 +764,8 @@ int launch_local(const void* q, const void* k, const void* v, float* y, const Sh
   p.WL = (int)std::min<int64_t>(lw.wl, s.L - 1);
   p.WR = (int)std::min<int64_t>(lw.wr, s.L - 1);
   p.scale2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
-  const dim3 grid((unsigned)((s.L + 127) / 128 * s.H * s.B));
-  return s.dtype == SPECTRE_F32 ? launch_local_d<IN_F32>(p, s.D, grid, st)
-                                : launch_local_d<IN_BF16>(p, s.D, grid, st);
+  return s.dtype == SPECTRE_F32 ? launch_block_d<IN_F32>(p, s.D, st)
+                                : launch_block_d<IN_BF16>(p, s.D, st);
 }
 
 // Bytes of the local branch's output (binary32 y_loc) in the workspace.
