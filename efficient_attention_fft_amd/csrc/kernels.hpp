@@ -2005,12 +2005,12 @@ __device__ __forceinline__ void local_block(const LocalParams& p) {
   // stores are unconditional (the tile index clamped to the last tile; a
   // store past the last tile fills a buffer nobody reads again), so the
   // wait before each store counts only that set.
-  // Odd blocks walk their tiles from the last to the first: the tiles a
-  // block shares with its neighbours (half of its range at window 128) are
-  // then read by the two within about two steps of each other, while they
-  // are still in L2 (the softmax does not depend on the order).
-  const bool rev = blk & 1;
-  auto tile_of = [&](int n) { return rev ? nt - 1 - n : n; };
+  // Even blocks start their walk 4 tiles in (one block's length): block b's
+  // tile 4 + s is block b + 1's tile s, so at window 128 (8 tiles) the two
+  // blocks that share a tile read it at the same step, once from HBM, and
+  // likewise for block b - 1 (the softmax does not depend on the order).
+  const int rot = (blk & 1) ? 0 : 4 % nt;
+  auto tile_of = [&](int n) { return n + rot < nt ? n + rot : n + rot - nt; };
   Stage st;
   stage_load(st, tile_of(0));
   st.store(lds, tid);
