@@ -134,27 +134,29 @@ def test_mix_with_local_branch_against_oracle(B, L, H, D, dt, keep, wl, wr):
     assert np.all(np.isfinite(got)) and err <= tol(w)
 
 
-def test_mix_with_local_branch_full_size_sampled():
-    """The 65536-token shape (binary32), window 128, in the launch
-    configuration the benchmark times: at sampled tokens the oracle's
-    spectral y, plus its windowed attention over each token's sub-sequence,
-    through its residual LayerNorm."""
+@pytest.mark.parametrize("wid,wl,wr", [(3, 64, 64), (4, 128, 128)])
+def test_mix_with_local_branch_full_size_sampled(wid, wl, wr):
+    """The 65536-token shapes (binary32, B = 1, window 128, the launch
+    configuration the benchmark times; bfloat16, B = 2, truncated, window
+    256): at sampled tokens of every batch element the oracle's spectral y,
+    plus its windowed attention over each token's sub-sequence, through its
+    residual LayerNorm."""
     import efficient_attention_fft_amd as sm
     t = torch()
-    w = workloads.WORKLOADS[3]
+    w = workloads.WORKLOADS[wid]
     inp = workloads.make_inputs(w)
-    wl = wr = 64
-    toks = np.array(sorted(set([0, 5, 64, 65535, 32768] +
-                               list(np.random.default_rng(7).integers(0, w.L, 27)))), np.int64)
+    picks = [0, 5, 64, w.L - 1, w.L // 2] + list(np.random.default_rng(7).integers(0, w.L, 27))
+    toks = np.array(sorted(set(b * w.L + int(p) for b in range(w.B) for p in picks)), np.int64)
     _, ref_y = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
                                          inp["gamma"], inp["beta"], w.keep_bins, toks,
                                          dtype=w.dtype, nthreads=oracle_threads())
     yl = np.empty_like(ref_y)
-    for i, tk in enumerate(toks):
+    for i, flat in enumerate(toks):
+        b, tk = divmod(int(flat), w.L)
         lo, hi = max(0, tk - wl), min(w.L, tk + wr + 1)
-        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[:, lo:hi] for n in "qkv"}
+        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[b:b + 1, lo:hi] for n in "qkv"}
         yl[i] = oracle.local_attention(sub["q"], sub["k"], sub["v"], wl, wr, dtype=w.dtype)[0, tk - lo]
-    xs = inp["x"].reshape(w.L, w.H, w.D)[toks]
+    xs = inp["x"].reshape(w.B * w.L, w.H, w.D)[toks]
     ref = oracle.layernorm_residual(ref_y + yl, xs, inp["gamma"], inp["beta"], dtype=w.dtype)
     q, k, v, x = (dev(inp[n]) for n in "qkvx")
     g, gam, bet = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
@@ -162,7 +164,7 @@ def test_mix_with_local_branch_full_size_sampled():
     sm.check(sm.spectre_mix_fwd_local(q, k, v, x, g, gam, bet, out, w.B, w.H, w.L, w.D,
                                       w.keep_bins, wl, wr, w.dtype))
     t.cuda.synchronize()
-    got = to_host_f64(out.view(w.L, w.C)[t.from_numpy(toks).cuda()], w.dtype).reshape(ref.shape)
+    got = to_host_f64(out.view(w.B * w.L, w.C)[t.from_numpy(toks).cuda()], w.dtype).reshape(ref.shape)
     err = np.abs(got - ref).max()
-    say("  out max-abs err %.3g over %d tokens" % (err, len(toks)))
+    say("  %s window %d/%d: out max-abs err %.3g over %d tokens" % (w.name, wl, wr, err, len(toks)))
     assert err <= tol(w)
