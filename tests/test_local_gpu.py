@@ -67,6 +67,31 @@ def test_local_attention_against_oracle(B, L, H, D, dt, wl, wr):
     assert np.all(np.isfinite(got)) and err <= y_tol(ref)
 
 
+def _sweep_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        L = int(rng.integers(1, 700))
+        cases.append((int(rng.integers(1, 3)), L, int(rng.integers(1, 5)),
+                      int(rng.choice([16, 32, 64, 128])), int(rng.integers(0, 2)),
+                      int(rng.integers(0, 300)), int(rng.integers(0, 300))))
+    return cases
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,wl,wr", _sweep_cases())
+def test_local_attention_sweep(B, L, H, D, dt, wl, wr):
+    """Seeded random shapes and windows (lengths not multiples of the 32-
+    or 128-token tiles, windows wider than the sequence, both dtypes, every
+    head size), against the oracle."""
+    import efficient_attention_fft_amd as sm
+    w = workloads.custom(700 + L, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=L // 2 + 1)
+    inp = workloads.make_inputs(w)
+    ref = oracle.local_attention(inp["q"], inp["k"], inp["v"], wl, wr, dtype=dt)
+    got = run_local(sm, inp, w, wl, wr)
+    err = np.abs(got - ref).max()
+    assert np.all(np.isfinite(got)) and err <= y_tol(ref), (err, y_tol(ref))
+
+
 def test_window_of_one_key_is_v():
     """win_left = win_right = 0: each query sees only itself, so y_loc = v, to
     the split-bfloat16 representation of v (hi + lo carries 16 significant
