@@ -114,6 +114,26 @@ def test_edge_shapes(B, L, H, D, dt, keep):
     check_full(w)
 
 
+def _sweep_cases(n=20, seed=4242):
+    """Seeded random supported shapes: L = 2^a 3^b (b <= 1), H * D even, any
+    keep_bins, both dtypes, at most about 2^22 elements per tensor."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        L = int(2 ** rng.integers(1, 17) * (3 if rng.random() < 0.3 else 1))
+        H, D, B = int(rng.integers(1, 9)), int(rng.integers(1, 65)), int(rng.integers(1, 4))
+        if (H * D) % 2 or B * L * H * D > 2 ** 22 or L > 3 * 2 ** 20:
+            continue
+        cases.append((B, L, H, D, int(rng.integers(0, 2)), int(rng.integers(0, L // 2 + 2))))
+    return cases
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep", _sweep_cases())
+def test_sweep_shapes(B, L, H, D, dt, keep):
+    w = workloads.custom(300 + L % 89, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=keep, affine=True)
+    check_full(w)
+
+
 @pytest.mark.timeout(600)
 def test_longest_supported_length():
     """L = 3 * 2^20, the longest length the library plans: 64 x 48 x 1024,
