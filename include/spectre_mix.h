@@ -239,9 +239,11 @@ int spectre_mix_release(void);
 
 /*
  * Per-kernel timing with HIP events (tracing).  After spectre_mix_trace_start,
- * each of the next `max_calls` calls to spectre_mix_fwd / spectre_mix_y also
- * records a HIP event on its own stream before its first kernel and after
- * each kernel it enqueues; nothing synchronises.  spectre_mix_trace_stop
+ * each of the next `max_calls` calls to a computing entry point (spectre_mix_fwd,
+ * spectre_mix_y and their _ex, _chunked and _local forms, and
+ * spectre_mix_local_attention) also records a HIP event on its own stream
+ * before its first kernel and after each kernel it enqueues; nothing
+ * synchronises.  spectre_mix_trace_stop
  * waits for those events, stops tracing, and reports per position k of the
  * calls' launch sequence: total_ms[k] = summed duration over the traced
  * calls, names[k * name_len ...] = the kernel's short NUL-terminated name;
