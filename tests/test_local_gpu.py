@@ -130,6 +130,7 @@ def test_local_attention_full_size_sampled():
 MIX_CASES = [
     # (B, L, H, D, dtype, keep_bins, win_left, win_right)
     (1, 256, 2, 16, 0, 129, 64, 64),       # single-level square kernel
+    (1, 1536, 2, 32, 1, 700, 64, 64),      # single-level generic LDS kernel (radix 3), bf16
     (2, 4096, 8, 64, 0, 2049, 64, 64),     # single-level generic LDS kernel, window 128
     (1, 16384, 2, 32, 0, 3000, 128, 128),  # two-level plan, window 256
     (1, 16384, 8, 64, 1, 4097, 64, 63),    # bfloat16, LDS-copy B kernel
