@@ -38,6 +38,10 @@ MUTANTS = {
     "local_window_right": ("const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;",
                            "const int64_t j1 = t + win_right + 1 > L - 1 ? L - 1 : t + win_right + 1;"),
     "local_not_normalised": ("y[qb + d] = acc / sum;", "y[qb + d] = acc;"),
+    "local_wrong_head": ("const int64_t kb = (b * L + j) * C + h * D;",
+                         "const int64_t kb = (b * L + j) * C + ((h + 1) % H) * D;"),
+    "local_window_left": ("const int64_t j0 = t - win_left < 0 ? 0 : t - win_left;",
+                          "const int64_t j0 = t - win_left + 1 < 0 ? 0 : t - win_left + 1;"),
     "inverse_scale_dropped": ("double re = bufq[t].re * invL, im = bufq[t].im * invL;",
                               "double re = bufq[t].re, im = bufq[t].im * invL;"),
     "truncation_inclusive": ("if (f < J->keep) {", "if (f <= J->keep) {"),

@@ -608,6 +608,24 @@ def test_local_attention_closed_forms():
     assert np.abs(yc[:, 0] - v64[:, 0]).max() == 0.0
 
 
+def test_local_attention_invariants():
+    """Shifting q, k, v along the sequence shifts y_loc away from the ends;
+    permuting the heads permutes y_loc's heads; q * c with k / c leaves
+    every score, so y_loc, unchanged."""
+    B, L, H, D = 1, 96, 3, 8
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    wl, wr, sh = 7, 5, 11
+    y = oracle.local_attention(q, k, v, wl, wr)
+    ys = oracle.local_attention(*(np.roll(a, sh, axis=1) for a in (q, k, v)), wl, wr)
+    inner = slice(wl + sh, L - wr)
+    assert np.abs(ys[:, inner] - np.roll(y, sh, axis=1)[:, inner]).max() <= 1e-12
+    perm = [2, 0, 1]
+    yp = oracle.local_attention(*(np.ascontiguousarray(a[:, :, perm]) for a in (q, k, v)), wl, wr)
+    assert np.abs(yp - y[:, :, perm]).max() <= 1e-12
+    yc = oracle.local_attention(q * 2.0, k * 0.5, v, wl, wr)
+    assert np.abs(yc - y).max() <= 1e-12
+
+
 def test_mix_with_local_branch_adds_the_two_outputs():
     B, L, H, D = 1, 64, 2, 4
     q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
