@@ -32,7 +32,7 @@ EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "s
            "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
            "spectre_mix_strerror", "spectre_mix_fwd_ex", "spectre_mix_y_ex",
            "spectre_mix_workspace_bytes_ex", "spectre_mix_fwd_chunked", "spectre_mix_y_chunked",
-           "spectre_mix_fwd_local", "spectre_mix_local_attention")
+           "spectre_mix_fwd_local", "spectre_mix_local_attention", "spectre_mix_fwd_local_ex")
 
 
 class SpectreError(RuntimeError):
@@ -91,6 +91,9 @@ def _load():
     lib.spectre_mix_fwd_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                           i64, i64, ci, vp]
     lib.spectre_mix_fwd_local.restype = ci
+    lib.spectre_mix_fwd_local_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                             i64, i64, i64, ci, ci, ci, vp]
+    lib.spectre_mix_fwd_local_ex.restype = ci
     lib.spectre_mix_local_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
                                                 vp]
     lib.spectre_mix_local_attention.restype = ci
@@ -183,6 +186,15 @@ def spectre_mix_fwd_local(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_b
     return _lib.spectre_mix_fwd_local(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
                                       _addr(gamma), _addr(beta), _addr(out), B, H, L, D, keep_bins,
                                       win_left, win_right, dtype, _stream(stream))
+
+
+def spectre_mix_fwd_local_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins,
+                             win_left, win_right, dtype, gate_kind, norm_order,
+                             stream=None) -> int:
+    return _lib.spectre_mix_fwd_local_ex(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
+                                         _addr(gamma), _addr(beta), _addr(out), B, H, L, D,
+                                         keep_bins, win_left, win_right, dtype, gate_kind,
+                                         norm_order, _stream(stream))
 
 
 def spectre_mix_local_attention(q, k, v, y, B, H, L, D, win_left, win_right, dtype,

@@ -666,7 +666,9 @@ int launch_final_r(const FinalParams& p, bool fuse, bool pre, int64_t B, hipStre
       const dim3 grid((unsigned)(B * p.M)), block((unsigned)(2 * p.CP2));
       if (p.yblk != nullptr)  // chunked mix (post-norm only)
         hipLaunchKernelGGL((k_final_split<R, DT, false, 1>), grid, block, 0, st, p);
-      else if (p.yloc != nullptr)  // local branch (post-norm only)
+      else if (p.yloc != nullptr && pre)  // local branch
+        hipLaunchKernelGGL((k_final_split<R, DT, true, 2>), grid, block, 0, st, p);
+      else if (p.yloc != nullptr)
         hipLaunchKernelGGL((k_final_split<R, DT, false, 2>), grid, block, 0, st, p);
       else if (pre)
         hipLaunchKernelGGL((k_final_split<R, DT, true>), grid, block, 0, st, p);
@@ -1167,15 +1169,16 @@ int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const flo
   return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream, &ch);
 }
 
-int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,
-                          const float* gate, const float* gamma, const float* beta, void* out,
-                          int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
-                          int64_t win_left, int64_t win_right, int dtype, hipStream_t stream) {
+int spectre_mix_fwd_local_ex(const void* q, const void* k, const void* v, const void* x,
+                             const float* gate, const float* gamma, const float* beta, void* out,
+                             int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                             int64_t win_left, int64_t win_right, int dtype, int gate_kind,
+                             int norm_order, hipStream_t stream) {
   if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
   if (win_left < 0 || win_right < 0) return SPECTRE_EINVAL;
   Shape s;
   Plan pl;
-  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl, gate_kind, norm_order);
   if (rc) return rc;
   if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
   const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
@@ -1186,6 +1189,15 @@ int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const voi
     if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
   const Local lw{win_left, win_right};
   return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream, nullptr, &lw);
+}
+
+int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,
+                          const float* gate, const float* gamma, const float* beta, void* out,
+                          int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                          int64_t win_left, int64_t win_right, int dtype, hipStream_t stream) {
+  return spectre_mix_fwd_local_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins,
+                                  win_left, win_right, dtype, SPECTRE_GATE_REAL, SPECTRE_NORM_POST,
+                                  stream);
 }
 
 int spectre_mix_local_attention(const void* q, const void* k, const void* v, float* y, int64_t B,

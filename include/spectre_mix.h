@@ -198,6 +198,19 @@ int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const voi
                           int64_t win_left, int64_t win_right, int dtype, hipStream_t stream);
 
 /*
+ * spectre_mix_fwd_local with a chosen gate kind and norm order (as
+ * spectre_mix_fwd_ex): SPECTRE_NORM_PRE gives out = x + LayerNorm(y + y_loc).
+ * spectre_mix_fwd_local(...) is spectre_mix_fwd_local_ex(..., SPECTRE_GATE_REAL,
+ * SPECTRE_NORM_POST, stream).  An unknown gate_kind or norm_order returns
+ * SPECTRE_EINVAL (nothing enqueued).
+ */
+int spectre_mix_fwd_local_ex(const void* q, const void* k, const void* v, const void* x,
+                             const float* gate, const float* gamma, const float* beta, void* out,
+                             int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                             int64_t win_left, int64_t win_right, int dtype, int gate_kind,
+                             int norm_order, hipStream_t stream);
+
+/*
  * The local branch alone, the test hook of spectre_mix_fwd_local:
  * y[b, t, h, :] = sum_j p_j v[b, j, h, :], with p the softmax over the keys
  * j in [t - win_left, t + win_right] and [0, L) of (q[b,t,h,:] . k[b,j,h,:])

@@ -68,6 +68,9 @@ def _bind(lib):
     lib.oracle_spectre_mix_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                              i64, i64, ci, vp, vp, ci]
     lib.oracle_spectre_mix_local.restype = ci
+    lib.oracle_spectre_mix_local_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                i64, i64, i64, ci, ci, ci, vp, vp, ci]
+    lib.oracle_spectre_mix_local_ex.restype = ci
     for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
               lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads,
               lib.oracle_spectre_y_ex, lib.oracle_layernorm_residual_ex,
@@ -252,17 +255,20 @@ def local_attention(q, k, v, win_left: int, win_right: int, dtype: int = 0) -> n
 
 
 def spectre_mix_local(q, k, v, x, gate, gamma, beta, keep_bins: int, win_left: int,
-                      win_right: int, dtype: int = 0, nthreads: int = 0, want_y: bool = False):
-    """The mix with the local branch: out = LN(x + y + y_loc); y (if want_y) is
-    y + y_loc."""
+                      win_right: int, dtype: int = 0, nthreads: int = 0, want_y: bool = False,
+                      gate_kind: int = 0, norm_order: int = 0):
+    """The mix with the local branch: out = LN(x + y + y_loc) (norm_order 0)
+    or x + LN(y + y_loc) (norm_order 1); y (if want_y) is y + y_loc."""
     B, L, H, D = q.shape
     q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
-    gate, gamma, beta = (_c(t, np.float32) for t in (gate, gamma, beta))
+    gate = _gate(gate, H, L, gate_kind)
+    gamma, beta = (_c(t, np.float32) for t in (gamma, beta))
     out = np.empty((B, L, H, D), np.float64)
     y = np.empty((B, L, H, D), np.float64) if want_y else None
-    _check(_load().oracle_spectre_mix_local(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                                            x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
-                                            beta.ctypes.data, B, H, L, D, keep_bins, win_left,
-                                            win_right, dtype, out.ctypes.data,
-                                            y.ctypes.data if want_y else None, nthreads))
+    _check(_load().oracle_spectre_mix_local_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                               x.ctypes.data, gate.ctypes.data, gamma.ctypes.data,
+                                               beta.ctypes.data, B, H, L, D, keep_bins, win_left,
+                                               win_right, dtype, gate_kind, norm_order,
+                                               out.ctypes.data, y.ctypes.data if want_y else None,
+                                               nthreads))
     return (out, y) if want_y else out

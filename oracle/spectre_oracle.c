@@ -68,7 +68,9 @@
  * beside the FFT branch, window 128 to 256, the two outputs added).
  * Reading: for token t of head h, the keys j with t - win_left <= j <= t +
  * win_right and 0 <= j < L; scores (q_t . k_j) / sqrt(D); softmax over those
- * keys; y_loc[t] = sum_j p_j v_j.  out = LN(x + y + y_loc).
+ * keys; y_loc[t] = sum_j p_j v_j.  out = LN(x + y + y_loc);
+ * oracle_spectre_mix_local_ex takes the gate kinds and norm orders above
+ * (pre-norm: out = x + LN(y + y_loc)).
  */
 #include <math.h>
 #include <pthread.h>
@@ -743,13 +745,16 @@ int oracle_local_attention(const void *q, const void *k, const void *v, int64_t 
   return ORACLE_OK;
 }
 
-/* The mix with the local branch: out = LN(x + y + y_loc), and optionally y + y_loc. */
-int oracle_spectre_mix_local(const void *q, const void *k, const void *v, const void *x,
-                             const float *gate, const float *gamma, const float *beta,
-                             int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
-                             int64_t win_left, int64_t win_right, int dtype, double *out,
-                             double *y_out, int nthreads) {
+/* The mix with the local branch: out = LN(x + y + y_loc) (norm order 0) or
+ * x + LN(y + y_loc) (norm order 1), y with the given gate kind; optionally
+ * y + y_loc. */
+int oracle_spectre_mix_local_ex(const void *q, const void *k, const void *v, const void *x,
+                                const float *gate, const float *gamma, const float *beta,
+                                int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
+                                int64_t win_left, int64_t win_right, int dtype, int gate_kind,
+                                int norm_order, double *out, double *y_out, int nthreads) {
   if (!x || !gamma || !beta || !out) return ORACLE_EINVAL;
+  if (norm_order != 0 && norm_order != 1) return ORACLE_EINVAL;
   int s = check_dims(B, H, L, D, keep, dtype);
   if (s) return s;
   const int64_t C = H * D, ntok = B * L;
@@ -760,15 +765,24 @@ int oracle_spectre_mix_local(const void *q, const void *k, const void *v, const 
     free(yl);
     return ORACLE_ENOMEM;
   }
-  s = oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, 0, y, nthreads);
+  s = oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, gate_kind, y, nthreads);
   if (s == ORACLE_OK) s = oracle_local_attention(q, k, v, B, H, L, D, win_left, win_right, dtype, yl);
   if (s == ORACLE_OK) {
     for (int64_t i = 0; i < ntok * C; ++i) y[i] += yl[i];
-    layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, 0, out);
+    layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, norm_order, out);
   }
   if (!y_out) free(y);
   free(yl);
   return s;
+}
+
+int oracle_spectre_mix_local(const void *q, const void *k, const void *v, const void *x,
+                             const float *gate, const float *gamma, const float *beta,
+                             int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
+                             int64_t win_left, int64_t win_right, int dtype, double *out,
+                             double *y_out, int nthreads) {
+  return oracle_spectre_mix_local_ex(q, k, v, x, gate, gamma, beta, B, H, L, D, keep, win_left,
+                                     win_right, dtype, 0, 0, out, y_out, nthreads);
 }
 
 /* Number of threads a call with `nthreads` would use (0 = all online CPUs). */

@@ -130,6 +130,11 @@ def test_local_rejects_before_device():
     assert mix(D=48, H=8) == sm.SPECTRE_EUNSUPPORTED     # head size the kernel lacks
     assert mix(L=65535, keep=1) == sm.SPECTRE_EINVAL      # checked like spectre_mix_fwd
     assert mix(out=GOOD + 0x3000000) == sm.SPECTRE_EINVAL  # out == x
+    for gk, no in ((3, 0), (0, 2), (-1, 0)):  # unknown gate kind or norm order
+        assert sm.spectre_mix_fwd_local_ex(GOOD, GOOD + 0x1000000, GOOD + 0x2000000,
+                                           GOOD + 0x3000000, GOOD + 0x4000000, GOOD + 0x5000000,
+                                           GOOD + 0x6000000, GOOD + 0x70000000, 1, 8, 65536, 64,
+                                           32769, 64, 64, 0, gk, no, 0) == sm.SPECTRE_EINVAL
 
     def attn(**kw):
         a = dict(B=1, H=2, L=100, D=64, wl=3, wr=3, dt=0, y=GOOD + 0x1000000, q=GOOD)

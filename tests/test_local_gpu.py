@@ -160,6 +160,58 @@ def test_mix_with_local_branch_against_oracle(B, L, H, D, dt, keep, wl, wr):
     assert np.all(np.isfinite(got)) and err <= tol(w)
 
 
+VARIANT_CASES = [
+    # (B, L, H, D, dtype, keep_bins, win_left, win_right, gate_kind, norm_order)
+    (1, 16384, 8, 64, 0, 4097, 64, 64, 2, 1),    # 16 x 1024, fused inverse, complex gate, pre-norm
+    (1, 65536, 4, 64, 0, 30000, 64, 64, 1, 1),   # 64 x 1024, split fused inverse, logit gate, pre
+    (2, 4096, 4, 32, 1, 1000, 128, 0, 2, 0),     # 4 x 1024, bf16, complex gate, post
+    (1, 2048, 2, 16, 0, 900, 40, 40, 1, 1),      # single level, LayerNorm pass, logit gate, pre
+    (1, 16384, 2, 32, 0, 3000, 64, 63, 0, 1),    # unfused inverse + LayerNorm pass, pre
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep,wl,wr,gk,no", VARIANT_CASES)
+def test_mix_with_local_branch_variants(B, L, H, D, dt, keep, wl, wr, gk, no):
+    """spectre_mix_fwd_local_ex: the local branch with the logit and complex
+    gates and the pre-norm order, on each inverse / norm path."""
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.custom(640 + L % 83, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=keep, affine=True)
+    say("case", w.describe(), "window", wl, wr, "gate kind", gk, "norm order", no)
+    inp = workloads.make_inputs(w)
+    gate = workloads.make_gate(w, gk)
+    ref = oracle.spectre_mix_local(inp["q"], inp["k"], inp["v"], inp["x"], gate, inp["gamma"],
+                                   inp["beta"], keep, wl, wr, dtype=dt, nthreads=oracle_threads(),
+                                   gate_kind=gk, norm_order=no)
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, gam, bet = dev(gate), dev(inp["gamma"]), dev(inp["beta"])
+    _, out = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_local_ex(q, k, v, x, g, gam, bet, out, B, H, L, D, keep, wl, wr,
+                                         dt, gk, no))
+    t.cuda.synchronize()
+    got = to_host_f64(out, dt).reshape(ref.shape)
+    err = np.abs(got - ref).max()
+    say("  out max-abs err %.3g (tol %.1g)" % (err, tol(w)))
+    assert np.all(np.isfinite(got)) and err <= tol(w)
+
+
+def test_local_plain_entry_is_the_real_post_variant():
+    """spectre_mix_fwd_local and spectre_mix_fwd_local_ex(REAL, POST) agree bit for bit."""
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.custom(655, B=1, L=16384, H=4, D=64, dtype=0, keep_bins=5000, affine=True)
+    inp = workloads.make_inputs(w)
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, gam, bet = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
+    _, a = empty_like_storage(w)
+    _, b = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_local(q, k, v, x, g, gam, bet, a, w.B, w.H, w.L, w.D, 5000, 64, 64, 0))
+    sm.check(sm.spectre_mix_fwd_local_ex(q, k, v, x, g, gam, bet, b, w.B, w.H, w.L, w.D, 5000, 64,
+                                         64, 0, 0, 0))
+    t.cuda.synchronize()
+    assert t.equal(a, b)
+
+
 @pytest.mark.parametrize("wid,wl,wr", [(3, 64, 64), (4, 128, 128)])
 def test_mix_with_local_branch_full_size_sampled(wid, wl, wr):
     """The 65536-token shapes (binary32, B = 1, window 128, the launch

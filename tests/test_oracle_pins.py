@@ -626,6 +626,24 @@ def test_local_attention_invariants():
     assert np.abs(yc - y).max() <= 1e-12
 
 
+@pytest.mark.parametrize("gate_kind,norm_order", [(1, 0), (2, 1), (0, 1)])
+def test_mix_with_local_branch_variants_compose(gate_kind, norm_order):
+    """The local mix with a logit or complex gate and either norm order is
+    the variant's y plus the window attention, through that norm order."""
+    B, L, H, D = 1, 48, 2, 4
+    q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    shape = (H, L // 2 + 1, 2) if gate_kind == 2 else (H, L // 2 + 1)
+    gate = RNG.uniform(-1, 1, shape).astype(np.float32)
+    gamma = (1 + 0.1 * RNG.standard_normal(H * D)).astype(np.float32)
+    beta = (0.1 * RNG.standard_normal(H * D)).astype(np.float32)
+    out = oracle.spectre_mix_local(q, k, v, x, gate, gamma, beta, 17, 6, 3,
+                                   gate_kind=gate_kind, norm_order=norm_order)
+    y = oracle.spectre_y(q, k, v, gate, 17, gate_kind=gate_kind)
+    yl = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), 6, 3)
+    ref = oracle.layernorm_residual(y + yl, x, gamma, beta, norm_order=norm_order)
+    assert np.abs(out - ref).max() <= 1e-9
+
+
 def test_mix_with_local_branch_adds_the_two_outputs():
     B, L, H, D = 1, 64, 2, 4
     q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
