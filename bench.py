@@ -141,12 +141,13 @@ def cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis):
             "columns x %d tokens, float64, %.2f s wall" % (F, w.B * w.C, w.L, dt)}
 
 
-def cpu_baseline_local(w, inp, wl, wr):
+def cpu_baseline_local(w, inp, wl, wr, gate_kind=0, norm_order=0):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
     oracle.spectre_mix_local(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
-                             inp["beta"], w.keep_bins, wl, wr, dtype=w.dtype, nthreads=threads)
+                             inp["beta"], w.keep_bins, wl, wr, dtype=w.dtype, nthreads=threads,
+                             gate_kind=gate_kind, norm_order=norm_order)
     dt = time.perf_counter() - t0
     return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
             "kind": "oracle", "sample": "the whole workload once with the local branch (keys "
@@ -205,8 +206,8 @@ def run_bench(args):
 
     def step():
         if win:
-            return sm.spectre_mix_fwd_local(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L, w.D,
-                                            w.keep_bins, wl, wr, w.dtype, stream)
+            return sm.spectre_mix_fwd_local_ex(q, k, v, x, gate, gamma, beta, out, w.B, w.H, w.L,
+                                               w.D, w.keep_bins, wl, wr, w.dtype, gk, no, stream)
         if F:
             return sm.spectre_mix_fwd_chunked(q, k, v, x, gate, gbd, gamma, beta, out, w.B, w.H,
                                               w.L, w.D, F, keep_blk, keep_axis, w.dtype, stream)
@@ -300,7 +301,7 @@ def run_bench(args):
     if not args.profile_run and not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         if win:
-            res["cpu_baseline"] = cpu_baseline_local(w, inp, wl, wr)
+            res["cpu_baseline"] = cpu_baseline_local(w, inp, wl, wr, gk, no)
         elif F:
             res["cpu_baseline"] = cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis)
         else:
@@ -450,9 +451,8 @@ def main():
         text, _, _ = summarize(args.summarize)
         print(text)
         return 0
-    if args.window and (args.window % 2 or args.fft_len or args.gate_kind or args.norm_order):
-        print("--window takes an even W and the plain mix (real gate, post-norm, no fft_len)",
-              file=sys.stderr)
+    if args.window and (args.window % 2 or args.fft_len):
+        print("--window takes an even W and no --fft-len", file=sys.stderr)
         return 2
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

@@ -21,7 +21,7 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
-def test_window_must_be_even_and_plain():
+def test_window_must_be_even_and_unchunked():
     assert run_bench("--window", "127").returncode == 2
     assert run_bench("--window", "128", "--fft-len", "4096").returncode == 2
 
