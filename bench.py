@@ -15,7 +15,13 @@ device synchronisations.  Prints one JSON line:
                `traffic` is HBM bytes per launch from the committed
                rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by a plain
                copy's reading), or null when the kernels have changed since
-  cpu_baseline the CPU oracle timed on this host on the whole workload
+  whole_call   the byte model of the whole call and its fraction of 8 TB/s;
+               also the median of up to 50 calls timed one at a time with
+               the 256 MB memory-side cache cleared before each (a 1 GiB
+               fill outside the events): flushed_ms_median
+  cpu_baseline the CPU oracle timed on this host on the whole workload, on
+               the host threads this job is given (OMP_NUM_THREADS when
+               set, else every online CPU), with the CPU model named
 
 The default workload is the article's long-context shape B=1, L=65536, H=8,
 D=64 in binary32 with no truncation.
@@ -47,6 +53,7 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 CSRC = os.path.join(ROOT, "efficient_attention_fft_amd", "csrc")
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+FLUSH_BYTES = 1 << 30  # fill that clears the 256 MB memory-side cache before a flushed call
 
 
 def source_hash() -> str:
@@ -115,41 +122,73 @@ def model_bytes(w) -> int:
     return m_min + extra
 
 
+def host_threads():
+    """Host threads the CPU leg may use: the CPU share this process is
+    given (the job's thread allotment, OMP_NUM_THREADS when the environment
+    sets one, which a GPU host shares among its GPUs), else every online
+    CPU."""
+    online = os.cpu_count() or 1
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return max(1, min(share, online) if share > 0 else online)
+
+
+def host_cpu():
+    """The host CPU's model name and its online CPU count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, os.cpu_count() or 1
+
+
+def _cpu_fields(threads):
+    name, online = host_cpu()
+    return {"cores": threads, "cpu_model": name, "cpus_online": online}
+
+
 def cpu_baseline(w, inp, gate_kind=0, norm_order=0):
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     t0 = time.perf_counter()
     oracle.spectre_mix(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
                        inp["beta"], w.keep_bins, dtype=w.dtype, nthreads=threads,
                        gate_kind=gate_kind, norm_order=norm_order)
     dt = time.perf_counter() - t0
-    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+    return {"value": w.tokens / dt, "unit": "tokens/s", **_cpu_fields(oracle.threads(threads)),
             "kind": "oracle", "sample": "the whole workload once: %d columns x %d tokens, "
             "float64, %.2f s wall" % (w.B * w.C, w.L, dt)}
 
 
 def cpu_baseline_chunked(w, inp, gate_blocks, F, keep_blk, keep_axis):
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     t0 = time.perf_counter()
     oracle.spectre_mix_chunked(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], gate_blocks,
                                inp["gamma"], inp["beta"], F, keep_blk, keep_axis, dtype=w.dtype,
                                nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+    return {"value": w.tokens / dt, "unit": "tokens/s", **_cpu_fields(oracle.threads(threads)),
             "kind": "oracle", "sample": "the whole workload once, chunked (fft_len %d): %d "
             "columns x %d tokens, float64, %.2f s wall" % (F, w.B * w.C, w.L, dt)}
 
 
 def cpu_baseline_local(w, inp, wl, wr, gate_kind=0, norm_order=0):
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_threads()
     t0 = time.perf_counter()
     oracle.spectre_mix_local(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"], inp["gamma"],
                              inp["beta"], w.keep_bins, wl, wr, dtype=w.dtype, nthreads=threads,
                              gate_kind=gate_kind, norm_order=norm_order)
     dt = time.perf_counter() - t0
-    return {"value": w.tokens / dt, "unit": "tokens/s", "cores": oracle.threads(threads),
+    return {"value": w.tokens / dt, "unit": "tokens/s", **_cpu_fields(oracle.threads(threads)),
             "kind": "oracle", "sample": "the whole workload once with the local branch (keys "
             "t-%d..t+%d): %d columns x %d tokens, float64, %.2f s wall"
             % (wl, wr, w.B * w.C, w.L, dt)}
@@ -235,6 +274,23 @@ def run_bench(args):
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = w.tokens * args.steps / wall
 
+    # each call alone with the memory-side cache cleared first: a 1 GiB fill
+    # (outside the events) before every call, so no input or workspace line
+    # is left in the 256 MB cache from the previous call
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    fl = []
+    for _ in range(min(args.steps, 50)):
+        flush.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sm.check(step())
+        e1.record(stream)
+        e1.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del flush
+    flushed_ms = float(sorted(fl)[len(fl) // 2])
+
     # per-kernel durations: the same K calls again, with the library's events
     sm.check(sm.spectre_mix_trace_start(args.steps))
     for _ in range(args.steps):
@@ -266,6 +322,8 @@ def run_bench(args):
     whole = {"model_bytes": mb,
              "model_GBps": round(mb / (ms_per_step * 1e-3) / 1e9, 1),
              "model_frac": round(mb / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "flushed_ms_median": round(flushed_ms, 5),
+             "flushed_model_frac": round(mb / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
              "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()}}
 
     if args.profile_run:

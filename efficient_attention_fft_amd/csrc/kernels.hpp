@@ -975,13 +975,11 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 //    grid a multiple of 8 an item's XCD is its index mod 8, as for one item
 //    per workgroup), and the next item's q copy runs under this item's last
 //    inverse DFT and its stores.
-// Every wave issues the same sequence of memory operations (each wave has
-// active slot-0 lanes), so a wave's vmcnt counts are exact: at the top of an
-// item, the 32 stores of the previous one may still be in flight.
-
-__device__ __forceinline__ void wait_vmcnt_32() {
-  __builtin_amdgcn_s_waitcnt((32 & 15) | ((32 >> 4) << 14) | 0x0F70);  // vmcnt(32)
-}
+// The asynchronous copies write LDS, and the compiler knows that much: before
+// the first LDS read after a copy it waits for every outstanding vector
+// memory operation (vmcnt(0)), which at the top of an item also retires the
+// previous item's U stores.  The explicit waits before the barriers that
+// publish a copy are full waits as well; nothing counts operations by hand.
 
 // CG: complex gate, read from the table in the product (no LDS copy).
 // UK: the product runs over k2 = u < UK only (UK = 17: all); the host takes
@@ -1056,7 +1054,6 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
         if (tid + NT * r < NGL) gl[tid + NT * r] = gv[r];
     }
   }
-  bool first = true;
   float2 v[R];
   float2 sa[H2 + 1], sb[H2 + 1];
 
@@ -1088,13 +1085,9 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     for (int x = 0; x < 3; ++x) {
       int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
       asm volatile("" : "+v"(t1o));
-      // ---- stage 1 input: this wave's copies have landed (at the top of an
-      // item, the previous item's 32 stores may still be in flight), then
-      // every other wave's
-      if (x == 0 && !first)
-        wait_vmcnt_32();
-      else
-        __builtin_amdgcn_s_waitcnt(0);
+      // ---- stage 1 input: this wave's copies have landed, then every other
+      // wave's
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (active1) {
         const float2* raw = lds + s1 * kSlot + t1 * 4 + j1;
@@ -1244,7 +1237,6 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     tile = next;
     blk = nblk;
     cols = ncols;
-    first = false;
   }
 }
 

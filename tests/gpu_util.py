@@ -13,7 +13,14 @@ TOL_BF16 = 2e-2  # max-abs on out, bfloat16 storage
 
 
 def oracle_threads():
-    return max(1, min(16, os.cpu_count() or 1))
+    """The CPU share of this process: OMP_NUM_THREADS when set, else every
+    online CPU."""
+    online = os.cpu_count() or 1
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return max(1, min(share, online) if share > 0 else online)
 
 
 def torch():

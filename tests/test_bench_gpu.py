@@ -37,3 +37,6 @@ def test_bench_line(args):
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
+    assert cpu["cpu_model"] and cpu["cpus_online"] >= cpu["cores"]
+    whole = res["whole_call"]
+    assert whole["flushed_ms_median"] > 0

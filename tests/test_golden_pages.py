@@ -2,8 +2,10 @@
 
 The article prints no worked numeric example of the mix itself; what it does
 print is a memory estimate for the complex spectra and the fraction of bins a
-truncated model keeps.  Both are tied here to the library's workspace formula
-and to the truncated workload's keep_bins.
+truncated model keeps.  These are consistency checks of the build's sizes
+against the article's figures (the workspace formula, the truncated
+workload's keep_bins), not pins of the mix's arithmetic: the oracle's pins are
+in test_oracle_pins.py and test_oracle_mutants.py.
 """
 import json
 import os
@@ -16,9 +18,11 @@ FIG = json.load(open(os.path.join(HERE, "golden", "page_figures.json")))
 
 
 def test_spectrum_workspace_matches_article_memory_estimate():
-    """One tensor's spectrum in the workspace (binary32 half spectrum: L/2
-    complex bins per channel = 4 bytes per real element) is the size the
-    article gives for the half-precision full spectrum of the same shape.
+    """Sanity check of the workspace formula (no arithmetic of the mix is
+    involved): one tensor's spectrum in the workspace (binary32 half
+    spectrum: L/2 complex bins per channel = 4 bytes per real element) has
+    the size the article gives for the half-precision full spectrum of the
+    same shape, the two encodings happening to cost the same.
     L = 131072 plans as 64 x 2 x 1024: the first pass writes the spectra of
     q, k and v, the second pass writes them again (out of place, in the LDS
     pass's layout), so the workspace holds six spectra plus the gate table."""

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from test_oracle_pins import (closed_form_y, closed_form_y_g, complex_gate,
-                              irfft_gate_complex, naive_dft)
+                              irfft_gate_complex, naive_dft, two_key_case)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "spectre_oracle.c")
 
@@ -35,6 +35,9 @@ MUTANTS = {
     "chunk_block_index": ("y2[(b * nb + t / F) * C + c]", "y2[(b * nb + (t / F + 1) % nb) * C + c]"),
     "chunk_block_gate": ("J.gate = gate_blocks;", "J.gate = gate;"),
     "local_scale_dropped": ("const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0;"),
+    "local_scale_over_d": ("const double scale = 1.0 / sqrt((double)D);",
+                           "const double scale = 1.0 / (double)D;"),
+    "local_exp2_weights": ("sc[j - j0] = exp(sc[j - j0] - mx);", "sc[j - j0] = exp2(sc[j - j0] - mx);"),
     "local_window_right": ("const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;",
                            "const int64_t j1 = t + win_right + 1 > L - 1 ? L - 1 : t + win_right + 1;"),
     "local_not_normalised": ("y[qb + d] = acc / sum;", "y[qb + d] = acc;"),
@@ -155,12 +158,18 @@ def _pins_pass() -> bool:
                         axis=1)
         if np.abs(y - ref).max() > 1e-10:
             return False
-        # local branch against the softmax definition on a tiny case
-        from test_oracle_pins import _brute_window_attention
-        q, k, v = (rng.standard_normal((1, 12, 2, 4)).astype(np.float32) for _ in range(3))
-        ref = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), 3, 2)
-        if np.abs(oracle.local_attention(q, k, v, 3, 2) - ref).max() > 1e-10:
-            return False
+        # local branch by closed forms only: two keys whose scores differ by
+        # ln 3 (weights 3/4, 1/4), and k = 0 (the plain mean over the window)
+        for D in (4, 64):
+            q, k, v, ref = two_key_case(D)
+            if np.abs(oracle.local_attention(q, k, v, 1, 1) - ref).max() > 1e-7:
+                return False
+        q, v = (rng.standard_normal((1, 12, 2, 4)).astype(np.float32) for _ in range(2))
+        y = oracle.local_attention(q, np.zeros_like(q), v, 3, 2)
+        for t in (0, 5, 11):
+            lo, hi = max(0, t - 3), min(11, t + 2)
+            if np.abs(y[0, t] - v[0, lo:hi + 1].astype(np.float64).mean(axis=0)).max() > 1e-14:
+                return False
     except oracle.OracleError:
         return False
     return True

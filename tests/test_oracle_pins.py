@@ -608,6 +608,39 @@ def test_local_attention_closed_forms():
     assert np.abs(yc[:, 0] - v64[:, 0]).max() == 0.0
 
 
+def two_key_case(D):
+    """q, k, v of a two-token sequence whose window (one key on each side)
+    holds both tokens: every query is e_0, key 0 is e_0 * sqrt(D) ln 3 in
+    head 0 and e_0 * sqrt(D) ln(1/3) in head 1, key 1 is 0, and v is e_1 at
+    token 0, e_2 at token 1.  The scores q.k / sqrt(D) are ln 3 (or ln 1/3)
+    and 0, so the softmax weights are exactly 3/4 and 1/4 (1/4 and 3/4 in
+    head 1) up to the binary32 rounding of the key: y = (0, 3/4, 1/4, 0...)
+    in head 0 and (0, 1/4, 3/4, 0...) in head 1, for both tokens."""
+    B, L, H = 1, 2, 2
+    q = np.zeros((B, L, H, D), np.float32)
+    k = np.zeros((B, L, H, D), np.float32)
+    v = np.zeros((B, L, H, D), np.float32)
+    q[..., 0] = 1.0
+    k[0, 0, 0, 0] = np.sqrt(D) * np.log(3.0)
+    k[0, 0, 1, 0] = -np.sqrt(D) * np.log(3.0)
+    v[0, 0, :, 1] = 1.0
+    v[0, 1, :, 2] = 1.0
+    y = np.zeros((B, L, H, D))
+    y[0, :, 0, 1], y[0, :, 0, 2] = 0.75, 0.25
+    y[0, :, 1, 1], y[0, :, 1, 2] = 0.25, 0.75
+    return q, k, v, y
+
+
+@pytest.mark.parametrize("D", [4, 16, 64, 128])
+def test_local_attention_two_key_weights(D):
+    """The score scale 1/sqrt(D) and the exponential weighting: two keys
+    whose scores differ by ln 3 get the weights 3/4 and 1/4 (the binary32
+    key moves them by at most a few 1e-8)."""
+    q, k, v, ref = two_key_case(D)
+    y = oracle.local_attention(q, k, v, 1, 1)
+    assert np.abs(y - ref).max() <= 1e-7
+
+
 def test_local_attention_invariants():
     """Shifting q, k, v along the sequence shifts y_loc away from the ends;
     permuting the heads permutes y_loc's heads; q * c with k / c leaves
