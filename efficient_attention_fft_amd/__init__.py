@@ -32,7 +32,8 @@ EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "s
            "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
            "spectre_mix_strerror", "spectre_mix_fwd_ex", "spectre_mix_y_ex",
            "spectre_mix_workspace_bytes_ex", "spectre_mix_fwd_chunked", "spectre_mix_y_chunked",
-           "spectre_mix_fwd_local", "spectre_mix_local_attention", "spectre_mix_fwd_local_ex")
+           "spectre_mix_fwd_local", "spectre_mix_local_attention", "spectre_mix_fwd_local_ex",
+           "spectre_mix_fwd_noalloc")
 
 
 class SpectreError(RuntimeError):
@@ -71,6 +72,9 @@ def _load():
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.spectre_mix_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp]
     lib.spectre_mix_fwd.restype = ci
+    lib.spectre_mix_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                            ci, vp]
+    lib.spectre_mix_fwd_noalloc.restype = ci
     lib.spectre_mix_y.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, vp]
     lib.spectre_mix_y.restype = ci
     lib.spectre_mix_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
@@ -146,6 +150,13 @@ def spectre_mix_fwd(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, d
     return _lib.spectre_mix_fwd(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate), _addr(gamma),
                                 _addr(beta), _addr(out), B, H, L, D, keep_bins, dtype,
                                 _stream(stream))
+
+
+def spectre_mix_fwd_noalloc(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, dtype,
+                            stream=None) -> int:
+    return _lib.spectre_mix_fwd_noalloc(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
+                                        _addr(gamma), _addr(beta), _addr(out), B, H, L, D,
+                                        keep_bins, dtype, _stream(stream))
 
 
 def spectre_mix_y(q, k, v, gate, y, B, H, L, D, keep_bins, dtype, stream=None) -> int:

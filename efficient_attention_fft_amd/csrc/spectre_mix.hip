@@ -158,12 +158,25 @@ struct LenTables {
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  int cus = 0;  // compute units, queried once
   std::map<int64_t, LenTables> tables;
 };
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
+
+// Per-device facts kept in fixed arrays (no allocation on any path).
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices] = {0};  // compute units, queried once; guarded by g_mu
+
+int cu_count(int dev, int* cus) {
+  if (dev < 0 || dev >= kMaxDevices) return SPECTRE_EUNSUPPORTED;
+  if (g_cus[dev] <= 0 &&
+      (hipDeviceGetAttribute(&g_cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+       g_cus[dev] <= 0))
+    return SPECTRE_EHIP;
+  *cus = g_cus[dev];
+  return SPECTRE_OK;
+}
 
 // ---------------------------------------------------------------- tracing
 //
@@ -221,13 +234,15 @@ void trace_rename_last(const char* name) {
 }
 
 // exp(-2 pi i e / n) in double, angle split exactly into a quarter turn and
-// a residual of at most pi/4, then rounded to binary32.
-float2 host_twiddle(int64_t e, int64_t n) {
+// a residual of at most pi/4, then rounded to binary32 (host tables, and the
+// allocation-free entry point's table kernel).
+__host__ __device__ float2 host_twiddle(int64_t e, int64_t n) {
+  constexpr double kHalfPi = 1.57079632679489661923;
   e %= n;
   int64_t q = (4 * e + n / 2) / n;
   int64_t r = 4 * e - q * n;
-  double phi = (M_PI / 2) * (double)r / (double)n;
-  double c = std::cos(phi), s = std::sin(phi);
+  double phi = kHalfPi * (double)r / (double)n;
+  double c = cos(phi), s = sin(phi);
   double re, im;
   switch (q & 3) {
     case 0: re = c; im = s; break;
@@ -590,11 +605,9 @@ int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
     // turn of workgroups on one XCD) stay close in time.  Larger grids keep
     // one item per workgroup: over more turns the sharers drift apart, and
     // the dispatcher's own order keeps them together.
-    int dev = 0;
+    int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
-    int& cus = g_dev[dev].cus;  // guarded by g_mu
-    if (cus <= 0 && (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0))
-      return SPECTRE_EHIP;
+    if (int rc = cu_count(dev, &cus)) return rc;
     const int64_t slots = 2 * (int64_t)cus;
     int64_t wgs = ntile;
     if (ntile <= 4 * slots) {
@@ -856,6 +869,11 @@ int launch_block_mix(int dev, const Shape& s, const Chunk& ch, const float2* dc,
 
 // The spectral part into `y` (pairs, binary32), and optionally the fused
 // residual + LayerNorm into `out`.
+int launch_all(int dev, const void* q, const void* k, const void* v, const void* x,
+               const float* gate, const float* gamma, const float* beta, void* out, float* y,
+               const Shape& s, const Plan& pl, const LenTables* tab, void* ws, hipStream_t st,
+               const Chunk* chunk, const Local* local);
+
 int run(const void* q, const void* k, const void* v, const void* x, const float* gate,
         const float* gamma, const float* beta, void* out, float* y, const Shape& s,
         const Plan& pl, hipStream_t st, const Chunk* chunk = nullptr,
@@ -873,6 +891,16 @@ int run(const void* q, const void* k, const void* v, const void* x, const float*
     rc = get_workspace(dev, wsb, &ws);
     if (rc) return rc;
   }
+  return launch_all(dev, q, k, v, x, gate, gamma, beta, out, y, s, pl, tab, ws, st, chunk, local);
+}
+
+// Every launch of one call, given its tables and workspace (g_mu held).
+int launch_all(int dev, const void* q, const void* k, const void* v, const void* x,
+               const float* gate, const float* gamma, const float* beta, void* out, float* y,
+               const Shape& s, const Plan& pl, const LenTables* tab, void* ws, hipStream_t st,
+               const Chunk* chunk, const Local* local) {
+  int rc = SPECTRE_OK;
+  const bool want_out = out != nullptr;
   // local branch: y_loc after the rest, computed first and added by the norm
   float2* yloc = local ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) +
                                                    ((workspace_for(s, pl, want_out) + 255) & ~(size_t)255))
@@ -1071,6 +1099,40 @@ int check_chunked(int64_t B, int64_t H, int64_t L, int64_t D, int64_t fft_len, i
   return SPECTRE_OK;
 }
 
+// ------------------------------------------- allocation-free entry point
+//
+// spectre_mix_fwd_noalloc keeps its workspace and tables in `scratch`, a
+// file-scope device array of kNoAllocBytes that every GPU the library runs
+// on holds until the process ends.  In host code the array's name is only a
+// stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (once per device, with that device current) and is the
+// only handle used for it.  Every call on one GPU shares that GPU's array, so
+// calls that overlap on one GPU race.  Layout: the workspace of
+// spectre_mix_fwd (spectra, gate table), then the twiddles w_L^e, e < L, the
+// twiddles w_N^e, e < N, and B's column pairs, each 256-byte aligned and all
+// written by every call before they are read (nothing needs clearing).
+
+constexpr size_t kNoAllocBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+void* g_scratch[kMaxDevices] = {nullptr};  // per device; guarded by g_mu
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// The tables of a one- or two-level plan: w_L^e (e < L), w_N^e (e < N) and
+// B's column pairs -- (0, -1) for one level; for two levels (L2 = 1) the
+// pairs (k1, L1 - k1), k1 = 1 .. L1/2 - 1, then the self-paired columns
+// (0, L1/2), the order build_wgcols gives.
+__global__ void k_build_tables(float2* twL, int64_t L, float2* twN, int64_t N, int2* wgcols,
+                               int nwg, int L1, int single) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < L) twL[i] = host_twiddle(i, L);
+  if (i < N) twN[i] = host_twiddle(i, N);
+  if (i < nwg) {
+    const int c = (int)i;
+    wgcols[i] = single ? make_int2(0, -1) : c < L1 / 2 - 1 ? make_int2(c + 1, L1 - 1 - c) : make_int2(0, L1 / 2);
+  }
+}
+
 }  // namespace
 }  // namespace spectre
 
@@ -1101,6 +1163,54 @@ int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x, 
                     int64_t L, int64_t D, int64_t keep_bins, int dtype, hipStream_t stream) {
   return spectre_mix_fwd_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, keep_bins, dtype,
                             SPECTRE_GATE_REAL, SPECTRE_NORM_POST, stream);
+}
+
+int spectre_mix_fwd_noalloc(const void* q, const void* k, const void* v, const void* x,
+                            const float* gate, const float* gamma, const float* beta, void* out,
+                            int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                            int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v, x})
+    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
+  // one- and two-level plans only; everything must fit the scratch array
+  const bool single = is_single(pl);
+  if (!single && pl.L2 != 1) return SPECTRE_EUNSUPPORTED;
+  const int nwg = single ? 1 : (int)(pl.L1 / 2);
+  const size_t o_twl = align256(workspace_for(s, pl, true));
+  const size_t o_twn = o_twl + align256(sizeof(float2) * (size_t)pl.L);
+  const size_t o_wg = o_twn + align256(sizeof(float2) * (size_t)pl.L3);
+  if (o_wg + align256(sizeof(int2) * (size_t)nwg) > kNoAllocBytes) return SPECTRE_EUNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SPECTRE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch[dev]) {  // set-up, once per device: this GPU's copy of the array
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return SPECTRE_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  char* base = static_cast<char*>(g_scratch[dev]);
+  LenTables t;
+  t.twL = reinterpret_cast<float2*>(base + o_twl);
+  t.twN = reinterpret_cast<float2*>(base + o_twn);
+  t.wgcols = reinterpret_cast<int2*>(base + o_wg);
+  t.nwg = nwg;
+  t.selfwg = single ? -1 : nwg - 1;
+  const int64_t n = std::max<int64_t>(pl.L, nwg);
+  hipLaunchKernelGGL(k_build_tables, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, t.twL,
+                     (int64_t)pl.L, t.twN, (int64_t)pl.L3, t.wgcols, nwg, (int)pl.L1, single ? 1 : 0);
+  if (hipGetLastError() != hipSuccess) return SPECTRE_EHIP;
+  return launch_all(dev, q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, &t, base, stream, nullptr,
+                    nullptr);
 }
 
 int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* gate, float* y,

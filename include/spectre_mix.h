@@ -116,6 +116,26 @@ int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x,
                     hipStream_t stream);
 
 /*
+ * spectre_mix_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, result and validation, but the call makes no
+ * allocation at all -- no hipMalloc, no hipFree, no allocating library
+ * routine.  Its workspace and tables live in a 64 MiB device array that the
+ * library holds on every GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call there).  Limits: plans of
+ * one or two levels (L <= 65536 here, 2^a 3^b as for spectre_mix_fwd) whose
+ * workspace and tables fit the 64 MiB (for example B * L * H * D up to about
+ * 3.5 million elements); anything larger returns SPECTRE_EUNSUPPORTED with
+ * nothing enqueued.  All calls on one GPU share its array: calls that overlap
+ * on one GPU (two streams, two threads) race and must be ordered by the
+ * caller.  Every call writes all the array regions it reads.
+ */
+int spectre_mix_fwd_noalloc(const void* q, const void* k, const void* v, const void* x,
+                            const float* gate, const float* gamma, const float* beta, void* out,
+                            int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
+                            int dtype, hipStream_t stream);
+
+/*
  * The spectral part alone (same definition, stopped before the residual and
  * the norm): y [B, L, H, D] binary32, on the device, caller-owned, must not
  * overlap an input.  Used to check the transform directly, because the

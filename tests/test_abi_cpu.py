@@ -221,3 +221,25 @@ def test_workspace_bytes():
 
 def test_release_without_device_is_clean():
     assert sm.spectre_mix_release() == sm.SPECTRE_OK
+
+
+def test_noalloc_rejects_before_device():
+    """The allocation-free entry point validates like spectre_mix_fwd and
+    refuses, before any device call, the plans it does not serve: three
+    levels (L = 98304 = 64 x 1.5 x 1024 plans as 64 x 3 x 512) and workspaces
+    beyond its 64 MiB array."""
+    def call(**kw):
+        a = dict(q=GOOD, k=GOOD + 0x1000000, v=GOOD + 0x2000000, x=GOOD + 0x3000000,
+                 gate=GOOD + 0x4000000, gamma=GOOD + 0x5000000, beta=GOOD + 0x6000000,
+                 out=GOOD + 0x70000000, B=1, H=8, L=4096, D=64, keep_bins=2049, dtype=0)
+        a.update(kw)
+        return sm.spectre_mix_fwd_noalloc(a["q"], a["k"], a["v"], a["x"], a["gate"], a["gamma"],
+                                          a["beta"], a["out"], a["B"], a["H"], a["L"], a["D"],
+                                          a["keep_bins"], a["dtype"], 0)
+    assert call(q=0) == sm.SPECTRE_EINVAL
+    assert call(L=4095) == sm.SPECTRE_EINVAL
+    assert call(q=GOOD + 8) == sm.SPECTRE_EINVAL
+    assert call(out=GOOD + 0x3000000) == sm.SPECTRE_EINVAL
+    assert call(L=98304, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED   # three-level plan
+    assert call(L=65536, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED   # 537 MB of workspace
+    assert call(B=2, L=4096, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED  # 16 N bytes = 64 MiB + tables
