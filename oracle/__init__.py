@@ -65,6 +65,9 @@ def _bind(lib):
     lib.oracle_spectre_mix_chunked.restype = ci
     lib.oracle_local_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci, vp]
     lib.oracle_local_attention.restype = ci
+    lib.oracle_local_attention_tokens.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
+                                                  vp, i64, vp]
+    lib.oracle_local_attention_tokens.restype = ci
     lib.oracle_spectre_mix_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                              i64, i64, ci, vp, vp, ci]
     lib.oracle_spectre_mix_local.restype = ci
@@ -251,6 +254,20 @@ def local_attention(q, k, v, win_left: int, win_right: int, dtype: int = 0) -> n
     y = np.empty((B, L, H, D), np.float64)
     _check(_load().oracle_local_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, L, D,
                                           win_left, win_right, dtype, y.ctypes.data))
+    return y
+
+
+def local_attention_tokens(q, k, v, win_left: int, win_right: int, tokens,
+                           dtype: int = 0) -> np.ndarray:
+    """The sliding-window branch at listed flat tokens b * L + t only:
+    [len(tokens), H, D] float64, each row as local_attention computes it."""
+    B, L, H, D = q.shape
+    q, k, v = (_storage(t, dtype) for t in (q, k, v))
+    toks = np.ascontiguousarray(tokens, np.int64)
+    y = np.empty((len(toks), H, D), np.float64)
+    _check(_load().oracle_local_attention_tokens(q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H,
+                                                 L, D, win_left, win_right, dtype,
+                                                 toks.ctypes.data, len(toks), y.ctypes.data))
     return y
 
 

@@ -704,6 +704,39 @@ int oracle_spectre_mix_chunked(const void *q, const void *k, const void *v, cons
   return s;
 }
 
+/* One query of the local branch: token t of batch b, head h -- softmax of the
+ * scores (q_t . k_j) / sqrt(D) over the keys j in t - win_left .. t + win_right
+ * inside the sequence, times v; the D values go to yq.  sc holds
+ * win_left + win_right + 1 doubles of scratch. */
+static void local_query(const void *q, const void *k, const void *v, int64_t B, int64_t H,
+                        int64_t L, int64_t D, int64_t win_left, int64_t win_right, int dtype,
+                        int64_t b, int64_t h, int64_t t, double *sc, double *yq) {
+  (void)B;
+  const int64_t C = H * D;
+  const double scale = 1.0 / sqrt((double)D);
+  const int64_t j0 = t - win_left < 0 ? 0 : t - win_left;
+  const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;
+  const int64_t qb = (b * L + t) * C + h * D;
+  double mx = -INFINITY;
+  for (int64_t j = j0; j <= j1; ++j) {
+    const int64_t kb = (b * L + j) * C + h * D;
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) dot += load_elem(q, dtype, qb + d) * load_elem(k, dtype, kb + d);
+    sc[j - j0] = dot * scale;
+    if (sc[j - j0] > mx) mx = sc[j - j0];
+  }
+  double sum = 0.0;
+  for (int64_t j = j0; j <= j1; ++j) {
+    sc[j - j0] = exp(sc[j - j0] - mx);
+    sum += sc[j - j0];
+  }
+  for (int64_t d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int64_t j = j0; j <= j1; ++j) acc += sc[j - j0] * load_elem(v, dtype, (b * L + j) * C + h * D + d);
+    yq[d] = acc / sum;
+  }
+}
+
 /* The local branch alone: y_loc [B, L, H, D], double (see the header). */
 int oracle_local_attention(const void *q, const void *k, const void *v, int64_t B, int64_t H,
                            int64_t L, int64_t D, int64_t win_left, int64_t win_right, int dtype,
@@ -713,34 +746,37 @@ int oracle_local_attention(const void *q, const void *k, const void *v, int64_t 
   if (s) return s;
   if (win_left < 0 || win_right < 0) return ORACLE_EINVAL;
   const int64_t C = H * D;
-  const double scale = 1.0 / sqrt((double)D);
   double *sc = (double *)malloc(sizeof(double) * (size_t)(win_left + win_right + 1));
   if (!sc) return ORACLE_ENOMEM;
   for (int64_t b = 0; b < B; ++b)
     for (int64_t h = 0; h < H; ++h)
-      for (int64_t t = 0; t < L; ++t) {
-        const int64_t j0 = t - win_left < 0 ? 0 : t - win_left;
-        const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;
-        const int64_t qb = (b * L + t) * C + h * D;
-        double mx = -INFINITY;
-        for (int64_t j = j0; j <= j1; ++j) {
-          const int64_t kb = (b * L + j) * C + h * D;
-          double dot = 0.0;
-          for (int64_t d = 0; d < D; ++d) dot += load_elem(q, dtype, qb + d) * load_elem(k, dtype, kb + d);
-          sc[j - j0] = dot * scale;
-          if (sc[j - j0] > mx) mx = sc[j - j0];
-        }
-        double sum = 0.0;
-        for (int64_t j = j0; j <= j1; ++j) {
-          sc[j - j0] = exp(sc[j - j0] - mx);
-          sum += sc[j - j0];
-        }
-        for (int64_t d = 0; d < D; ++d) {
-          double acc = 0.0;
-          for (int64_t j = j0; j <= j1; ++j) acc += sc[j - j0] * load_elem(v, dtype, (b * L + j) * C + h * D + d);
-          y[qb + d] = acc / sum;
-        }
-      }
+      for (int64_t t = 0; t < L; ++t)
+        local_query(q, k, v, B, H, L, D, win_left, win_right, dtype, b, h, t, sc,
+                    y + (b * L + t) * C + h * D);
+  free(sc);
+  return ORACLE_OK;
+}
+
+/* The local branch at listed tokens only: tokens[i] = b * L + t, and row i
+ * of y_tok [ntok, H, D] gets y_loc of that token (the same per-query
+ * arithmetic as oracle_local_attention). */
+int oracle_local_attention_tokens(const void *q, const void *k, const void *v, int64_t B,
+                                  int64_t H, int64_t L, int64_t D, int64_t win_left,
+                                  int64_t win_right, int dtype, const int64_t *tokens, int64_t ntok,
+                                  double *y_tok) {
+  if (!q || !k || !v || !tokens || !y_tok || ntok < 1) return ORACLE_EINVAL;
+  int s = check_dims(B, H, L, D, 0, dtype);
+  if (s) return s;
+  if (win_left < 0 || win_right < 0) return ORACLE_EINVAL;
+  for (int64_t i = 0; i < ntok; ++i)
+    if (tokens[i] < 0 || tokens[i] >= B * L) return ORACLE_EINVAL;
+  const int64_t C = H * D;
+  double *sc = (double *)malloc(sizeof(double) * (size_t)(win_left + win_right + 1));
+  if (!sc) return ORACLE_ENOMEM;
+  for (int64_t i = 0; i < ntok; ++i)
+    for (int64_t h = 0; h < H; ++h)
+      local_query(q, k, v, B, H, L, D, win_left, win_right, dtype, tokens[i] / L, h,
+                  tokens[i] % L, sc, y_tok + i * C + h * D);
   free(sc);
   return ORACLE_OK;
 }

@@ -106,23 +106,30 @@ def test_window_of_one_key_is_v():
     assert err <= 2.0 ** -16 * np.abs(v).max()
 
 
+def tile_tokens(w, salt=0):
+    """One query of every 32-query tile of the branch's kernel in every batch
+    element (position (tile + salt) mod 32 within the tile), plus each
+    sequence's first and last tokens."""
+    picks = []
+    for b in range(w.B):
+        tiles = np.arange((w.L + 31) // 32, dtype=np.int64)
+        t = np.minimum(32 * tiles + (tiles + salt + b) % 32, w.L - 1)
+        picks.append(b * w.L + np.concatenate([t, [0, w.L - 1]]))
+    return np.unique(np.concatenate(picks))
+
+
 def test_local_attention_full_size_sampled():
     """The 65536-token shape (B=1, H=8, D=64, binary32), window 128: the
-    oracle computes sampled tokens from the sub-sequence their window covers
-    (a token's output depends only on the keys in its window)."""
+    oracle computes one query of every 32-query tile (2048 tokens) and the
+    edges."""
     import efficient_attention_fft_amd as sm
     w = workloads.WORKLOADS[3]
     inp = workloads.make_inputs(w)
     wl = wr = 64
     got = run_local(sm, inp, w, wl, wr)
-    toks = [0, 1, 31, 32, 63, 64, 65, 1000, 32767, 32768, 65471, 65472, 65503, 65504, 65535]
-    toks += list(np.random.default_rng(5).integers(0, w.L, 17))
-    worst = 0.0
-    for t in toks:
-        lo, hi = max(0, t - wl), min(w.L, t + wr + 1)
-        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[:, lo:hi] for n in "qkv"}
-        ref = oracle.local_attention(sub["q"], sub["k"], sub["v"], wl, wr)[:, t - lo]
-        worst = max(worst, np.abs(got[:, t] - ref).max())
+    toks = tile_tokens(w, salt=5)
+    ref = oracle.local_attention_tokens(inp["q"], inp["k"], inp["v"], wl, wr, toks)
+    worst = np.abs(got.reshape(w.B * w.L, w.H, w.D)[toks] - ref).max()
     say("  sampled y_loc max-abs err %.3g over %d tokens" % (worst, len(toks)))
     assert worst <= 1e-4
 
@@ -216,24 +223,18 @@ def test_local_plain_entry_is_the_real_post_variant():
 def test_mix_with_local_branch_full_size_sampled(wid, wl, wr):
     """The 65536-token shapes (binary32, B = 1, window 128, the launch
     configuration the benchmark times; bfloat16, B = 2, truncated, window
-    256): at sampled tokens of every batch element the oracle's spectral y,
-    plus its windowed attention over each token's sub-sequence, through its
-    residual LayerNorm."""
+    256): at one query of every 32-query tile of every batch element, the
+    oracle's spectral y plus its windowed attention, through its residual
+    LayerNorm."""
     import efficient_attention_fft_amd as sm
     t = torch()
     w = workloads.WORKLOADS[wid]
     inp = workloads.make_inputs(w)
-    picks = [0, 5, 64, w.L - 1, w.L // 2] + list(np.random.default_rng(7).integers(0, w.L, 27))
-    toks = np.array(sorted(set(b * w.L + int(p) for b in range(w.B) for p in picks)), np.int64)
+    toks = tile_tokens(w, salt=7)
     _, ref_y = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"], inp["gate"],
                                          inp["gamma"], inp["beta"], w.keep_bins, toks,
                                          dtype=w.dtype, nthreads=oracle_threads())
-    yl = np.empty_like(ref_y)
-    for i, flat in enumerate(toks):
-        b, tk = divmod(int(flat), w.L)
-        lo, hi = max(0, tk - wl), min(w.L, tk + wr + 1)
-        sub = {n: inp[n].reshape(w.B, w.L, w.H, w.D)[b:b + 1, lo:hi] for n in "qkv"}
-        yl[i] = oracle.local_attention(sub["q"], sub["k"], sub["v"], wl, wr, dtype=w.dtype)[0, tk - lo]
+    yl = oracle.local_attention_tokens(inp["q"], inp["k"], inp["v"], wl, wr, toks, dtype=w.dtype)
     xs = inp["x"].reshape(w.B * w.L, w.H, w.D)[toks]
     ref = oracle.layernorm_residual(ref_y + yl, xs, inp["gamma"], inp["beta"], dtype=w.dtype)
     q, k, v, x = (dev(inp[n]) for n in "qkvx")

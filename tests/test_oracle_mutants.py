@@ -40,7 +40,7 @@ MUTANTS = {
     "local_exp2_weights": ("sc[j - j0] = exp(sc[j - j0] - mx);", "sc[j - j0] = exp2(sc[j - j0] - mx);"),
     "local_window_right": ("const int64_t j1 = t + win_right > L - 1 ? L - 1 : t + win_right;",
                            "const int64_t j1 = t + win_right + 1 > L - 1 ? L - 1 : t + win_right + 1;"),
-    "local_not_normalised": ("y[qb + d] = acc / sum;", "y[qb + d] = acc;"),
+    "local_not_normalised": ("yq[d] = acc / sum;", "yq[d] = acc;"),
     "local_wrong_head": ("const int64_t kb = (b * L + j) * C + h * D;",
                          "const int64_t kb = (b * L + j) * C + ((h + 1) % H) * D;"),
     "local_window_left": ("const int64_t j0 = t - win_left < 0 ? 0 : t - win_left;",

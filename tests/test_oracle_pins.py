@@ -591,6 +591,20 @@ def test_local_attention_equals_definition(L, wl, wr):
     assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
 
 
+def test_local_attention_at_listed_tokens():
+    """The token-list form of the branch (used where the full sequence is too
+    long to compute whole) gives, row by row, the full form's outputs at
+    those tokens, ragged batch boundaries included."""
+    B, L, H, D = 2, 50, 3, 8
+    q, k, v = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(3))
+    full = oracle.local_attention(q, k, v, 6, 4)
+    toks = np.array([0, 1, 7, 49, 50, 51, 77, 99], np.int64)
+    got = oracle.local_attention_tokens(q, k, v, 6, 4, toks)
+    assert np.array_equal(got, full.reshape(B * L, H, D)[toks])
+    with pytest.raises(oracle.OracleError):
+        oracle.local_attention_tokens(q, k, v, 6, 4, np.array([100], np.int64))
+
+
 def test_local_attention_closed_forms():
     """A one-token window returns v; with k = 0 every score is 0, so y is
     the plain mean of v over the window; the first token of a causal window

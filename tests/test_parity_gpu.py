@@ -46,15 +46,32 @@ def test_workload_full(wid):
     check_full(workloads.WORKLOADS[wid])
 
 
+def c1_row_tokens(w):
+    """One token of every row the last inverse pass handles: that pass runs one
+    workgroup per (b, m), m < M = L2 * L3, over the tokens n1 * M + m; token
+    m + M * (m mod L1) takes each m once and every n1 in turn, plus the batch
+    boundaries and the sample of workloads.sample_tokens."""
+    import efficient_attention_fft_amd as sm
+    st, (l1, l2, l3) = sm.spectre_mix_plan(w.L)
+    assert st == 0
+    M = l2 * l3
+    m = np.arange(M, dtype=np.int64)
+    rows = np.concatenate([b * w.L + m + M * (m % l1) for b in range(w.B)])
+    return np.unique(np.concatenate([rows, workloads.sample_tokens(w, 48)]))
+
+
 @pytest.mark.timeout(900)
 def test_workload5_sampled_tokens():
-    """786432 tokens: the oracle transforms every column in full and keeps a
-    sample of tokens; the GPU output is compared at those tokens."""
+    """786432 tokens (64 x 12 x 1024): the oracle transforms every column in
+    full and keeps one token of each of the 12288 rows of the last inverse
+    pass (every workgroup of it, each of its 64 token positions in turn); the
+    GPU output and y are compared at those tokens."""
     w = workloads.WORKLOADS[5]
-    say("case", w.describe(), "(sampled)")
+    say("case", w.describe(), "(one token per C1 row)")
     t = torch()
     inp = workloads.make_inputs(w)
-    toks = workloads.sample_tokens(w, 48)
+    toks = c1_row_tokens(w)
+    assert len(toks) >= 12288
     ref_out, ref_y = oracle.spectre_mix_tokens(inp["q"], inp["k"], inp["v"], inp["x"],
                                                inp["gate"], inp["gamma"], inp["beta"],
                                                w.keep_bins, toks, nthreads=oracle_threads())
