@@ -1078,8 +1078,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     }
     const int partner_byte = (((j2 * 64 + ps * R + pk1) & 63) << 2);
     const bool special = a_zero && k1 == 0;
-    const int colid1 = s1 == 0 ? cols.x : cols.y;
-    const bool active1 = colid1 >= 0;
+    const int colid1 = s1 == 0 ? cols.x : cols.y;  // every workgroup holds two columns
 
 #pragma unroll 1
     for (int x = 0; x < 3; ++x) {
@@ -1089,13 +1088,10 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
       // wave's
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (active1) {
+      {
         const float2* raw = lds + s1 * kSlot + t1 * 4 + j1;
 #pragma unroll
         for (int i = 0; i < R; ++i) v[i] = raw[i * R * 4];
-      } else {
-#pragma unroll
-        for (int i = 0; i < R; ++i) v[i] = make_float2(0.f, 0.f);
       }
       // the next item's columns (a vector load: the top of the next tensor
       // waits for it), then its gate values, both used at the end of the item
@@ -1123,30 +1119,36 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
         p.dc[x * p.dc_stride + (int64_t)blk.z * p.CP2 + blk.y * 4 + j2] = cscale(v[0], p.dc_scale);
 
       // ---- split the packed spectra and accumulate / finish the product
-      // (the same arithmetic as k_mid_sq)
-      auto mirror = [&](int u) -> float2 {
-        if (u == H2) return v[H2];
-        const float2 pulled = lane_pull2(v[R - 1 - u], partner_byte);
-        return special ? v[(R - u) % R] : pulled;
-      };
-      {
+      // (the same arithmetic as k_mid_sq).  Regular workgroups pair every
+      // bin with the partner lane and use no bin k2 = R/2 of their own; the
+      // workgroup of the self-paired columns has lane k1 = 0 of column (0, 0)
+      // holding its own mirrors and the self-mirrored bin k2 = R/2.
+      auto product = [&](auto self_tag) __attribute__((always_inline)) {
+        constexpr bool SELF = decltype(self_tag)::value;
+        constexpr int NU = SELF ? H2 + 1 : H2;  // bins owned: k2 = u < NU
+        auto mirror = [&](int u) -> float2 {
+          if (u == H2) return v[H2];
+          const float2 pulled = lane_pull2(v[R - 1 - u], partner_byte);
+          if constexpr (SELF) return special ? v[(R - u) % R] : pulled;
+          else return pulled;
+        };
         if (x == 0) {
 #pragma unroll
-          for (int u = 0; u < UK; ++u) {
+          for (int u = 0; u < UK && u < NU; ++u) {
             const float2 z = v[u], zm = mirror(u);
             sa[u] = make_float2(z.x + zm.x, z.y - zm.y);
             sb[u] = make_float2(z.y + zm.y, zm.x - z.x);
           }
         } else if (x == 1) {
 #pragma unroll
-          for (int u = 0; u < UK; ++u) {
+          for (int u = 0; u < UK && u < NU; ++u) {
             const float2 z = v[u], zm = mirror(u);
             sa[u] = cmulc(sa[u], make_float2(z.x + zm.x, z.y - zm.y));
             sb[u] = cmulc(sb[u], make_float2(z.y + zm.y, zm.x - z.x));
           }
         } else {
 #pragma unroll
-          for (int u = 0; u <= H2; ++u) {
+          for (int u = 0; u < NU; ++u) {
             if (u >= UK) {  // every bin from here on truncated
               sa[u] = sb[u] = make_float2(0.f, 0.f);
               continue;
@@ -1170,15 +1172,24 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
             sb[u] = make_float2(oa.x + ob.y, ob.x - oa.y);
           }
         }
-      }
+      };
+      if (regular)
+        product(std::false_type{});
+      else
+        product(std::true_type{});
     }
     // ---- W back into this lane's own bins k2 = 0 .. R-1
 #pragma unroll
     for (int u = 0; u < H2; ++u) v[u] = sa[u];
+    if (regular) {
 #pragma unroll
-    for (int q = 0; q < H2; ++q) {
-      const float2 pulled = lane_pull2(sb[H2 - 1 - q], partner_byte);
-      v[H2 + q] = special ? (q == 0 ? sa[H2] : sb[H2 - q]) : pulled;
+      for (int q = 0; q < H2; ++q) v[H2 + q] = lane_pull2(sb[H2 - 1 - q], partner_byte);
+    } else {
+#pragma unroll
+      for (int q = 0; q < H2; ++q) {
+        const float2 pulled = lane_pull2(sb[H2 - 1 - q], partner_byte);
+        v[H2 + q] = special ? (q == 0 ? sa[H2] : sb[H2 - q]) : pulled;
+      }
     }
     // ---- inverse, stage 2 lanes: along k2, twiddle w_N^{-k1 n}
     int k1o = k1;
@@ -1198,7 +1209,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     // output twiddle w^-(m3 tw_mul), w = w_L, for m3 = t1 + R i, i = 4 a + j:
     // the seeds w^(t1 + R j), j < 4, times (w^(4 R))^a; loaded before the
     // next item's copy so that waiting for them does not wait for it
-    const int kc1 = active1 ? colid1 % p.L1 : 0, k2c1 = active1 ? colid1 / p.L1 : 0;
+    const int kc1 = colid1 % p.L1, k2c1 = colid1 / p.L1;
     const int tw_mul = p.L1 * k2c1 + (p.L2 == 1 ? kc1 : 0);
     float2 tws[4];
 #pragma unroll
@@ -1228,8 +1239,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * a + j;
-        if (active1)
-          *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) = cmul(v[i], cconj(cmul(tws[j], step)));
+        *reinterpret_cast<float2*>(dst + i * row_pair * 8 + off) = cmul(v[i], cconj(cmul(tws[j], step)));
       }
       step = cmul(step, tw4r);
     }
