@@ -8,8 +8,9 @@ Every function takes host numpy arrays: q, k, v, x as [B, L, H, D] float32
 (dtype 0) or uint16 bfloat16 bit patterns (dtype 1); gate as [H, L//2 + 1]
 float32 (gate_kind 0: the multiplier, 1: its logit), or [H, L//2 + 1, 2]
 float32 (gate_kind 2: real and imaginary parts); gamma, beta as [H*D]
-float32.  norm_order 0 is out = LN(x + y), 1 is out = x + LN(y).  Results
-are float64.
+float32.  norm_order 0 is out = LN(x + y), 1 is out = x + LN(y); adding 2
+uses an RMSNorm (no mean subtracted) in place of the LayerNorm.  Results are
+float64.
 """
 from __future__ import annotations
 
@@ -74,6 +75,9 @@ def _bind(lib):
     lib.oracle_spectre_mix_local_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                 i64, i64, i64, ci, ci, ci, vp, vp, ci]
     lib.oracle_spectre_mix_local_ex.restype = ci
+    lib.oracle_spectre_mix_local_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                                   i64, i64, i64, i64, ci, ci, ci, vp, vp, ci]
+    lib.oracle_spectre_mix_local_gated.restype = ci
     for f in (lib.oracle_fft, lib.oracle_spectre_y, lib.oracle_layernorm_residual,
               lib.oracle_spectre_mix, lib.oracle_spectre_mix_tokens, lib.oracle_threads,
               lib.oracle_spectre_y_ex, lib.oracle_layernorm_residual_ex,
@@ -269,6 +273,27 @@ def local_attention_tokens(q, k, v, win_left: int, win_right: int, tokens,
                                                  L, D, win_left, win_right, dtype,
                                                  toks.ctypes.data, len(toks), y.ctypes.data))
     return y
+
+
+def spectre_mix_local_gated(q, k, v, x, gate, mix, gamma, beta, keep_bins: int, win_left: int,
+                            win_right: int, dtype: int = 0, nthreads: int = 0,
+                            want_y: bool = False, gate_kind: int = 0, norm_order: int = 0):
+    """The mix with the local branch weighted per channel: the branch sum is
+    mix[c] * y + (1 - mix[c]) * y_loc (mix: [H*D] float32 in [0, 1]), then
+    the residual and the norm of norm_order; y (if want_y) is that sum."""
+    B, L, H, D = q.shape
+    q, k, v, x = (_storage(t, dtype) for t in (q, k, v, x))
+    gate = _gate(gate, H, L, gate_kind)
+    mix, gamma, beta = (_c(t, np.float32) for t in (mix, gamma, beta))
+    out = np.empty((B, L, H, D), np.float64)
+    y = np.empty((B, L, H, D), np.float64) if want_y else None
+    _check(_load().oracle_spectre_mix_local_gated(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                                  x.ctypes.data, gate.ctypes.data, mix.ctypes.data,
+                                                  gamma.ctypes.data, beta.ctypes.data, B, H, L, D,
+                                                  keep_bins, win_left, win_right, dtype, gate_kind,
+                                                  norm_order, out.ctypes.data,
+                                                  y.ctypes.data if want_y else None, nthreads))
+    return (out, y) if want_y else out
 
 
 def spectre_mix_local(q, k, v, x, gate, gamma, beta, keep_bins: int, win_left: int,

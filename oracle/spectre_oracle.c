@@ -52,7 +52,10 @@
  *    the gate acts there.
  *  - norm order 0 (post-norm, section 2.2's pseudocode): out = LN(x + y);
  *    norm order 1 (pre-norm, the order section 3.3 settles on): out =
- *    x + LN(y), the same LayerNorm applied to y alone.
+ *    x + LN(y), the same LayerNorm applied to y alone.  Adding 2 to either
+ *    order uses an RMSNorm instead (section 3.3 names "RMSNorm or
+ *    LayerNorm"): z / sqrt(mean(z^2) + eps) * gamma + beta over the H*D
+ *    channels -- no mean is subtracted; beta = 0 gives the textbook form.
  *
  * Chunked mix (oracle_spectre_mix_chunked; section 3.2's fft_len below L:
  * an FFT inside 4096-token blocks, then one more low-frequency interaction
@@ -70,7 +73,12 @@
  * win_right and 0 <= j < L; scores (q_t . k_j) / sqrt(D); softmax over those
  * keys; y_loc[t] = sum_j p_j v_j.  out = LN(x + y + y_loc);
  * oracle_spectre_mix_local_ex takes the gate kinds and norm orders above
- * (pre-norm: out = x + LN(y + y_loc)).
+ * (pre-norm: out = x + LN(y + y_loc)).  Section 4.3 has the two branches
+ * "summed or gated"; oracle_spectre_mix_local_gated reads the gated form as
+ * a per-channel weight g in [0, 1] given by the caller (the sigmoid that
+ * would produce it is upstream, as for the gate): the branch sum becomes
+ * g * y + (1 - g) * y_loc, channel by channel, before the residual and the
+ * norm (g = 1: the FFT branch alone; g = 0: the local branch alone).
  */
 #include <math.h>
 #include <pthread.h>
@@ -470,7 +478,7 @@ static int check_dims(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, 
 }
 
 static int check_variant(int gate_kind, int norm_order) {
-  if (gate_kind < 0 || gate_kind > 2 || norm_order < 0 || norm_order > 1) return ORACLE_EINVAL;
+  if (gate_kind < 0 || gate_kind > 2 || norm_order < 0 || norm_order > 3) return ORACLE_EINVAL;
   return ORACLE_OK;
 }
 
@@ -516,10 +524,15 @@ int oracle_spectre_y(const void *q, const void *k, const void *v, const float *g
  * after the affine step.  xrow[i] selects the row of x for row i of y (NULL:
  * row i).
  */
+/* The norm and the residual, token by token.  norm_order: bit 0 pre-norm
+ * (out = x + N(y)) instead of post-norm (out = N(x + y)); bit 1 RMSNorm
+ * (nothing subtracted, the mean square in place of the variance) instead of
+ * LayerNorm. */
 static void layernorm_rows(const double *y, const void *x, int dtype, const int64_t *xrow,
                            const float *gamma, const float *beta, int64_t nrows, int64_t C,
-                           int pre, double *out) {
+                           int norm_order, double *out) {
   const double eps = 1e-5;
+  const int pre = norm_order & 1, rms = (norm_order & 2) != 0;
   for (int64_t i = 0; i < nrows; ++i) {
     int64_t xr = xrow ? xrow[i] : i;
     const double *yr = y + i * C;
@@ -529,7 +542,7 @@ static void layernorm_rows(const double *y, const void *x, int dtype, const int6
       o[c] = pre ? yr[c] : load_elem(x, dtype, xr * C + c) + yr[c];
       sum += o[c];
     }
-    double mean = sum / (double)C;
+    double mean = rms ? 0.0 : sum / (double)C;
     double var = 0.0;
     for (int64_t c = 0; c < C; ++c) var += (o[c] - mean) * (o[c] - mean);
     var /= (double)C;
@@ -781,6 +794,13 @@ int oracle_local_attention_tokens(const void *q, const void *k, const void *v, i
   return ORACLE_OK;
 }
 
+int oracle_spectre_mix_local_gated(const void *q, const void *k, const void *v, const void *x,
+                                   const float *gate, const float *mix, const float *gamma,
+                                   const float *beta, int64_t B, int64_t H, int64_t L, int64_t D,
+                                   int64_t keep, int64_t win_left, int64_t win_right, int dtype,
+                                   int gate_kind, int norm_order, double *out, double *y_out,
+                                   int nthreads);
+
 /* The mix with the local branch: out = LN(x + y + y_loc) (norm order 0) or
  * x + LN(y + y_loc) (norm order 1), y with the given gate kind; optionally
  * y + y_loc. */
@@ -789,8 +809,23 @@ int oracle_spectre_mix_local_ex(const void *q, const void *k, const void *v, con
                                 int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep,
                                 int64_t win_left, int64_t win_right, int dtype, int gate_kind,
                                 int norm_order, double *out, double *y_out, int nthreads) {
+  return oracle_spectre_mix_local_gated(q, k, v, x, gate, NULL, gamma, beta, B, H, L, D, keep,
+                                        win_left, win_right, dtype, gate_kind, norm_order, out,
+                                        y_out, nthreads);
+}
+
+/* The mix with the local branch, the branches weighted per channel:
+ * y_sum = mix[c] * y + (1 - mix[c]) * y_loc (mix null: the plain sum
+ * y + y_loc), then the residual and the norm of the given order; y_out, if
+ * given, receives y_sum. */
+int oracle_spectre_mix_local_gated(const void *q, const void *k, const void *v, const void *x,
+                                   const float *gate, const float *mix, const float *gamma,
+                                   const float *beta, int64_t B, int64_t H, int64_t L, int64_t D,
+                                   int64_t keep, int64_t win_left, int64_t win_right, int dtype,
+                                   int gate_kind, int norm_order, double *out, double *y_out,
+                                   int nthreads) {
   if (!x || !gamma || !beta || !out) return ORACLE_EINVAL;
-  if (norm_order != 0 && norm_order != 1) return ORACLE_EINVAL;
+  if (check_variant(gate_kind, norm_order)) return ORACLE_EINVAL;
   int s = check_dims(B, H, L, D, keep, dtype);
   if (s) return s;
   const int64_t C = H * D, ntok = B * L;
@@ -804,7 +839,14 @@ int oracle_spectre_mix_local_ex(const void *q, const void *k, const void *v, con
   s = oracle_spectre_y_ex(q, k, v, gate, B, H, L, D, keep, dtype, gate_kind, y, nthreads);
   if (s == ORACLE_OK) s = oracle_local_attention(q, k, v, B, H, L, D, win_left, win_right, dtype, yl);
   if (s == ORACLE_OK) {
-    for (int64_t i = 0; i < ntok * C; ++i) y[i] += yl[i];
+    if (mix) {
+      for (int64_t i = 0; i < ntok * C; ++i) {
+        const double g = (double)mix[i % C];
+        y[i] = g * y[i] + (1.0 - g) * yl[i];
+      }
+    } else {
+      for (int64_t i = 0; i < ntok * C; ++i) y[i] += yl[i];
+    }
     layernorm_rows(y, x, dtype, NULL, gamma, beta, ntok, C, norm_order, out);
   }
   if (!y_out) free(y);

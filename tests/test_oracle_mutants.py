@@ -58,6 +58,12 @@ MUTANTS = {
     "prime_dft_index": ("acc = cadd(acc, cmul(y[r], twiddle(t, p, r * s, sign)));",
                         "acc = cadd(acc, cmul(y[r], twiddle(t, p, r + s, sign)));"),
     "variance_unbiased": ("var /= (double)C;", "var /= (double)(C - 1);"),
+    "rms_subtracts_mean": ("double mean = rms ? 0.0 : sum / (double)C;",
+                           "double mean = sum / (double)C;"),
+    "gated_weights_swapped": ("y[i] = g * y[i] + (1.0 - g) * yl[i];",
+                              "y[i] = (1.0 - g) * y[i] + g * yl[i];"),
+    "gated_channel_index": ("const double g = (double)mix[i % C];",
+                            "const double g = (double)mix[(i / C) % C];"),
     "eps_outside_sqrt": ("double rstd = 1.0 / sqrt(var + eps);",
                          "double rstd = 1.0 / (sqrt(var) + eps);"),
     "gamma_beta_swapped": ("o[c] = (o[c] - mean) * rstd * (double)gamma[c] + (double)beta[c];",
@@ -170,6 +176,32 @@ def _pins_pass() -> bool:
             lo, hi = max(0, t - 3), min(11, t + 2)
             if np.abs(y[0, t] - v[0, lo:hi + 1].astype(np.float64).mean(axis=0)).max() > 1e-14:
                 return False
+        # RMSNorm: a constant token keeps c / sqrt(c^2 + eps)
+        H, D, Lr = 2, 2, 4
+        cst = np.full((1, Lr, H, D), 0.75, np.float32)
+        zr = np.zeros_like(cst)
+        o = oracle.spectre_mix(zr, zr, zr, cst, np.ones((H, 3), np.float32),
+                               np.ones(H * D, np.float32), np.zeros(H * D, np.float32), 0,
+                               norm_order=2)
+        if np.abs(o - 0.75 / np.sqrt(0.75 ** 2 + 1e-5)).max() > 1e-12:
+            return False
+        # gated branches: g = 1 is the FFT mix alone; a half-and-half token
+        # mix is affine in g channel by channel
+        B, L, H, D = 1, 24, 2, 2
+        C = H * D
+        q, k, v, x = (rng.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+        gt = rng.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+        ones, zeros = np.ones(C, np.float32), np.zeros(C, np.float32)
+        a = oracle.spectre_mix_local_gated(q, k, v, x, gt, ones, ones, zeros, 9, 2, 2)
+        if np.abs(a - oracle.spectre_mix(q, k, v, x, gt, ones, zeros, 9)).max() > 1e-12:
+            return False
+        gw = np.array([0.1, 0.4, 0.7, 0.9], np.float32)
+        _, yg = oracle.spectre_mix_local_gated(q, k, v, x, gt, gw, ones, zeros, 9, 2, 2, want_y=True)
+        yf = oracle.spectre_y(q, k, v, gt, 9)
+        yl = oracle.local_attention(q, k, v, 2, 2)
+        gc = gw.astype(np.float64).reshape(H, D)
+        if np.abs(yg - (gc * yf + (1 - gc) * yl)).max() > 1e-12:
+            return False
     except oracle.OracleError:
         return False
     return True

@@ -486,9 +486,94 @@ def test_variant_arguments_rejected():
         oracle.spectre_y(q, q, q, g, 5, gate_kind=2)  # a complex gate needs [H, bins, 2]
     with pytest.raises(oracle.OracleError):
         oracle.spectre_y(q, q, q, g, 5, gate_kind=3)
-    with pytest.raises(oracle.OracleError):
-        oracle.spectre_mix(q, q, q, q, g, np.ones(2, np.float32), np.zeros(2, np.float32), 5,
-                           norm_order=2)
+    for bad in (-1, 4):  # 0..3: post / pre, LayerNorm / RMSNorm
+        with pytest.raises(oracle.OracleError):
+            oracle.spectre_mix(q, q, q, q, g, np.ones(2, np.float32), np.zeros(2, np.float32), 5,
+                               norm_order=bad)
+
+
+# ------------------------------------------------------------------ RMSNorm
+#
+# Section 3.3's "RMSNorm or LayerNorm": norm_order + 2 selects an RMSNorm,
+# z / sqrt(mean(z^2) + eps) * gamma + beta, in either order.
+
+def test_rmsnorm_constant_token():
+    """A token whose channels all equal c normalises to c / sqrt(c^2 + eps)
+    under RMSNorm (a LayerNorm would give 0): with y = 0 (keep_bins 0) the
+    post-norm output is that times gamma plus beta, and the pre-norm output
+    of y = c (x = 0) is the same."""
+    H, D, L = 2, 3, 4
+    C = H * D
+    c = 0.75
+    gamma = np.linspace(0.5, 2.0, C).astype(np.float32)
+    beta = np.linspace(-0.2, 0.3, C).astype(np.float32)
+    x = np.full((1, L, H, D), c, np.float32)
+    z = np.zeros_like(x)
+    g = np.ones((H, L // 2 + 1), np.float32)
+    out = oracle.spectre_mix(z, z, z, x, g, gamma, beta, 0, norm_order=2)
+    ref = c / np.sqrt(c * c + 1e-5) * gamma.astype(np.float64) + beta
+    assert np.abs(out.reshape(L, C) - ref).max() <= 1e-12
+    ln = oracle.spectre_mix(z, z, z, x, g, gamma, beta, 0, norm_order=0)
+    assert np.abs(ln.reshape(L, C) - beta).max() <= 1e-12
+    y = np.full((1, L, H, D), c)
+    pre = oracle.layernorm_residual(y, np.zeros_like(x), gamma, beta, norm_order=3)
+    assert np.abs(pre.reshape(L, C) - ref).max() <= 1e-12
+
+
+def test_rmsnorm_statistics_and_zero_mean_tokens():
+    """RMSNorm with gamma = 1, beta = 0 leaves each token with mean square
+    m / (m + eps), m the token's mean square; on tokens of zero mean it equals
+    the LayerNorm; pre-norm RMS minus x is the RMSNorm of y."""
+    rng = np.random.default_rng(21)
+    B, L, H, D = 1, 16, 2, 8
+    C = H * D
+    y = 3.0 * rng.standard_normal((B, L, H, D)) + 1.5
+    x = rng.standard_normal((B, L, H, D)).astype(np.float32)
+    ones, zeros = np.ones(C, np.float32), np.zeros(C, np.float32)
+    out = oracle.layernorm_residual(y, np.zeros_like(x), ones, zeros, norm_order=2).reshape(L, C)
+    m = (y.reshape(L, C) ** 2).mean(axis=1)
+    assert np.abs((out ** 2).mean(axis=1) - m / (m + 1e-5)).max() <= 1e-12
+    zm = y.reshape(L, C) - y.reshape(L, C).mean(axis=1, keepdims=True)
+    zm = zm.reshape(B, L, H, D)
+    a = oracle.layernorm_residual(zm, np.zeros_like(x), ones, zeros, norm_order=2)
+    b = oracle.layernorm_residual(zm, np.zeros_like(x), ones, zeros, norm_order=0)
+    assert np.abs(a - b).max() <= 1e-12
+    pre = oracle.layernorm_residual(y, x, ones, zeros, norm_order=3)
+    rms = oracle.layernorm_residual(y, np.zeros_like(x), ones, zeros, norm_order=2)
+    assert np.abs(pre - x.astype(np.float64) - rms).max() <= 1e-12
+
+
+# ------------------------------------------------------- gated branch sum
+#
+# Section 4.3's branches "summed or gated": a per-channel weight g mixes the
+# FFT branch and the local branch, g * y + (1 - g) * y_loc.
+
+def test_gated_branches_limits_and_linearity():
+    """g = 1 is the FFT mix alone, g = 0 the residual norm of the local branch
+    alone, and y is affine in g channel by channel (half of each)."""
+    B, L, H, D = 1, 40, 2, 4
+    C = H * D
+    q, k, v, x = (RNG.standard_normal((B, L, H, D)).astype(np.float32) for _ in range(4))
+    gate = RNG.uniform(0, 1, (H, L // 2 + 1)).astype(np.float32)
+    gamma = (1 + 0.1 * RNG.standard_normal(C)).astype(np.float32)
+    beta = (0.1 * RNG.standard_normal(C)).astype(np.float32)
+    one, zero = np.ones(C, np.float32), np.zeros(C, np.float32)
+    for norm_order in (0, 1, 2, 3):
+        out1 = oracle.spectre_mix_local_gated(q, k, v, x, gate, one, gamma, beta, 15, 5, 3,
+                                              norm_order=norm_order)
+        ref1 = oracle.spectre_mix(q, k, v, x, gate, gamma, beta, 15, norm_order=norm_order)
+        assert np.abs(out1 - ref1).max() <= 1e-12
+        out0 = oracle.spectre_mix_local_gated(q, k, v, x, gate, zero, gamma, beta, 15, 5, 3,
+                                              norm_order=norm_order)
+        yl = _brute_window_attention(*(a.astype(np.float64) for a in (q, k, v)), 5, 3)
+        ref0 = oracle.layernorm_residual(yl, x, gamma, beta, norm_order=norm_order)
+        assert np.abs(out0 - ref0).max() <= 1e-9
+    g = RNG.uniform(0, 1, C).astype(np.float32)
+    _, yg = oracle.spectre_mix_local_gated(q, k, v, x, gate, g, gamma, beta, 15, 5, 3, want_y=True)
+    _, y1 = oracle.spectre_mix_local_gated(q, k, v, x, gate, one, gamma, beta, 15, 5, 3, want_y=True)
+    _, y0 = oracle.spectre_mix_local_gated(q, k, v, x, gate, zero, gamma, beta, 15, 5, 3, want_y=True)
+    gc = g.astype(np.float64).reshape(H, D)
+    assert np.abs(yg - (gc * y1 + (1 - gc) * y0)).max() <= 1e-12
 
 
 # ---------------------------------------------------------------- chunked mix
