@@ -27,13 +27,15 @@ SPECTRE_GATE_LOGIT = 1
 SPECTRE_GATE_COMPLEX = 2
 SPECTRE_NORM_POST = 0
 SPECTRE_NORM_PRE = 1
+SPECTRE_NORM_POST_RMS = 2
+SPECTRE_NORM_PRE_RMS = 3
 
 EXPORTS = ("spectre_mix_fwd", "spectre_mix_y", "spectre_mix_workspace_bytes", "spectre_mix_plan",
            "spectre_mix_release", "spectre_mix_trace_start", "spectre_mix_trace_stop",
            "spectre_mix_strerror", "spectre_mix_fwd_ex", "spectre_mix_y_ex",
            "spectre_mix_workspace_bytes_ex", "spectre_mix_fwd_chunked", "spectre_mix_y_chunked",
            "spectre_mix_fwd_local", "spectre_mix_local_attention", "spectre_mix_fwd_local_ex",
-           "spectre_mix_fwd_noalloc")
+           "spectre_mix_fwd_noalloc", "spectre_mix_fwd_local_gated")
 
 
 class SpectreError(RuntimeError):
@@ -98,6 +100,9 @@ def _load():
     lib.spectre_mix_fwd_local_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                              i64, i64, i64, ci, ci, ci, vp]
     lib.spectre_mix_fwd_local_ex.restype = ci
+    lib.spectre_mix_fwd_local_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                                i64, i64, i64, i64, ci, ci, ci, vp]
+    lib.spectre_mix_fwd_local_gated.restype = ci
     lib.spectre_mix_local_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ci,
                                                 vp]
     lib.spectre_mix_local_attention.restype = ci
@@ -206,6 +211,15 @@ def spectre_mix_fwd_local_ex(q, k, v, x, gate, gamma, beta, out, B, H, L, D, kee
                                          _addr(gamma), _addr(beta), _addr(out), B, H, L, D,
                                          keep_bins, win_left, win_right, dtype, gate_kind,
                                          norm_order, _stream(stream))
+
+
+def spectre_mix_fwd_local_gated(q, k, v, x, gate, mix, gamma, beta, out, B, H, L, D, keep_bins,
+                                win_left, win_right, dtype, gate_kind, norm_order,
+                                stream=None) -> int:
+    return _lib.spectre_mix_fwd_local_gated(_addr(q), _addr(k), _addr(v), _addr(x), _addr(gate),
+                                            _addr(mix), _addr(gamma), _addr(beta), _addr(out), B,
+                                            H, L, D, keep_bins, win_left, win_right, dtype,
+                                            gate_kind, norm_order, _stream(stream))
 
 
 def spectre_mix_local_attention(q, k, v, y, B, H, L, D, win_left, win_right, dtype,

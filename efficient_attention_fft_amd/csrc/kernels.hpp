@@ -1291,6 +1291,13 @@ __device__ __forceinline__ float wave_token_sums(float (&t)[Rp], int lane) {
 constexpr int next_pow2(int r) { return r <= 1 ? 1 : 2 * next_pow2((r + 1) / 2); }
 constexpr int ilog2(int r) { return r <= 1 ? 0 : 1 + ilog2(r / 2); }
 
+// The local branch joins y: y + y_loc, or with per-channel weights
+// g = mix[2 cp], mix[2 cp + 1] the gated form g y + (1 - g) y_loc.
+__device__ __forceinline__ float2 join_branches(float2 y, float2 yl, bool gated, float2 g) {
+  if (!gated) return cadd(y, yl);
+  return make_float2(g.x * y.x + (1.0f - g.x) * yl.x, g.y * y.y + (1.0f - g.y) * yl.y);
+}
+
 // ----------------------------------------- C1: inverse L1 DFT (+ LayerNorm)
 //
 // One thread per (b, m, pair): R = L1 loads U[b][k1][m][pair], an inverse
@@ -1312,6 +1319,8 @@ struct FinalParams {
   float eps;
   const float2* yblk;  // chunked mix: [B][CP2] term added to every token of batch (block) b, or null
   const float2* yloc;  // local branch: [B][L][CP2] term added to y, or null
+  const float* mix;    // with yloc: per-channel weight g, y <- g y + (1 - g) y_loc; null: y + y_loc
+  int rms;             // 1: RMSNorm (no mean subtracted), 0: LayerNorm
 };
 
 template <int R, int DT, bool FUSE, bool PRE = false>
@@ -1341,8 +1350,10 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
   const int64_t obase = (b * p.L + m) * p.CP2 + cp;
   const int64_t ostep = p.M * p.CP2;
   if (p.yloc != nullptr) {  // local branch: its output joins y
+    const bool gated = p.mix != nullptr;
+    const float2 g = gated ? make_float2(p.mix[2 * cp], p.mix[2 * cp + 1]) : make_float2(1.f, 1.f);
 #pragma unroll
-    for (int r = 0; r < R; ++r) z[r] = cadd(z[r], load_nt(p.yloc + obase + r * ostep));
+    for (int r = 0; r < R; ++r) z[r] = join_branches(z[r], load_nt(p.yloc + obase + r * ostep), gated, g);
   }
   if constexpr (!FUSE) {
 #pragma unroll
@@ -1363,24 +1374,24 @@ __global__ __launch_bounds__(256) void k_final(FinalParams p) {
 
     float t[Rp];
     float mean[R], rstd[R];
-    // pass 1: mean
-#pragma unroll
-    for (int r = 0; r < Rp; ++r) t[r] = r < R ? z[r].x + z[r].y : 0.f;
+    // pass 1: mean (times 0 for an RMSNorm, which subtracts none)
     {
+#pragma unroll
+      for (int r = 0; r < Rp; ++r) t[r] = r < R ? z[r].x + z[r].y : 0.f;
       float s = wave_token_sums<Rp>(t, lane);
       if ((lane & ((64 / Rp) - 1)) == 0) red[wave][lane / (64 / Rp)] = s;
       __syncthreads();
       if (threadIdx.x < Rp) {
         float a = 0.f;
         for (int w = 0; w < nw; ++w) a += red[w][threadIdx.x];
-        tot[threadIdx.x] = a * p.inv_c;
+        tot[threadIdx.x] = a * (p.rms ? 0.f : p.inv_c);
       }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < R; ++r) mean[r] = tot[r];
       __syncthreads();
     }
-    // pass 2: biased variance of the centred values
+    // pass 2: biased variance of the centred values (mean square for RMSNorm)
 #pragma unroll
     for (int r = 0; r < Rp; ++r) {
       if (r < R) {
@@ -1462,10 +1473,13 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   const int64_t obase = (b * p.L + m) * p.CP2 + cp + (int64_t)(Q * h) * ostep;
   auto toff = [&](int j) { return (int64_t)(j < Q ? j : j + Q) * ostep; };  // tok(j) - Q h
   if constexpr (ADD == 2) {  // local branch: its output joins y
+    const bool gated = p.mix != nullptr;
+    const float2 gw = gated ? make_float2(p.mix[2 * cp], p.mix[2 * cp + 1]) : make_float2(1.f, 1.f);
 #pragma unroll
     for (int g = 0; g < R2; g += 8) {
 #pragma unroll
-      for (int j = g; j < g + 8 && j < R2; ++j) z[j] = cadd(z[j], load_nt(p.yloc + obase + toff(j)));
+      for (int j = g; j < g + 8 && j < R2; ++j)
+        z[j] = join_branches(z[j], load_nt(p.yloc + obase + toff(j)), gated, gw);
       asm volatile("" ::: "memory");
     }
   }
@@ -1481,6 +1495,7 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   }
 
   // per-token sums over the workgroup's pairs: lane c ends with slot c's total
+  const float mean_w = p.rms ? 0.f : p.inv_c;  // an RMSNorm subtracts no mean
   auto token_sums = [&](float (&t)[T2], float* dst, bool is_var) __attribute__((always_inline)) {
     halve_sums<T2, 16>(t, lane);
     if (c < R2) red[wave][tok(c)] = t[0];
@@ -1488,11 +1503,11 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
     if (tid < R) {
       float a = 0.f;
       for (int w = 0; w < nw; ++w) a += red[w][tid];
-      dst[tid] = is_var ? 1.0f / sqrtf(a * p.inv_c + p.eps) : a * p.inv_c;
+      dst[tid] = is_var ? 1.0f / sqrtf(a * p.inv_c + p.eps) : a * mean_w;
     }
     __syncthreads();
   };
-  {
+  {  // the mean, times 0 for an RMSNorm (straight-line code either way)
     float t[T2];
 #pragma unroll
     for (int n = 0; n < T2; ++n) t[n] = n < R2 ? z[n].x + z[n].y : 0.f;
@@ -1541,6 +1556,8 @@ struct NormParams {
   const float2* yblk;  // chunked mix: [ntok / Lb][CP2] block term added to y, or null
   int64_t Lb;          // tokens per block
   const float2* yloc;  // local branch: [ntok][CP2] term added to y, or null
+  const float* mix;    // with yloc: per-channel weight g, y <- g y + (1 - g) y_loc; null: y + y_loc
+  int rms;             // 1: RMSNorm (no mean subtracted), 0: LayerNorm
 };
 
 template <int DT, bool PRE = false>
@@ -1558,12 +1575,16 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
     if (c < p.CP2) {
       z[it] = load_nt(p.y + base + c);
       if (p.yblk != nullptr) z[it] = cadd(z[it], p.yblk[(tok / p.Lb) * p.CP2 + c]);
-      if (p.yloc != nullptr) z[it] = cadd(z[it], load_nt(p.yloc + base + c));
+      if (p.yloc != nullptr) {
+        const bool gated = p.mix != nullptr;
+        const float2 g = gated ? make_float2(p.mix[2 * c], p.mix[2 * c + 1]) : make_float2(1.f, 1.f);
+        z[it] = join_branches(z[it], load_nt(p.yloc + base + c), gated, g);
+      }
       if constexpr (!PRE) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
   }
-  const float mean = wave_sum(s) * p.inv_c;
+  const float mean = p.rms ? 0.f : wave_sum(s) * p.inv_c;  // an RMSNorm subtracts none
   float q = 0.f;
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) {

@@ -380,6 +380,7 @@ struct Chunk {
 // Local branch: keys t - wl .. t + wr of token t (clipped to the sequence).
 struct Local {
   int64_t wl, wr;
+  const float* mix;  // per-channel gate of the two branches, or null (summed)
 };
 
 int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dtype, Shape& s,
@@ -389,7 +390,7 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   if (gate_kind != SPECTRE_GATE_REAL && gate_kind != SPECTRE_GATE_LOGIT &&
       gate_kind != SPECTRE_GATE_COMPLEX)
     return SPECTRE_EINVAL;
-  if (norm_order != SPECTRE_NORM_POST && norm_order != SPECTRE_NORM_PRE) return SPECTRE_EINVAL;
+  if (norm_order < SPECTRE_NORM_POST || norm_order > SPECTRE_NORM_PRE_RMS) return SPECTRE_EINVAL;
   if (L % 2 != 0) return SPECTRE_EINVAL;
   if (keep < 0 || keep > L / 2 + 1) return SPECTRE_EINVAL;
   if (H > kMaxC || D > kMaxC || H * D > kMaxC) return SPECTRE_EUNSUPPORTED;
@@ -1007,7 +1008,9 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
 
   const float inv_c = (float)(1.0 / (double)s.C);
   const float eps = 1e-5f;
-  const bool pre = s.norm_order == SPECTRE_NORM_PRE;
+  const bool pre = (s.norm_order & 1) != 0;  // bit 0: order, bit 1: RMSNorm
+  const int rms = (s.norm_order & 2) != 0 ? 1 : 0;
+  const float* mix = local ? local->mix : nullptr;
   if (single) {
     if (!want_out) return SPECTRE_OK;
     NormParams n{};
@@ -1023,6 +1026,8 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
     n.yblk = yblk;  // chunked mix: the block term joins y here
     n.Lb = s.L;
     n.yloc = yloc;  // local branch: joins y here
+    n.mix = mix;
+    n.rms = rms;
     return launch_norm(n, s.dtype, pre, st);
   }
 
@@ -1053,6 +1058,8 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
   f.eps = eps;
   f.yblk = yblk;  // chunked mix: the block term joins y in C1
   f.yloc = fuse ? yloc : nullptr;  // local branch: joins y in the fused C1, else in the norm
+  f.mix = mix;
+  f.rms = rms;
   // y for a separate LayerNorm: k's spectrum region is free once B has run
   float* ybuf = want_out ? reinterpret_cast<float*>(T + pairs) : y;
   if (fuse) {
@@ -1075,6 +1082,8 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
   n.inv_c = inv_c;
   n.eps = eps;
   n.yloc = yloc;
+  n.mix = mix;
+  n.rms = rms;
   return launch_norm(n, s.dtype, pre, st);
 }
 
@@ -1097,6 +1106,28 @@ int check_chunked(int64_t B, int64_t H, int64_t L, int64_t D, int64_t fft_len, i
   ch.keep_blocks = keep_blocks;
   ch.B = B;
   return SPECTRE_OK;
+}
+
+// The mix with the local branch, summed (mix null) or gated per channel.
+int local_call(const void* q, const void* k, const void* v, const void* x, const float* gate,
+               const float* mix, const float* gamma, const float* beta, void* out, int64_t B,
+               int64_t H, int64_t L, int64_t D, int64_t keep_bins, int64_t win_left,
+               int64_t win_right, int dtype, int gate_kind, int norm_order, hipStream_t stream) {
+  if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
+  if (win_left < 0 || win_right < 0) return SPECTRE_EINVAL;
+  Shape s;
+  Plan pl;
+  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl, gate_kind, norm_order);
+  if (rc) return rc;
+  if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
+  const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECTRE_EINVAL;
+  const size_t tb = (size_t)s.N * s.esz;
+  for (const void* p : {q, k, v, x})
+    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
+  const Local lw{win_left, win_right, mix};
+  return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream, nullptr, &lw);
 }
 
 // ------------------------------------------- allocation-free entry point
@@ -1279,26 +1310,23 @@ int spectre_mix_y_chunked(const void* q, const void* k, const void* v, const flo
   return run(q, k, v, nullptr, gate, nullptr, nullptr, nullptr, y, s, pl, stream, &ch);
 }
 
+int spectre_mix_fwd_local_gated(const void* q, const void* k, const void* v, const void* x,
+                                const float* gate, const float* mix, const float* gamma,
+                                const float* beta, void* out, int64_t B, int64_t H, int64_t L,
+                                int64_t D, int64_t keep_bins, int64_t win_left, int64_t win_right,
+                                int dtype, int gate_kind, int norm_order, hipStream_t stream) {
+  if (!mix || !aligned16(mix)) return SPECTRE_EINVAL;
+  return local_call(q, k, v, x, gate, mix, gamma, beta, out, B, H, L, D, keep_bins, win_left,
+                    win_right, dtype, gate_kind, norm_order, stream);
+}
+
 int spectre_mix_fwd_local_ex(const void* q, const void* k, const void* v, const void* x,
                              const float* gate, const float* gamma, const float* beta, void* out,
                              int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
                              int64_t win_left, int64_t win_right, int dtype, int gate_kind,
                              int norm_order, hipStream_t stream) {
-  if (!q || !k || !v || !x || !gate || !gamma || !beta || !out) return SPECTRE_EINVAL;
-  if (win_left < 0 || win_right < 0) return SPECTRE_EINVAL;
-  Shape s;
-  Plan pl;
-  int rc = check_shape(B, H, L, D, keep_bins, dtype, s, pl, gate_kind, norm_order);
-  if (rc) return rc;
-  if (!local_shape_ok(s)) return SPECTRE_EUNSUPPORTED;
-  const void* ptrs[] = {q, k, v, x, gate, gamma, beta, out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SPECTRE_EINVAL;
-  const size_t tb = (size_t)s.N * s.esz;
-  for (const void* p : {q, k, v, x})
-    if (overlaps(out, tb, p, tb)) return SPECTRE_EINVAL;
-  const Local lw{win_left, win_right};
-  return run(q, k, v, x, gate, gamma, beta, out, nullptr, s, pl, stream, nullptr, &lw);
+  return local_call(q, k, v, x, gate, nullptr, gamma, beta, out, B, H, L, D, keep_bins, win_left,
+                    win_right, dtype, gate_kind, norm_order, stream);
 }
 
 int spectre_mix_fwd_local(const void* q, const void* k, const void* v, const void* x,

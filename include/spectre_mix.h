@@ -87,14 +87,24 @@ typedef enum {
 } spectre_gate_kind;
 
 /*
- * Where the LayerNorm sits (the *_ex entry points; the others use POST).
+ * Where the norm sits and which norm it is (the *_ex entry points; the
+ * others use POST).  Bit 0 is the order, bit 1 the norm:
  *  SPECTRE_NORM_POST: out = LayerNorm(x + y)   (section 2.2's pseudocode)
  *  SPECTRE_NORM_PRE:  out = x + LayerNorm(y)   (the order section 3.3 settles
  *                     on: the inverse FFT output is normalised, then added
  *                     to x), the same LayerNorm (eps 1e-5, biased variance,
  *                     gamma, beta) applied to y alone.
+ *  SPECTRE_NORM_POST_RMS, SPECTRE_NORM_PRE_RMS: the same orders with
+ *                     RMSNorm (section 3.3 allows RMSNorm or LayerNorm):
+ *                     z / sqrt(mean_c(z^2) + 1e-5) * gamma + beta, no mean
+ *                     subtracted (beta = 0 gives the textbook RMSNorm).
  */
-typedef enum { SPECTRE_NORM_POST = 0, SPECTRE_NORM_PRE = 1 } spectre_norm_order;
+typedef enum {
+  SPECTRE_NORM_POST = 0,
+  SPECTRE_NORM_PRE = 1,
+  SPECTRE_NORM_POST_RMS = 2,
+  SPECTRE_NORM_PRE_RMS = 3
+} spectre_norm_order;
 
 typedef enum {
   SPECTRE_OK = 0,
@@ -229,6 +239,23 @@ int spectre_mix_fwd_local_ex(const void* q, const void* k, const void* v, const 
                              int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep_bins,
                              int64_t win_left, int64_t win_right, int dtype, int gate_kind,
                              int norm_order, hipStream_t stream);
+
+/*
+ * spectre_mix_fwd_local_ex with the two branches gated instead of summed
+ * (SPECTRE article, section 4.3: the FFT and sliding-window outputs summed
+ * or gated; read as a learned per-channel weight): the branch sum becomes
+ *   g_c * y + (1 - g_c) * y_loc,   g_c = mix[c], c = h * D + d,
+ * before the residual and the norm of norm_order.  mix: device, H * D
+ * float32, 16-byte aligned, read only, owned by the caller; the values are
+ * used as given (g = 1 keeps y alone, g = 0 y_loc alone; nothing is
+ * clipped).  Every other argument, the workspace and the errors as
+ * spectre_mix_fwd_local_ex; a null mix returns SPECTRE_EINVAL.
+ */
+int spectre_mix_fwd_local_gated(const void* q, const void* k, const void* v, const void* x,
+                                const float* gate, const float* mix, const float* gamma,
+                                const float* beta, void* out, int64_t B, int64_t H, int64_t L,
+                                int64_t D, int64_t keep_bins, int64_t win_left, int64_t win_right,
+                                int dtype, int gate_kind, int norm_order, hipStream_t stream);
 
 /*
  * The local branch alone, the test hook of spectre_mix_fwd_local:

@@ -84,7 +84,7 @@ def fwd_ex(gate_kind, norm_order, **kw):
                                  a["dtype"], gate_kind, norm_order, 0)
 
 
-@pytest.mark.parametrize("gate_kind,norm_order", [(3, 0), (-1, 0), (0, 2), (2, -1)])
+@pytest.mark.parametrize("gate_kind,norm_order", [(3, 0), (-1, 0), (0, 4), (2, -1)])
 def test_fwd_ex_rejects_unknown_variant(gate_kind, norm_order):
     assert fwd_ex(gate_kind, norm_order) == sm.SPECTRE_EINVAL
     assert sm.spectre_mix_y_ex(GOOD, GOOD + 0x1000000, GOOD + 0x2000000, GOOD + 0x4000000,
@@ -130,7 +130,7 @@ def test_local_rejects_before_device():
     assert mix(D=48, H=8) == sm.SPECTRE_EUNSUPPORTED     # head size the kernel lacks
     assert mix(L=65535, keep=1) == sm.SPECTRE_EINVAL      # checked like spectre_mix_fwd
     assert mix(out=GOOD + 0x3000000) == sm.SPECTRE_EINVAL  # out == x
-    for gk, no in ((3, 0), (0, 2), (-1, 0)):  # unknown gate kind or norm order
+    for gk, no in ((3, 0), (0, 4), (-1, 0)):  # unknown gate kind or norm order
         assert sm.spectre_mix_fwd_local_ex(GOOD, GOOD + 0x1000000, GOOD + 0x2000000,
                                            GOOD + 0x3000000, GOOD + 0x4000000, GOOD + 0x5000000,
                                            GOOD + 0x6000000, GOOD + 0x70000000, 1, 8, 65536, 64,
@@ -142,6 +142,21 @@ def test_local_rejects_before_device():
         return sm.spectre_mix_local_attention(a["q"], GOOD + 0x400000, GOOD + 0x800000, a["y"],
                                               a["B"], a["H"], a["L"], a["D"], a["wl"], a["wr"],
                                               a["dt"], 0)
+
+    def gated(mix=GOOD + 0x6800000, no=0, **kw):
+        a = dict(B=1, H=8, L=65536, D=64, keep=32769, wl=64, wr=64, dt=0)
+        a.update(kw)
+        return sm.spectre_mix_fwd_local_gated(GOOD, GOOD + 0x1000000, GOOD + 0x2000000,
+                                              GOOD + 0x3000000, GOOD + 0x4000000, mix,
+                                              GOOD + 0x5000000, GOOD + 0x6000000, GOOD + 0x70000000,
+                                              a["B"], a["H"], a["L"], a["D"], a["keep"], a["wl"],
+                                              a["wr"], a["dt"], 0, no, 0)
+    assert gated(mix=0) == sm.SPECTRE_EINVAL               # the branch weights are required
+    assert gated(mix=GOOD + 0x6800004) == sm.SPECTRE_EINVAL  # misaligned
+    assert gated(no=4) == sm.SPECTRE_EINVAL
+    assert gated(wl=-1) == sm.SPECTRE_EINVAL
+    assert gated(D=48) == sm.SPECTRE_EUNSUPPORTED
+
     assert attn(L=0) == sm.SPECTRE_EINVAL
     assert attn(wl=-1) == sm.SPECTRE_EINVAL
     assert attn(dt=2) == sm.SPECTRE_EINVAL

@@ -202,6 +202,64 @@ def test_mix_with_local_branch_variants(B, L, H, D, dt, keep, wl, wr, gk, no):
     assert np.all(np.isfinite(got)) and err <= tol(w)
 
 
+GATED_CASES = [
+    # (B, L, H, D, dtype, keep_bins, win_left, win_right, gate_kind, norm_order)
+    (1, 16384, 8, 64, 0, 4097, 64, 64, 0, 0),    # 16 x 1024, fused inverse, LayerNorm
+    (1, 65536, 4, 64, 0, 30000, 64, 64, 0, 3),   # 64 x 1024, split fused inverse, pre RMSNorm
+    (1, 49152, 8, 64, 1, 12289, 128, 0, 1, 2),   # 48 x 1024, split, bf16, logit gate, RMSNorm
+    (1, 2048, 2, 16, 0, 900, 40, 40, 2, 1),      # single level, LayerNorm pass, complex gate, pre
+    (1, 16384, 2, 32, 0, 3000, 64, 63, 0, 2),    # unfused inverse + norm pass, RMSNorm
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep,wl,wr,gk,no", GATED_CASES)
+def test_mix_with_gated_local_branch(B, L, H, D, dt, keep, wl, wr, gk, no):
+    """spectre_mix_fwd_local_gated: the two branches weighted per channel
+    (g y + (1 - g) y_loc, channel 0 at g = 1 and channel 1 at g = 0), on
+    each inverse / norm path, with LayerNorm and RMSNorm in both orders."""
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.custom(660 + L % 79, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=keep, affine=True)
+    say("case", w.describe(), "window", wl, wr, "gate kind", gk, "norm order", no, "gated")
+    inp = workloads.make_inputs(w)
+    gate = workloads.make_gate(w, gk)
+    mix = workloads.make_branch_mix(w)
+    ref = oracle.spectre_mix_local_gated(inp["q"], inp["k"], inp["v"], inp["x"], gate, mix,
+                                         inp["gamma"], inp["beta"], keep, wl, wr, dtype=dt,
+                                         nthreads=oracle_threads(), gate_kind=gk, norm_order=no)
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, m, gam, bet = dev(gate), dev(mix), dev(inp["gamma"]), dev(inp["beta"])
+    _, out = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_local_gated(q, k, v, x, g, m, gam, bet, out, B, H, L, D, keep,
+                                            wl, wr, dt, gk, no))
+    t.cuda.synchronize()
+    got = to_host_f64(out, dt).reshape(ref.shape)
+    err = np.abs(got - ref).max()
+    say("  out max-abs err %.3g (tol %.1g)" % (err, tol(w)))
+    assert np.all(np.isfinite(got)) and err <= tol(w)
+
+
+def test_gate_of_one_keeps_the_fft_branch_alone():
+    """Every branch weight 1: the gated mix is the FFT mix without the local
+    branch (spectre_mix_fwd_ex, RMSNorm post-norm), to rounding."""
+    import efficient_attention_fft_amd as sm
+    t = torch()
+    w = workloads.custom(671, B=1, L=16384, H=4, D=64, dtype=0, keep_bins=5000, affine=True)
+    inp = workloads.make_inputs(w)
+    q, k, v, x = (dev(inp[n]) for n in "qkvx")
+    g, gam, bet = dev(inp["gate"]), dev(inp["gamma"]), dev(inp["beta"])
+    ones = dev(np.ones(w.C, np.float32))
+    _, a = empty_like_storage(w)
+    _, b = empty_like_storage(w)
+    sm.check(sm.spectre_mix_fwd_ex(q, k, v, x, g, gam, bet, a, w.B, w.H, w.L, w.D, 5000, 0, 0, 2))
+    sm.check(sm.spectre_mix_fwd_local_gated(q, k, v, x, g, ones, gam, bet, b, w.B, w.H, w.L, w.D,
+                                            5000, 64, 64, 0, 0, 2))
+    t.cuda.synchronize()
+    err = (a - b).abs().max().item()
+    say("  gate 1 vs FFT branch alone: max-abs diff %.3g" % err)
+    assert err <= 1e-5
+
+
 def test_local_plain_entry_is_the_real_post_variant():
     """spectre_mix_fwd_local and spectre_mix_fwd_local_ex(REAL, POST) agree bit for bit."""
     import efficient_attention_fft_amd as sm

@@ -1,7 +1,8 @@
 """The variant entry points on the GPU against the oracle: a logit gate
 (sigmoid applied in the kernels), a complex gate (the SPECTRE article's
-section 2.4 rotation inside G(f)), and the pre-norm order out = x + LN(y)
-(section 3.3), through spectre_mix_fwd_ex / spectre_mix_y_ex.
+section 2.4 rotation inside G(f)), the pre-norm order out = x + LN(y) and
+RMSNorm in place of LayerNorm in either order (section 3.3), through
+spectre_mix_fwd_ex / spectre_mix_y_ex.
 
 Tolerances as for the plain mix: max-abs on out 1e-4 (binary32 storage) and
 2e-2 (bfloat16 storage); y within 1e-4 * max(1, max|y|).  The shapes cover
@@ -22,7 +23,8 @@ from gpu_util import (DeviceInputs, empty_like_storage, oracle_threads, to_host_
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [(1, 0), (2, 0), (0, 1), (2, 1)]  # (gate kind, norm order)
+# (gate kind, norm order); norm order bit 0 = pre-norm, bit 1 = RMSNorm
+VARIANTS = [(1, 0), (2, 0), (0, 1), (2, 1), (0, 2), (1, 3)]
 
 SHAPES = [
     # (B, L, H, D, dtype, keep)  keep None = no truncation

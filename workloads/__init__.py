@@ -233,6 +233,15 @@ def make_gate(w: Workload, gate_kind: int) -> np.ndarray:
 
 
 _GATE_BLOCK_SEED, _GATE_BLOCKS_SEED = 54, 55
+_BRANCH_MIX_SEED = 56
+
+
+def make_branch_mix(w: Workload) -> np.ndarray:
+    """Per-channel weights of the gated branch sum, [H*D] float32 ~ U[0, 1),
+    with channel 0 at 1 and channel 1 at 0 (each branch alone)."""
+    g = uniform(w.seed(_BRANCH_MIX_SEED), (w.C,)).astype(np.float32)
+    g[0], g[1] = 1.0, 0.0
+    return g
 
 
 def make_chunk_gates(w: Workload, fft_len: int):
