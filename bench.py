@@ -66,12 +66,15 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_bytes(name: str, w, gate_kind: int = 0, local: bool = False) -> int:
+def kernel_bytes(name: str, w, gate_kind: int = 0, local: bool = False,
+                 norm_order: int = 0) -> int:
     """Algorithmic HBM bytes of one launch of a pass: every tensor element the
     pass must read or write once (inputs, the spectra it exchanges, outputs,
     the kept gate bins).  A complex gate has 8 bytes per bin, so its gate and
     gate-table bytes double.  With the local branch the pass that normalises
-    also reads y_loc (4 bytes per element)."""
+    also reads y_loc (4 bytes per element).  The single-pass column kernel
+    (L = 3072, 4096) of a post-norm call without the local branch reads x and
+    stores x + y, so its norm pass reads that one tensor."""
     N = w.N
     s = w.elem_bytes
     spec = 4 * N  # one tensor's spectrum as binary32 complex channel pairs
@@ -94,6 +97,9 @@ def kernel_bytes(name: str, w, gate_kind: int = 0, local: bool = False) -> int:
         if l3 in (256, 1024):
             gate = gb * w.H * w.L  # the gate table A1's launch writes
         return 3 * spec + spec + gate
+    fold = (norm_order & 1) == 0 and not local
+    if name == "B_col":  # q, k, v read once, the kept gate bins, y (or x + y) written
+        return 3 * N * s + gate + spec + (N * s if fold else 0)
     if name == "C2_inv_strided":
         return 2 * spec
     yl = 4 * N if local else 0
@@ -102,6 +108,8 @@ def kernel_bytes(name: str, w, gate_kind: int = 0, local: bool = False) -> int:
     if name == "C1_inv":
         return 2 * spec
     if name == "LN_norm":
+        if fold and w.L in (3072, 4096):  # x + y from the column kernel
+            return spec + N * s + 8 * w.C
         return spec + 2 * N * s + 8 * w.C + yl
     if name == "L_local":  # q, k, v read once; y_loc (binary32) written
         return 3 * N * s + 4 * N
@@ -308,7 +316,7 @@ def run_bench(args):
     nl = launches[dom]
     # the chunked mix transforms blocks of F tokens: the passes follow that plan
     wk = w if not F else dataclasses.replace(w, B=w.B * (w.L // F), L=F, keep_bins=F // 2 + 1)
-    dom_bytes = kernel_bytes(dom, wk, gk, local=bool(win)) / nl  # per launch
+    dom_bytes = kernel_bytes(dom, wk, gk, local=bool(win), norm_order=no) / nl  # per launch
     avg_ms = per_kernel[dom] / nl
     achieved = dom_bytes / (avg_ms * 1e-3) / 1e9
     traffic = traffic_for(dom, w) if gk == 0 and no == 0 and not F and not win else None
@@ -492,8 +500,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate-kind", type=int, default=0, choices=[0, 1, 2],
                     help="0 real gate, 1 logit gate (sigmoid in the kernels), 2 complex gate")
-    ap.add_argument("--norm-order", type=int, default=0, choices=[0, 1],
-                    help="0 out = LN(x + y), 1 out = x + LN(y)")
+    ap.add_argument("--norm-order", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="0 out = LN(x + y), 1 out = x + LN(y); 2, 3: the same with RMSNorm")
     ap.add_argument("--fft-len", type=int, default=0,
                     help="chunked mix with blocks of this many tokens (0: one block, the plain mix)")
     ap.add_argument("--window", type=int, default=0,

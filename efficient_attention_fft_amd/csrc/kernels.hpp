@@ -25,8 +25,9 @@
 //       L2 = 1, standing in for C2's twiddle)                          -> U (in place)
 //   C2  inverse L2-point DFT over k2, times w_L^{-m k1}                (in place)
 //   C1  inverse L1-point DFT over k1, residual, LayerNorm              -> out
-// M = L2 L3.  A pass whose size is 1 is skipped.  For L <= 4096 the whole
-// column fits one workgroup's LDS and only B runs (then a LayerNorm pass).
+// M = L2 L3.  A pass whose size is 1 is skipped.  For L <= 2048, and for
+// L = 3072 and 4096 (the single-pass column kernel k_col), the whole column
+// fits one workgroup's LDS and only B runs (then a LayerNorm pass).
 //
 // Separating the two packed real spectra needs Z[f] and Z[L-f]; f and L-f
 // always sit in a column pair {(k1, k2), (k1', k2')} (or in one self-paired
@@ -88,6 +89,18 @@ __device__ __forceinline__ float2 load_pair_u(const char* ubase, uint32_t off) {
     return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
   } else {
     return load_nt(reinterpret_cast<const float2*>(ubase + off));
+  }
+}
+
+// The same with a plain (cached) load: for rows whose 128-byte lines are
+// shared by several workgroups, which must find them in L2.
+template <int IN>
+__device__ __forceinline__ float2 load_pair_c(const char* ubase, uint32_t off) {
+  if constexpr (IN == IN_BF16) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(ubase + off);
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float2*>(ubase + off);
   }
 }
 
@@ -1250,6 +1263,259 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
   }
 }
 
+// ------------------------------ single-pass column kernel, L = RA * RB * RC
+//
+// For L up to 8192 a channel pair's whole column fits in LDS, so one
+// workgroup runs the whole spectral path for CPT neighbouring channel pairs
+// of one batch element: q, k and v read once (CPT * 8 bytes of every row),
+// three forward transforms, the spectral product, the inverse, y written
+// once.  The norm runs as its own pass, since it needs every channel of a
+// token.  The L-point transform is three register-DFT stages joined by two
+// LDS exchanges (a four-step split applied twice):
+//   n = a + TA jA (TA = RB RC),  a = b + RC jB,  f = kA + RA (kB + RB kC)
+//   A  thread a < TA:             DFT_RA over jA, times w_L^{a kA}
+//   B  thread b + RC kA < TB:     DFT_RB over jB, times w_L^{RA b kB}
+//   C  thread kA + RA kB < TC:    DFT_RC over b  -> X[f], f = t + TC kC
+// (TB = L / RB, TC = L / RC).  Per pair, in binary32 pairs, the A -> B
+// exchange sits at kA TA + a and the B -> C exchange at (kA + RA kB)(RC + 1)
+// + b: the pad of one element per C thread makes both the strided writes
+// and the transposed reads hit distinct banks.  Bins go through LDS in
+// natural order for the mirror reads of the product and for the inverse.
+// A wave's lanes take 16 consecutive column threads of each of its pairs,
+// and the pair regions are REGION = 16 (mod 32) elements apart, so every
+// exchange touches distinct banks per 16 lanes (32 banks) and per 32 lanes
+// (64 banks).  Twiddle powers come from one table value per stage by repeated
+// multiplication (at most RA - 2 products, a few units of binary32
+// rounding).
+//
+// Measured on MI355X at L = 4096 (B = 4, H*D = 512): about 4100 VALU
+// instructions per thread (28 us of issue per CU), 10 us of LDS exchanges and
+// the HBM traffic do not overlap, since one 1024-thread workgroup per CU
+// moves through them in lockstep; loading the next tensor during a transform
+// (registers) gained nothing there and is not done.
+
+template <int RA_, int RB_, int RC_, int CPT>
+struct ColCfg {
+  static constexpr int RA = RA_, RB = RB_, RC = RC_;
+  static constexpr int N = RA * RB * RC;
+  static constexpr int TA = N / RA, TB = N / RB, TC = N / RC;
+  static constexpr int TP = TA > TB ? (TA > TC ? TA : TC) : (TB > TC ? TB : TC);
+  static constexpr int THREADS = CPT * TP;
+  static constexpr int VMAX = RA > RB ? (RA > RC ? RA : RC) : (RB > RC ? RB : RC);
+  static constexpr int NH = RC / 2 + 1;  // product slots of a C thread
+  static constexpr int region() {
+    int r = N + TC;
+    while (r % 32 != 16) ++r;
+    return r;
+  }
+  static constexpr int REGION = region();
+  static constexpr size_t LDS_BYTES = (size_t)CPT * REGION * sizeof(float2);
+  // waves per SIMD to allow: two workgroups per CU when their LDS fits
+  static constexpr int WAVES_PER_EU = (THREADS / 256) * (2 * LDS_BYTES <= 160 * 1024 ? 2 : 1);
+  static_assert(RC % 2 == 0, "the product pairs bins t + TC i with i < RC / 2");
+  static_assert(THREADS <= 1024 && THREADS % (16 * CPT) == 0, "one workgroup of whole lane groups");
+};
+
+struct ColParams {
+  const void* in[3];   // q, k, v: [B][L][CP2] channel pairs (storage kind IN)
+  const void* x;       // residual (storage kind IN) added to y before the store, or null
+  float2* out;         // y, or x + y: [B][L][CP2] binary32 pairs
+  const float* gate;   // [H][nbins] (pairs for a complex gate)
+  const float2* tw;    // tw[e] = exp(-2 pi i e / L), e < L
+  int gate_kind;
+  int CP2, D, keep, nbins;
+  float scale;         // 1 / (8 L^2): the mix's 1/L, the inverse's 1/L, (1/2)^3 of the split
+  // chunked mix: bin 0 of each tensor times dc_scale to dc[x * dc_stride + b * CP2 + pair]
+  float2* dc;
+  int64_t dc_stride;
+  float dc_scale;
+};
+
+// v[k] *= w^k, k = 1 .. R - 1.  The base is passed through an empty asm
+// statement so that the powers are recomputed at each use: otherwise the
+// compiler merges the identical powers of every transform of the kernel and
+// keeps all of them live across it, which costs more registers than the
+// multiplications.
+template <int R>
+__device__ __forceinline__ void twiddle_powers(float2* v, float2 w) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y));
+  float2 t = w;
+#pragma unroll
+  for (int k = 1; k < R; ++k) {
+    v[k] = cmul(v[k], t);
+    if (k + 1 < R) t = cmul(t, w);
+  }
+}
+
+// The L-point transform of one pair's column.  On entry thread t < TA holds
+// v[j] = x[t + TA j]; on exit thread t < TC holds v[kC] = X[t + TC kC].  The
+// caller makes sure the region is free on entry; on exit the C stage's LDS
+// reads are issued (the caller synchronises before the region is reused).
+template <class C, int SIGN>
+__device__ __forceinline__ void col_fft(float2 (&v)[C::VMAX], float2* col, int t, float2 wa,
+                                        float2 wb) {
+  if (t < C::TA) {
+    dft<C::RA, SIGN>(v);
+    twiddle_powers<C::RA>(v, wa);
+#pragma unroll
+    for (int k = 0; k < C::RA; ++k) col[k * C::TA + t] = v[k];
+  }
+  __syncthreads();
+  const int b = t % C::RC, kA = t / C::RC;
+  if (t < C::TB) {
+#pragma unroll
+    for (int j = 0; j < C::RB; ++j) v[j] = col[kA * C::TA + b + C::RC * j];
+  }
+  __syncthreads();
+  if (t < C::TB) {
+    dft<C::RB, SIGN>(v);
+    twiddle_powers<C::RB>(v, wb);
+#pragma unroll
+    for (int k = 0; k < C::RB; ++k) col[(kA + C::RA * k) * (C::RC + 1) + b] = v[k];
+  }
+  __syncthreads();
+  if (t < C::TC) {
+#pragma unroll
+    for (int j = 0; j < C::RC; ++j) v[j] = col[t * (C::RC + 1) + j];
+    dft<C::RC, SIGN>(v);
+  }
+}
+
+template <int RA, int RB, int RC, int CPT, int IN>
+__global__ __launch_bounds__((ColCfg<RA, RB, RC, CPT>::THREADS), (ColCfg<RA, RB, RC, CPT>::WAVES_PER_EU))
+void k_col(ColParams p) {
+  using C = ColCfg<RA, RB, RC, CPT>;
+  constexpr int N = C::N;
+  extern __shared__ float2 lds[];
+  // one-dimensional grid: item = pair block + nblk * batch element, XCD-grouped
+  const int nblk = (p.CP2 + CPT - 1) / CPT;
+  const int item = xcd_grouped_block().x;
+  // lanes: 16 consecutive column threads per pair, the CPT pairs side by side
+  const int tid = threadIdx.x;
+  const int pr = (tid >> 4) % CPT, t = (tid & 15) + 16 * (tid / (16 * CPT));
+  const int cp = (item % nblk) * CPT + pr;
+  const bool live = cp < p.CP2;  // a ragged last block computes on zeros and stores nothing
+  const int64_t b = item / nblk;
+  float2* col = lds + pr * C::REGION;
+  // rows of this batch element: a uniform base per row group and one 32-bit
+  // lane offset (a batch element spans L * CP2 pairs, below 2^29)
+  const int64_t gbase = b * N * p.CP2;
+  const uint32_t rowb = (uint32_t)p.CP2 * pair_bytes<IN>();  // bytes per row, input
+  // Every row load is issued by every lane, from a clamped in-bounds address
+  // (row t or 0, pair cp or CP2 - 1), and zeroed afterwards where it is not
+  // wanted: loads under a branch would leave the number of younger loads in
+  // flight unknown, and the wait for the oldest would then drain them all.
+  const int cpc = live ? cp : p.CP2 - 1;
+  const uint32_t loff_a = ((uint32_t)(t < C::TA ? t : 0) * p.CP2 + cpc) * pair_bytes<IN>();
+  const uint32_t loff_c = ((uint32_t)(t < C::TC ? t : 0) * p.CP2 + cpc) * pair_bytes<IN>();
+  const bool want_a = t < C::TA && live;
+
+  // twiddle bases, loaded before the rows: a wait for them then drains nothing else
+  const float2 wa = p.tw[t < C::TA ? t : 0];
+  const float2 wb = p.tw[C::RA * (t % C::RC)];
+
+  float2 nxt[C::RA];
+  auto load_rows = [&](const void* src) __attribute__((always_inline)) {
+    const char* ub = static_cast<const char*>(src) + gbase * pair_bytes<IN>();
+#pragma unroll
+    for (int j = 0; j < C::RA; ++j) {
+      const float2 r = load_pair_c<IN>(ub + (size_t)j * C::TA * rowb, loff_a);
+      nxt[j] = want_a ? r : make_float2(0.f, 0.f);
+    }
+  };
+  load_rows(p.in[0]);
+
+  // mirror bin L - f of f = t + TC i (i < RC/2) at mcol[TC (RC/2 - 1 - i)],
+  // a base and positive immediate offsets; f = 0 and f = L/2 are their own
+  // mirrors
+  float2* const mcol = col + (N - t - C::TC * (RC / 2 - 1));
+  auto mirror_at = [](float2* mc, float2* c, int t, int i) __attribute__((always_inline)) -> float2* {
+    if (i == RC / 2) return c + N / 2;
+    if (i == 0 && t == 0) return c;
+    return mc + C::TC * (RC / 2 - 1 - i);
+  };
+  float2 v[C::VMAX];
+  float2 sa[C::NH], sb[C::NH];
+  const int ha = live ? (2 * cp) / p.D : 0, hb = live ? (2 * cp + 1) / p.D : 0;  // heads
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    if (x > 0) load_rows(p.in[x]);
+#pragma unroll
+    for (int j = 0; j < C::RA; ++j) v[j] = nxt[j];
+    if (x > 0) __syncthreads();  // the previous tensor's mirror reads are done
+    col_fft<C, -1>(v, col, t, wa, wb);
+    __syncthreads();  // every C-stage read is done before the bins overwrite the region
+    if (t < C::TC) {
+#pragma unroll
+      for (int i = 0; i < RC; ++i) col[t + C::TC * i] = v[i];
+    }
+    if (p.dc != nullptr && t == 0 && live)  // bin 0
+      p.dc[x * p.dc_stride + b * p.CP2 + cp] = cscale(v[0], p.dc_scale);
+    __syncthreads();
+    if (t < C::TC) {
+      // bin pairs (f, L - f), f = t + TC i for i < RC/2, and f = L/2 (t = 0):
+      // 2A = Z[f] + conj Z[L-f], 2B = -i (Z[f] - conj Z[L-f])
+#pragma unroll
+      for (int i = 0; i < C::NH; ++i) {
+        if (i == RC / 2 && t != 0) continue;
+        const int f = t + C::TC * i;
+        const float2 z = v[i], zm = *mirror_at(mcol, col, t, i);
+        const float2 A = make_float2(z.x + zm.x, z.y - zm.y);
+        const float2 Bv = make_float2(z.y + zm.y, zm.x - z.x);
+        if (x == 0) {
+          sa[i] = A;
+          sb[i] = Bv;
+        } else if (x == 1) {
+          sa[i] = cmulc(sa[i], A);
+          sb[i] = cmulc(sb[i], Bv);
+        } else {
+          float2 ga = make_float2(0.f, 0.f), gb = ga;
+          if (f < p.keep) {
+            ga = gate_value(p.gate, p.gate_kind, p.nbins, ha, f, f, N, p.scale);
+            gb = gate_value(p.gate, p.gate_kind, p.nbins, hb, f, f, N, p.scale);
+          }
+          sa[i] = cmul(cmul(sa[i], A), ga);
+          sb[i] = cmul(cmul(sb[i], Bv), gb);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every mirror read is done
+  if (t < C::TC) {
+    // W[f] = Oa + i Ob, W[L-f] = conj(Oa) + i conj(Ob)
+#pragma unroll
+    for (int i = 0; i < C::NH; ++i) {
+      if (i == RC / 2 && t != 0) continue;
+      const float2 oa = sa[i], ob = sb[i];
+      col[t + C::TC * i] = make_float2(oa.x - ob.y, oa.y + ob.x);
+      *mirror_at(mcol, col, t, i) = make_float2(oa.x + ob.y, ob.x - oa.y);
+    }
+  }
+  __syncthreads();
+  if (t < C::TA) {
+#pragma unroll
+    for (int j = 0; j < RA; ++j) v[j] = col[t + C::TA * j];
+  }
+  __syncthreads();  // read before the A stage overwrites the region
+  // the residual rows this thread stores, loaded while the inverse runs
+  float2 xr[RC];
+  const bool addx = p.x != nullptr;
+  if (addx) {
+    const char* xb = static_cast<const char*>(p.x) + gbase * pair_bytes<IN>();
+#pragma unroll
+    for (int i = 0; i < RC; ++i) xr[i] = load_pair_c<IN>(xb + (size_t)i * C::TC * rowb, loff_c);
+  }
+  col_fft<C, +1>(v, col, t, cconj(wa), cconj(wb));
+  if (t < C::TC && live) {
+    char* ob = reinterpret_cast<char*>(p.out + gbase);
+    const uint32_t orow = (uint32_t)p.CP2 * sizeof(float2);
+    const uint32_t ooff = ((uint32_t)t * p.CP2 + cp) * sizeof(float2);
+#pragma unroll
+    for (int i = 0; i < RC; ++i)
+      *reinterpret_cast<float2*>(ob + (size_t)i * C::TC * orow + ooff) = addx ? cadd(v[i], xr[i]) : v[i];
+  }
+}
+
 // ------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -1540,14 +1806,15 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
 
 // ------------------------------------------------ standalone LayerNorm
 //
-// One wave per token: lanes stride over the token's channel pairs (up to 32
-// pairs per lane, H*D <= 4096), z = x + y kept in registers, two-pass
-// statistics with wave butterflies, affine, store (PRE: z = y, and x is added
-// after the affine step).
+// One wave per token: lanes stride over the token's channel pairs (ITS
+// pairs per lane, CP2 <= 64 ITS; H*D <= 4096), z = x + y kept in registers,
+// two-pass statistics with wave butterflies, affine, store (PRE: z = y, and
+// x is added after the affine step).  ITS is the smallest power of two that
+// covers the token, so the registers (and the occupancy) follow H*D.
 
 struct NormParams {
   const float2* y;
-  const void* x;
+  const void* x;  // residual; null when y already holds x + y (post-norm only)
   const float* gamma;
   const float* beta;
   void* out;
@@ -1560,9 +1827,9 @@ struct NormParams {
   int rms;             // 1: RMSNorm (no mean subtracted), 0: LayerNorm
 };
 
-template <int DT, bool PRE = false>
+template <int DT, bool PRE, int ITS>
 __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
-  constexpr int MAXIT = 32;
+  constexpr int MAXIT = ITS;
   const int lane = threadIdx.x & 63;
   const int64_t tok = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (tok >= p.ntok) return;
@@ -1580,7 +1847,7 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
         const float2 g = gated ? make_float2(p.mix[2 * c], p.mix[2 * c + 1]) : make_float2(1.f, 1.f);
         z[it] = join_branches(z[it], load_nt(p.yloc + base + c), gated, g);
       }
-      if constexpr (!PRE) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
+      if (!PRE && p.x != nullptr) z[it] = cadd(z[it], load_pair<DT>(p.x, base + c));
       s += z[it].x + z[it].y;
     }
   }
@@ -1603,6 +1870,101 @@ __global__ __launch_bounds__(256) void k_layernorm(NormParams p) {
                              (z[it].y - mean) * rstd * p.gamma[2 * c + 1] + p.beta[2 * c + 1]);
       if constexpr (PRE) o = cadd(o, load_pair<DT>(p.x, base + c));  // x + LN(y)
       store_pair<DT>(p.out, base + c, o);
+    }
+  }
+}
+
+// The same with two channel pairs per lane (CP2 even): 16-byte loads of y
+// and of gamma / beta, lanes over pair couples c = lane + 64 it (pairs 2c,
+// 2c + 1), CP2 <= 128 ITS.
+template <int DT>
+__device__ __forceinline__ float4 load_pair2(const void* base, int64_t off2) {
+  if constexpr (DT == IN_BF16) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base) + off2);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base) + off2);
+    return make_float4(v.x, v.y, v.z, v.w);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_pair2(void* base, int64_t off2, float4 v) {
+  if constexpr (DT == IN_BF16) {
+    const uint2 u = make_uint2(f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16),
+                               f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16));
+    __builtin_nontemporal_store(u.x, &(reinterpret_cast<uint2*>(base) + off2)->x);
+    __builtin_nontemporal_store(u.y, &(reinterpret_cast<uint2*>(base) + off2)->y);
+  } else {
+    float4* p = reinterpret_cast<float4*>(base) + off2;
+    __builtin_nontemporal_store(v.x, &p->x);
+    __builtin_nontemporal_store(v.y, &p->y);
+    __builtin_nontemporal_store(v.z, &p->z);
+    __builtin_nontemporal_store(v.w, &p->w);
+  }
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+template <int DT, bool PRE, int ITS>
+__global__ __launch_bounds__(256) void k_layernorm2(NormParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tok >= p.ntok) return;
+  const int64_t C2 = p.CP2 / 2;  // pair couples per token
+  const int64_t base = tok * C2;
+  const float4* y4 = reinterpret_cast<const float4*>(p.y);
+  float4 z[ITS];
+  float s = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < C2) {
+      z[it] = load_pair2<IN_F32>(y4, base + c);
+      if (p.yblk != nullptr) {
+        const float4 yb = reinterpret_cast<const float4*>(p.yblk)[(tok / p.Lb) * C2 + c];
+        z[it] = add4(z[it], yb);
+      }
+      if (p.yloc != nullptr) {
+        const float4 yl = load_pair2<IN_F32>(p.yloc, base + c);
+        if (p.mix != nullptr) {
+          const float4 g = reinterpret_cast<const float4*>(p.mix)[c];
+          z[it] = make_float4(g.x * z[it].x + (1.0f - g.x) * yl.x, g.y * z[it].y + (1.0f - g.y) * yl.y,
+                              g.z * z[it].z + (1.0f - g.z) * yl.z, g.w * z[it].w + (1.0f - g.w) * yl.w);
+        } else {
+          z[it] = add4(z[it], yl);
+        }
+      }
+      if (!PRE && p.x != nullptr) z[it] = add4(z[it], load_pair2<DT>(p.x, base + c));
+      s += (z[it].x + z[it].y) + (z[it].z + z[it].w);
+    }
+  }
+  const float mean = p.rms ? 0.f : wave_sum(s) * p.inv_c;  // an RMSNorm subtracts none
+  float q = 0.f;
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < C2) {
+      const float a = z[it].x - mean, b = z[it].y - mean, d = z[it].z - mean, e = z[it].w - mean;
+      q += (a * a + b * b) + (d * d + e * e);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) * p.inv_c + p.eps);
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int64_t c = lane + 64 * it;
+    if (c < C2) {
+      const float4 g = reinterpret_cast<const float4*>(p.gamma)[c];
+      const float4 bb = reinterpret_cast<const float4*>(p.beta)[c];
+      float4 o = make_float4((z[it].x - mean) * rstd * g.x + bb.x, (z[it].y - mean) * rstd * g.y + bb.y,
+                             (z[it].z - mean) * rstd * g.z + bb.z, (z[it].w - mean) * rstd * g.w + bb.w);
+      if constexpr (PRE) o = add4(o, load_pair2<DT>(p.x, base + c));  // x + LN(y)
+      store_pair2<DT>(p.out, base + c, o);
     }
   }
 }

@@ -33,6 +33,7 @@ constexpr int kLdsBudget = 64 * 1024;  // bytes of LDS per B workgroup
 
 struct Plan {
   int64_t L = 0, L1 = 1, L2 = 1, L3 = 1;
+  int col = 0;  // single-level plan run by the column kernel k_col: its ColKind, else 0
   int sq = 0;  // R when L3 = R * R uses the two-register-DFT B kernel (R = 16, 32), else 0
   int P = 0;   // points per thread in B
   int Tc = 0;  // threads per column in B
@@ -82,12 +83,30 @@ bool plan_radices(int64_t N, int P, Plan& pl) {
   return true;
 }
 
+// Lengths the single-pass column kernel runs, L = RA * RB * RC (ColCfg).  At
+// 6144 and 8192 its first stage (24 or 32 points per thread) needs more
+// registers than four waves per SIMD leave, and the four-step plan is faster.
+enum ColKind { COL_NONE = 0, COL_3072 = 1, COL_4096 = 2 };
+
+int col_kind(int64_t L) {
+  switch (L) {
+    case 3072: return COL_3072;
+    case 4096: return COL_4096;
+    default: return COL_NONE;
+  }
+}
+
 int make_plan(int64_t L, Plan& pl) {
   pl = Plan();
   if (L < 2 || L % 2 != 0) return SPECTRE_EINVAL;
   int a = 0, b = 0;
   if (!factor23(L, a, b) || b > 1 || L > kMaxL) return SPECTRE_EUNSUPPORTED;
   pl.L = L;
+  if (int ck = col_kind(L)) {  // one pass: the whole column in one workgroup's LDS
+    pl.L3 = L;
+    pl.col = ck;
+    return SPECTRE_OK;
+  }
   if (L <= kMaxSingle) {
     pl.L3 = L;
   } else {
@@ -723,21 +742,34 @@ int launch_final(int64_t R, const FinalParams& p, bool fuse, bool pre, int64_t B
   }
 }
 
-int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
-  dim3 grid((unsigned)((p.ntok + 3) / 4));
-  if (dtype == SPECTRE_F32) {
-    if (pre)
-      hipLaunchKernelGGL((k_layernorm<IN_F32, true>), grid, dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((k_layernorm<IN_F32, false>), grid, dim3(256), 0, st, p);
-  } else {
-    if (pre)
-      hipLaunchKernelGGL((k_layernorm<IN_BF16, true>), grid, dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((k_layernorm<IN_BF16, false>), grid, dim3(256), 0, st, p);
+template <int DT, bool PRE>
+int launch_norm_its(const NormParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((p.ntok + 3) / 4)), block(256);
+  if (p.CP2 % 2 == 0) {  // two pairs per lane
+    if (p.CP2 <= 128) hipLaunchKernelGGL((k_layernorm2<DT, PRE, 1>), grid, block, 0, st, p);
+    else if (p.CP2 <= 256) hipLaunchKernelGGL((k_layernorm2<DT, PRE, 2>), grid, block, 0, st, p);
+    else if (p.CP2 <= 512) hipLaunchKernelGGL((k_layernorm2<DT, PRE, 4>), grid, block, 0, st, p);
+    else if (p.CP2 <= 1024) hipLaunchKernelGGL((k_layernorm2<DT, PRE, 8>), grid, block, 0, st, p);
+    else if (p.CP2 <= 2048) hipLaunchKernelGGL((k_layernorm2<DT, PRE, 16>), grid, block, 0, st, p);
+    else return SPECTRE_EUNSUPPORTED;
+    SPECTRE_LAUNCH_CHECK("LN_norm");
+    return SPECTRE_OK;
   }
+  if (p.CP2 <= 64) hipLaunchKernelGGL((k_layernorm<DT, PRE, 1>), grid, block, 0, st, p);
+  else if (p.CP2 <= 128) hipLaunchKernelGGL((k_layernorm<DT, PRE, 2>), grid, block, 0, st, p);
+  else if (p.CP2 <= 256) hipLaunchKernelGGL((k_layernorm<DT, PRE, 4>), grid, block, 0, st, p);
+  else if (p.CP2 <= 512) hipLaunchKernelGGL((k_layernorm<DT, PRE, 8>), grid, block, 0, st, p);
+  else if (p.CP2 <= 1024) hipLaunchKernelGGL((k_layernorm<DT, PRE, 16>), grid, block, 0, st, p);
+  else if (p.CP2 <= 2048) hipLaunchKernelGGL((k_layernorm<DT, PRE, 32>), grid, block, 0, st, p);
+  else return SPECTRE_EUNSUPPORTED;
   SPECTRE_LAUNCH_CHECK("LN_norm");
   return SPECTRE_OK;
+}
+
+int launch_norm(const NormParams& p, int dtype, bool pre, hipStream_t st) {
+  if (dtype == SPECTRE_F32)
+    return pre ? launch_norm_its<IN_F32, true>(p, st) : launch_norm_its<IN_F32, false>(p, st);
+  return pre ? launch_norm_its<IN_BF16, true>(p, st) : launch_norm_its<IN_BF16, false>(p, st);
 }
 
 // The windowed-attention branch over q, k, v of shape s into y (binary32
@@ -789,14 +821,43 @@ size_t local_bytes(const Shape& s, const Local* local) {
   return local ? 256 + (size_t)s.N * 4 : 0;
 }
 
+// The single-pass column kernel of a ColKind: grid (pair blocks, batch).
+template <int RA, int RB, int RC, int CPT, int IN>
+int launch_col_k(const ColParams& c, int64_t B, hipStream_t st) {
+  using C = ColCfg<RA, RB, RC, CPT>;
+  static bool attr_set = false;  // guarded by g_mu
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_col<RA, RB, RC, CPT, IN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES) != hipSuccess)
+      return SPECTRE_EHIP;
+    attr_set = true;
+  }
+  const int64_t items = (c.CP2 + CPT - 1) / CPT * B;
+  if (items > INT32_MAX) return SPECTRE_EUNSUPPORTED;
+  const dim3 grid((unsigned)items);
+  hipLaunchKernelGGL((k_col<RA, RB, RC, CPT, IN>), grid, dim3(C::THREADS), C::LDS_BYTES, st, c);
+  SPECTRE_LAUNCH_CHECK("B_col");
+  return SPECTRE_OK;
+}
+
+template <int IN>
+int launch_col(int kind, const ColParams& c, int64_t B, hipStream_t st) {
+  switch (kind) {
+    case COL_3072: return launch_col_k<12, 16, 16, 4, IN>(c, B, st);
+    case COL_4096: return launch_col_k<16, 16, 16, 4, IN>(c, B, st);
+    default: return SPECTRE_EUNSUPPORTED;
+  }
+}
+
 // B, the LDS pass, for shape s / plan pl: the column transforms, the
 // spectral product and the inverse.  in[] are the raw tensors (single level,
 // in_kind their storage) or the spectra (IN_C32); out gets y (single level)
 // or U; gtab is the gate table of a multi-level square kernel, else null;
-// dc (chunked mix) receives the block means.
+// dc (chunked mix) receives the block means; resid (column kernel only) is
+// added to y before it is stored.
 int launch_b(const Shape& s, const Plan& pl, const LenTables* tab, const void* const in[3],
              int in_kind, float2* out, const float* gate, const float* gtab, int tiled,
-             float2* dc, hipStream_t st) {
+             float2* dc, hipStream_t st, const void* resid = nullptr) {
   const bool single = is_single(pl);
   const int64_t CP2 = s.CP2;
   MidParams m{};
@@ -831,6 +892,25 @@ int launch_b(const Shape& s, const Plan& pl, const LenTables* tab, const void* c
   m.dc = dc;
   m.dc_stride = s.B * CP2;
   m.dc_scale = (float)(1.0 / (double)s.L);
+  if (pl.col) {
+    ColParams c{};
+    for (int t = 0; t < 3; ++t) c.in[t] = in[t];
+    c.x = resid;
+    c.out = out;
+    c.gate = gate;
+    c.tw = tab->twN;
+    c.gate_kind = s.gate_kind;
+    c.CP2 = (int)CP2;
+    c.D = (int)s.D;
+    c.keep = (int)s.keep;
+    c.nbins = (int)(s.L / 2 + 1);
+    c.scale = m.scale;
+    c.dc = dc;
+    c.dc_stride = m.dc_stride;
+    c.dc_scale = m.dc_scale;
+    return in_kind == IN_BF16 ? launch_col<IN_BF16>(pl.col, c, s.B, st)
+                              : launch_col<IN_F32>(pl.col, c, s.B, st);
+  }
   dim3 grid((unsigned)tab->nwg, (unsigned)(CP2 / cpt), (unsigned)s.B);
   const int threads = pl.Tc * nslot * cpt;
   if (pl.sq) {
@@ -979,7 +1059,10 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
     }
   }
 
-  // ---- B: LDS transform, spectral product, inverse
+  // ---- B: LDS transform, spectral product, inverse.  The column kernel of a
+  // post-norm call without the local branch stores x + y, so that the norm
+  // pass reads one tensor instead of two
+  const bool fold_x = pl.col && want_out && (s.norm_order & 1) == 0 && !local;
   {
     const void* ins[3] = {q, k, v};
     if (!single)
@@ -987,7 +1070,7 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
     float2* bout = single ? (want_out ? reinterpret_cast<float2*>(ws) : reinterpret_cast<float2*>(y))
                           : U;  // row layout: q's spectrum in place, unless tiled
     rc = launch_b(s, pl, tab, ins, single ? in_kind : IN_C32, bout, gate, g.gtab,
-                  tiled || tiled3 ? 1 : 0, chunk ? dc : nullptr, st);
+                  tiled || tiled3 ? 1 : 0, chunk ? dc : nullptr, st, fold_x ? x : nullptr);
     if (rc) return rc;
   }
 
@@ -1015,7 +1098,7 @@ int launch_all(int dev, const void* q, const void* k, const void* v, const void*
     if (!want_out) return SPECTRE_OK;
     NormParams n{};
     n.y = reinterpret_cast<const float2*>(ws);
-    n.x = x;
+    n.x = fold_x ? nullptr : x;
     n.gamma = gamma;
     n.beta = beta;
     n.out = out;

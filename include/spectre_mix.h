@@ -189,7 +189,8 @@ int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* g
  *     block;
  *   - then out = LayerNorm(x + y) as for spectre_mix_fwd.
  * Shapes: fft_len a supported length (see above), L a multiple of it, nb
- * even with nb = 2^a * 3^b <= 2048 (else SPECTRE_EINVAL / EUNSUPPORTED).
+ * even with nb = 2^a * 3^b <= 2048 or nb in {3072, 4096} (else
+ * SPECTRE_EINVAL / EUNSUPPORTED).
  * Everything else (layouts, ownership, stream, errors) as spectre_mix_fwd.
  * The block means are the transform's bin 0 of each block, taken from the
  * forward pass; the block-axis mix runs between the transform and the norm.

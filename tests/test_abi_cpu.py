@@ -177,8 +177,10 @@ def test_y_rejects_before_device():
 
 
 def test_plan_factorisation():
-    cases = {256: (1, 1, 256), 2048: (1, 1, 2048), 4096: (4, 1, 1024), 3072: (6, 1, 512), 6144: (6, 1, 1024),
-             8192: (8, 1, 1024), 65536: (64, 1, 1024), 98304: (32, 3, 1024),
+    # 3072 and 4096: one pass, the whole column in one workgroup
+    cases = {256: (1, 1, 256), 2048: (1, 1, 2048), 4096: (1, 1, 4096), 3072: (1, 1, 3072),
+             6144: (6, 1, 1024), 8192: (8, 1, 1024), 12288: (12, 1, 1024), 16384: (16, 1, 1024),
+             65536: (64, 1, 1024), 98304: (32, 3, 1024),
              786432: (64, 12, 1024), 3 * 2 ** 20: (64, 48, 1024), 2: (1, 1, 2), 6: (1, 1, 6)}
     for L, want in cases.items():
         st, got = sm.spectre_mix_plan(L)
@@ -206,8 +208,9 @@ def test_workspace_bytes():
     multi-level plans, a fourth for B's output when the first pass writes the
     tiled layout (two-level, 48- or 64-point first pass), six when a
     three-level plan's second pass writes it out of place, y (4 bytes per
-    element) for single-level ones, plus the H * L binary32 gate table when
-    the column length is 256 or 1024."""
+    element) for single-level ones (y is binary32 whatever the storage),
+    plus the H * L binary32 gate table when a multi-level plan's column
+    length is 256 or 1024."""
     N = 1 * 65536 * 512
     gate_tab = 4 * 8 * 65536
     assert sm.spectre_mix_workspace_bytes(1, 8, 65536, 64, 0) == 16 * N + gate_tab
@@ -218,8 +221,9 @@ def test_workspace_bytes():
     # L = 786432 = 64 x 12 x 1024: second pass out of place, six spectra
     N5 = 786432 * 512
     assert sm.spectre_mix_workspace_bytes(1, 8, 786432, 64, 0) == 24 * N5 + 4 * 8 * 786432
-    # L = 4096 = 4 x 1024: two-level with the tiled layout
-    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 16 * 4 * 4096 * 512 + 4 * 8 * 4096
+    # L = 4096 and 3072: one pass (column kernel), y only, no gate table
+    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
+    assert sm.spectre_mix_workspace_bytes(2, 8, 3072, 64, 1) == 4 * 2 * 3072 * 512
     # L = 2048: single level, generic LDS kernel, y only, no gate table
     assert sm.spectre_mix_workspace_bytes(4, 8, 2048, 64, 0) == 4 * 4 * 2048 * 512
     # L = 256: single level, square kernel reading the gate itself (no table)
@@ -257,4 +261,4 @@ def test_noalloc_rejects_before_device():
     assert call(out=GOOD + 0x3000000) == sm.SPECTRE_EINVAL
     assert call(L=98304, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED   # three-level plan
     assert call(L=65536, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED   # 537 MB of workspace
-    assert call(B=2, L=4096, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED  # 16 N bytes = 64 MiB + tables
+    assert call(B=8, L=4096, keep_bins=1) == sm.SPECTRE_EUNSUPPORTED  # y: 4 N bytes = 64 MiB, + tables

@@ -107,8 +107,8 @@ EDGE = [
     (1, 256, 1, 32, 0, 0),          # keep 0: out = LayerNorm(x)
     (1, 256, 2, 16, 0, 1),          # only the DC bin
     (1, 1536, 4, 8, 1, 700),
-    (2, 4096, 2, 8, 0, 2048),       # Nyquist dropped (4 x 1024, row layout: CP2 = 8)
-    (1, 3072, 2, 32, 0, None),      # two-level 6 x 512: radix 3 in the strided pass, generic LDS pass
+    (2, 4096, 2, 8, 0, 2048),       # Nyquist dropped (one pass: 16 x 16 x 16 column kernel)
+    (1, 3072, 2, 32, 0, None),      # one pass, 12 x 16 x 16
     (1, 2048, 2, 64, 0, 700),       # the longest single-level column
     (1, 6144, 2, 64, 0, None),      # two-level, radix 3 in the strided pass (l1 = 6)
     (2, 8192, 4, 32, 1, 1000),      # two-level, fused norm, bf16
@@ -117,7 +117,7 @@ EDGE = [
     (1, 98304, 2, 64, 0, None),     # three-level, l2 = 3
     (1, 196608, 1, 128, 1, 50000),  # three-level, l2 = 6
     (1, 16384, 4, 256, 0, None),    # H*D = 1024: separate norm pass
-    (1, 4096, 2, 5, 0, None),       # channel pairs straddle heads (odd D)
+    (1, 4096, 2, 5, 0, None),       # channel pairs straddle heads (odd D), ragged pair block
     (2, 65536, 4, 64, 0, None),     # LDS-copy B kernel, 4 work items per workgroup across batches
     (1, 65536, 4, 64, 1, 30000),    # LDS-copy B kernel, 2 work items per workgroup, bf16, truncated
     (1, 8192, 32, 6, 0, None),      # tiled input, 4-pair blocks spanning heads: gate from the table
@@ -128,6 +128,31 @@ EDGE = [
 def test_edge_shapes(B, L, H, D, dt, keep):
     kb = L // 2 + 1 if keep is None else keep
     w = workloads.custom(200 + L % 97, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=kb, affine=True)
+    check_full(w)
+
+
+# The single-pass column kernel (L = 3072, 4096): ragged last pair blocks
+# (CP2 = 9, 1, 3, 5), heads that split pairs, bfloat16 storage, truncation
+# down to keep 0 and 1, several batch elements.
+COLUMN = [
+    (3, 4096, 3, 6, 0, None),       # CP2 = 9: last block holds one live pair
+    (1, 4096, 8, 64, 1, 1000),      # bf16, truncated
+    (2, 3072, 4, 10, 0, 777),
+    (1, 3072, 1, 2, 0, None),       # a single pair
+    (2, 3072, 2, 6, 1, None),       # CP2 = 6, bf16
+    (1, 4096, 1, 2, 0, 1),          # a single pair, the DC bin only
+    (1, 4096, 3, 2, 0, 0),          # CP2 = 3, keep 0: out = LayerNorm(x)
+    (2, 3072, 8, 64, 0, None),
+    (5, 4096, 2, 64, 0, 2049),
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep", COLUMN)
+def test_column_kernel_shapes(B, L, H, D, dt, keep):
+    import efficient_attention_fft_amd as sm
+    assert sm.spectre_mix_plan(L) == (sm.SPECTRE_OK, (1, 1, L))
+    kb = L // 2 + 1 if keep is None else keep
+    w = workloads.custom(500 + L % 83, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=kb, affine=True)
     check_full(w)
 
 
