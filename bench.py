@@ -358,7 +358,7 @@ def run_bench(args):
         "data": "synthetic",
         "config": dict(w.describe(), parallelism="single GPU",
                        **({"gate_kind": ["real", "logit", "complex"][gk],
-                           "norm": ["post", "pre"][no]} if (gk or no) else {}),
+                           "norm": ["post", "pre", "post_rms", "pre_rms"][no]} if (gk or no) else {}),
                        **({"fft_len": F} if F else {}),
                        **({"local_window": [wl, wr]} if win else {})),
         "roofline": roofline,
@@ -405,7 +405,9 @@ def _short(name: str) -> str:
         return "B_mid_lds"
     if kern == "k_final":
         return "C1_inv_norm" if args[2] == "true" else "C1_inv"
-    if kern == "k_layernorm":
+    if kern == "k_col":
+        return "B_col"
+    if kern in ("k_layernorm", "k_layernorm2"):
         return "LN_norm"
     if kern == "k_local_attn":
         return "L_local"

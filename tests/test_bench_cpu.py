@@ -56,4 +56,6 @@ def test_short_names_of_library_kernels():
     assert bench._short("void spectre::k_mid_dma<false, 17>(spectre::MidParams)") == "B_mid_lds"
     assert bench._short("void spectre::k_local_attn<0, 64>(spectre::LocalParams)") == "L_local"
     assert bench._short("void spectre::k_layernorm<0, false>(spectre::NormParams)") == "LN_norm"
+    assert bench._short("void spectre::k_layernorm2<0, false, 2>(spectre::NormParams)") == "LN_norm"
+    assert bench._short("void spectre::k_col<16, 16, 16, 4, 0>(spectre::ColParams)") == "B_col"
     assert bench._short("__amd_rocclr_copyBuffer") == "copy (calibration)"
