@@ -96,13 +96,22 @@ int col_kind(int64_t L) {
   }
 }
 
-int make_plan(int64_t L, Plan& pl) {
+// The column kernel runs one workgroup per 4 channel pairs of a batch
+// element, one per CU, and its transform, LDS exchanges and memory phases do
+// not overlap inside a CU; it beats the four-step plan (whose last pass also
+// fuses the norm) only while its whole grid is one round on the chip's 256
+// CUs.  Larger calls at these lengths take the four-step plan.
+constexpr int64_t kColMaxItems = 256;
+
+bool col_fits(int64_t B, int64_t CP2) { return B * ((CP2 + 3) / 4) <= kColMaxItems; }
+
+int make_plan(int64_t L, Plan& pl, bool allow_col = true) {
   pl = Plan();
   if (L < 2 || L % 2 != 0) return SPECTRE_EINVAL;
   int a = 0, b = 0;
   if (!factor23(L, a, b) || b > 1 || L > kMaxL) return SPECTRE_EUNSUPPORTED;
   pl.L = L;
-  if (int ck = col_kind(L)) {  // one pass: the whole column in one workgroup's LDS
+  if (int ck = allow_col ? col_kind(L) : COL_NONE) {  // one pass: the whole column in LDS
     pl.L3 = L;
     pl.col = ck;
     return SPECTRE_OK;
@@ -177,7 +186,7 @@ struct LenTables {
 struct DeviceState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  std::map<int64_t, LenTables> tables;
+  std::map<int64_t, LenTables> tables;  // keyed by table_key(plan)
 };
 
 std::mutex g_mu;
@@ -308,9 +317,13 @@ void build_wgcols(const Plan& pl, std::vector<int2>& out, int& selfwg) {
   out.push_back(s);
 }
 
+// Tables are cached per (device, plan): one length can have two plans (the
+// column kernel's single pass and the four-step), whose tables differ.
+int64_t table_key(const Plan& pl) { return pl.L * 2 + (pl.col ? 1 : 0); }
+
 int get_tables(int dev, const Plan& pl, LenTables** res) {
   DeviceState& ds = g_dev[dev];
-  auto it = ds.tables.find(pl.L);
+  auto it = ds.tables.find(table_key(pl));
   if (it != ds.tables.end()) {
     *res = &it->second;
     return SPECTRE_OK;
@@ -338,7 +351,7 @@ int get_tables(int dev, const Plan& pl, LenTables** res) {
     (void)hipFree(t.wgcols);
     return SPECTRE_EHIP;
   }
-  auto ins = ds.tables.emplace(pl.L, t);
+  auto ins = ds.tables.emplace(table_key(pl), t);
   *res = &ins.first->second;
   return SPECTRE_OK;
 }
@@ -417,7 +430,7 @@ int check_shape(int64_t B, int64_t H, int64_t L, int64_t D, int64_t keep, int dt
   if (C % 2 != 0) return SPECTRE_EUNSUPPORTED;
   if (L * C >= (int64_t(1) << 29)) return SPECTRE_EUNSUPPORTED;  // 32-bit byte offsets per batch
   if (B > (int64_t(1) << 40) / (L * C)) return SPECTRE_EUNSUPPORTED;
-  int st = make_plan(L, pl);
+  int st = make_plan(L, pl, col_fits(B, C / 2));
   if (st != SPECTRE_OK) return st;
   s.B = B;
   s.H = H;
@@ -937,7 +950,7 @@ int launch_block_mix(int dev, const Shape& s, const Chunk& ch, const float2* dc,
   sb.esz = 4;
   sb.gate_kind = SPECTRE_GATE_REAL;
   Plan pb;
-  int rc = make_plan(ch.nb, pb);
+  int rc = make_plan(ch.nb, pb, col_fits(ch.B, s.CP2));
   if (rc) return rc;
   if (!is_single(pb)) return SPECTRE_EUNSUPPORTED;
   LenTables* tb = nullptr;
@@ -1182,7 +1195,7 @@ int check_chunked(int64_t B, int64_t H, int64_t L, int64_t D, int64_t fft_len, i
   int rc = check_shape(B * nb, H, fft_len, D, keep_bins, dtype, s, pl);
   if (rc) return rc;
   Plan pb;
-  rc = make_plan(nb, pb);
+  rc = make_plan(nb, pb, col_fits(B, s.CP2));  // as launch_block_mix plans it
   if (rc) return rc;
   if (!is_single(pb)) return SPECTRE_EUNSUPPORTED;
   ch.nb = nb;

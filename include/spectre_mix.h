@@ -189,8 +189,8 @@ int spectre_mix_y_ex(const void* q, const void* k, const void* v, const float* g
  *     block;
  *   - then out = LayerNorm(x + y) as for spectre_mix_fwd.
  * Shapes: fft_len a supported length (see above), L a multiple of it, nb
- * even with nb = 2^a * 3^b <= 2048 or nb in {3072, 4096} (else
- * SPECTRE_EINVAL / EUNSUPPORTED).
+ * even with nb = 2^a * 3^b <= 2048, or nb in {3072, 4096} when
+ * B * ceil(H*D / 8) <= 256 (else SPECTRE_EINVAL / EUNSUPPORTED).
  * Everything else (layouts, ownership, stream, errors) as spectre_mix_fwd.
  * The block means are the transform's bin 0 of each block, taken from the
  * forward pass; the block-axis mix runs between the transform and the norm.
@@ -286,7 +286,10 @@ size_t spectre_mix_workspace_bytes_ex(int64_t B, int64_t H, int64_t L, int64_t D
 /*
  * Transform plan for length L, for inspection: the sequence length factors
  * as L = l1 * l2 * l3 (l1: first strided pass, l2: second strided pass, 1 if
- * absent; l3: the LDS-resident pass).  Returns SPECTRE_OK or
+ * absent; l3: the LDS-resident pass).  L = 3072 and 4096 report the single
+ * pass (1, 1, L), which a call uses while B * ceil(H*D / 8) <= 256 (one
+ * workgroup per 4 channel pairs, one round on the chip); larger calls at
+ * those lengths use (L / 1024, 1, 1024).  Returns SPECTRE_OK or
  * SPECTRE_EUNSUPPORTED / SPECTRE_EINVAL.  No device call.
  */
 int spectre_mix_plan(int64_t L, int64_t* l1, int64_t* l2, int64_t* l3);

@@ -221,9 +221,11 @@ def test_workspace_bytes():
     # L = 786432 = 64 x 12 x 1024: second pass out of place, six spectra
     N5 = 786432 * 512
     assert sm.spectre_mix_workspace_bytes(1, 8, 786432, 64, 0) == 24 * N5 + 4 * 8 * 786432
-    # L = 4096 and 3072: one pass (column kernel), y only, no gate table
+    # L = 4096 and 3072: one pass (column kernel), y only, no gate table, while
+    # B * CP2 / 4 <= 256; beyond that the four-step plan (4 x 1024, tiled)
     assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
     assert sm.spectre_mix_workspace_bytes(2, 8, 3072, 64, 1) == 4 * 2 * 3072 * 512
+    assert sm.spectre_mix_workspace_bytes(5, 8, 4096, 64, 0) == 16 * 5 * 4096 * 512 + 4 * 8 * 4096
     # L = 2048: single level, generic LDS kernel, y only, no gate table
     assert sm.spectre_mix_workspace_bytes(4, 8, 2048, 64, 0) == 4 * 4 * 2048 * 512
     # L = 256: single level, square kernel reading the gate itself (no table)

@@ -146,6 +146,20 @@ COLUMN = [
     (5, 4096, 2, 64, 0, 2049),
 ]
 
+# Past one round of the column kernel (B * CP2 / 4 > 256): the same lengths
+# take the four-step plan.
+PAST_ONE_ROUND = [
+    (5, 4096, 8, 64, 0, 1500),
+    (2, 3072, 16, 64, 1, None),
+]
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep", PAST_ONE_ROUND)
+def test_column_lengths_past_one_round(B, L, H, D, dt, keep):
+    kb = L // 2 + 1 if keep is None else keep
+    w = workloads.custom(510 + L % 83, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=kb, affine=True)
+    check_full(w)
+
 
 @pytest.mark.parametrize("B,L,H,D,dt,keep", COLUMN)
 def test_column_kernel_shapes(B, L, H, D, dt, keep):
@@ -154,6 +168,14 @@ def test_column_kernel_shapes(B, L, H, D, dt, keep):
     kb = L // 2 + 1 if keep is None else keep
     w = workloads.custom(500 + L % 83, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=kb, affine=True)
     check_full(w)
+
+
+def test_both_plans_of_one_length_in_one_process():
+    """L = 4096 in one round (column kernel), past it (four-step) and in one
+    round again, in one process: each plan must get its own tables."""
+    for i, (B, H) in enumerate([(1, 8), (5, 8), (2, 4)]):
+        w = workloads.custom(520 + i, B=B, L=4096, H=H, D=64, keep_bins=1800, affine=True)
+        check_full(w, check_y=False)
 
 
 def _sweep_cases(n=20, seed=4242):
