@@ -24,6 +24,9 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # (B, L, H, D, dtype, fft_len, keep_bins, keep_blocks)
     (1, 65536, 8, 64, 0, 4096, 2049, 9),     # the article's 4096-token blocks; 4 x 1024 plan
+    (1, 16384, 4, 64, 0, 4096, 2049, 3),     # 4096-token blocks in one round of the column kernel
+    (2, 12288, 2, 32, 1, 3072, 1000, 2),     # 3072-token blocks, column kernel, bf16
+    (1, 8192, 2, 8, 0, 2, 2, 700),           # a block axis of 4096 blocks through the column kernel
     (2, 16384, 4, 32, 0, 2048, 700, 5),      # single-level generic LDS kernel, nb = 8
     (1, 49152, 2, 64, 0, 8192, 4097, 2),     # 8 x 1024 blocks, nb = 6, truncated block axis
     (1, 16384, 8, 64, 1, 256, 100, 20),      # single-level square kernel, bf16, nb = 64
