@@ -35,7 +35,7 @@
  *    Execution faults surface at the caller's next synchronisation.
  *  - Argument validation happens before any device call; on any error code
  *    nothing is enqueued and `out` is untouched.
- *  - The library owns a per-device workspace and per-(device, L) twiddle
+ *  - The library owns a per-device workspace and per-(device, plan) twiddle
  *    tables, created lazily on first use (so the first call on a device
  *    allocates device memory), guarded by a mutex, reused by later calls,
  *    and freed by spectre_mix_release().  Two calls that overlap in time on
@@ -134,8 +134,10 @@ int spectre_mix_fwd(const void* q, const void* k, const void* v, const void* x,
  * library holds on every GPU it runs on until the process ends (its address
  * is looked up once per device, on the first call there).  Limits: plans of
  * one or two levels (L <= 65536 here, 2^a 3^b as for spectre_mix_fwd) whose
- * workspace and tables fit the 64 MiB (for example B * L * H * D up to about
- * 3.5 million elements); anything larger returns SPECTRE_EUNSUPPORTED with
+ * workspace and tables fit the 64 MiB (single-pass plans need 4 bytes per
+ * element, B * L * H * D up to about 16 million; two-level plans 12 or 16
+ * bytes per element, about 4 million); anything larger returns
+ * SPECTRE_EUNSUPPORTED with
  * nothing enqueued.  All calls on one GPU share its array: calls that overlap
  * on one GPU (two streams, two threads) race and must be ordered by the
  * caller.  Every call writes all the array regions it reads.
@@ -274,7 +276,12 @@ int spectre_mix_local_attention(const void* q, const void* k, const void* v, flo
 
 /*
  * Device workspace bytes a spectre_mix_fwd call of this shape uses (0 if the
- * shape is invalid or unsupported).  Pure host arithmetic; no device call.
+ * shape is invalid or unsupported): 4 bytes per element (y) for single-pass
+ * plans (L <= 2048, and L = 3072, 4096 while B * ceil(H*D / 8) <= 256), 12 or
+ * 16 per element for two-level plans (three spectra, and a fourth region when
+ * the first pass writes its tiled layout), 24 for three-level plans, plus the
+ * 4 * H * L-byte gate table of a multi-level plan whose LDS pass has 256 or
+ * 1024 points.  Pure host arithmetic; no device call.
  */
 size_t spectre_mix_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int dtype);
 
