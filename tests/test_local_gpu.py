@@ -209,6 +209,7 @@ GATED_CASES = [
     (1, 49152, 8, 64, 1, 12289, 128, 0, 1, 2),   # 48 x 1024, split, bf16, logit gate, RMSNorm
     (1, 2048, 2, 16, 0, 900, 40, 40, 2, 1),      # single level, LayerNorm pass, complex gate, pre
     (1, 16384, 2, 32, 0, 3000, 64, 63, 0, 2),    # unfused inverse + norm pass, RMSNorm
+    (2, 4096, 8, 64, 0, 2049, 64, 64, 2, 3),     # single-pass column kernel, pre RMSNorm
 ]
 
 
