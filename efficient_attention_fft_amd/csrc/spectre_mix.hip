@@ -25,7 +25,8 @@ namespace {
 // ------------------------------------------------------------------ plan
 
 constexpr int64_t kMaxL = 3 * (int64_t(1) << 20);
-constexpr int64_t kMaxSingle = 2048;  // longest column kept whole in one workgroup's LDS
+constexpr int64_t kMaxSingle = 2048;  // longest length for the single-level k_mid / k_mid_sq
+                                      // (3072 and 4096 have the column kernel k_col)
 constexpr int kMaxC = 4096;
 constexpr int kMaxMidThreads = 512;   // launch bound of the B kernel
 constexpr int kMaxFusedPairs = 256; // launch bound of the fused C1 kernel

@@ -138,7 +138,7 @@ MIX_CASES = [
     # (B, L, H, D, dtype, keep_bins, win_left, win_right)
     (1, 256, 2, 16, 0, 129, 64, 64),       # single-level square kernel
     (1, 1536, 2, 32, 1, 700, 64, 64),      # single-level generic LDS kernel (radix 3), bf16
-    (2, 4096, 8, 64, 0, 2049, 64, 64),     # single-level generic LDS kernel, window 128
+    (2, 4096, 8, 64, 0, 2049, 64, 64),     # single-pass column kernel, window 128
     (1, 16384, 2, 32, 0, 3000, 128, 128),  # two-level plan, window 256
     (1, 16384, 8, 64, 1, 4097, 64, 63),    # bfloat16, LDS-copy B kernel
     (1, 98304, 1, 32, 0, 49153, 100, 0),   # three-level plan (32 x 3 x 1024), one-sided
@@ -171,7 +171,7 @@ VARIANT_CASES = [
     # (B, L, H, D, dtype, keep_bins, win_left, win_right, gate_kind, norm_order)
     (1, 16384, 8, 64, 0, 4097, 64, 64, 2, 1),    # 16 x 1024, fused inverse, complex gate, pre-norm
     (1, 65536, 4, 64, 0, 30000, 64, 64, 1, 1),   # 64 x 1024, split fused inverse, logit gate, pre
-    (2, 4096, 4, 32, 1, 1000, 128, 0, 2, 0),     # 4 x 1024, bf16, complex gate, post
+    (2, 4096, 4, 32, 1, 1000, 128, 0, 2, 0),     # column kernel, bf16, complex gate, post
     (1, 2048, 2, 16, 0, 900, 40, 40, 1, 1),      # single level, LayerNorm pass, logit gate, pre
     (1, 16384, 2, 32, 0, 3000, 64, 63, 0, 1),    # unfused inverse + LayerNorm pass, pre
 ]

@@ -6,7 +6,8 @@ spectre_mix_fwd_ex / spectre_mix_y_ex.
 
 Tolerances as for the plain mix: max-abs on out 1e-4 (binary32 storage) and
 2e-2 (bfloat16 storage); y within 1e-4 * max(1, max|y|).  The shapes cover
-every kernel path: single-level square and generic LDS kernels, two-level
+every kernel path: single-level square and generic LDS kernels, the single-pass
+column kernel, two-level
 generic, tiled with the LDS-copy B kernel, tiled blocks that span heads,
 three-level, the fused norm with and without the split inverse, and the
 separate LayerNorm pass.
@@ -30,8 +31,9 @@ SHAPES = [
     # (B, L, H, D, dtype, keep)  keep None = no truncation
     (1, 256, 2, 16, 0, None),      # single level, square LDS kernel (16 x 16)
     (1, 1536, 4, 8, 1, 700),       # single level, generic LDS kernel, bf16, separate norm pass
-    (1, 3072, 2, 32, 0, None),     # two-level 6 x 512, generic LDS kernel
-    (4, 4096, 8, 64, 0, None),     # two-level tiled, LDS-copy B kernel, fused norm
+    (1, 3072, 2, 32, 0, None),     # single-pass column kernel, 12 x 16 x 16
+    (4, 4096, 8, 64, 0, None),     # single-pass column kernel, x + y into the norm pass
+    (1, 16384, 8, 64, 0, None),    # two-level tiled, LDS-copy B kernel, fused norm
     (1, 8192, 32, 6, 0, None),     # tiled blocks spanning heads: square kernel, gate table
     (1, 98304, 2, 64, 0, None),    # three-level 32 x 3 x 1024
     (2, 8192, 4, 32, 1, 1000),     # fused norm with the one-lane inverse, bf16, truncated

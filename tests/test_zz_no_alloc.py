@@ -12,10 +12,14 @@ from gpu_util import DeviceInputs, empty_like_storage, to_host_f64, tol, torch
 
 pytestmark = pytest.mark.gpu
 
-# (B, L, H, D, keep): a two-level plan (4 x 1024, tiled LDS pass), then a
-# smaller one-level plan; then a ragged two-level one (6 x 512)
-CASES = [((1, 4096, 8, 64, 1500), (1, 2048, 4, 32, 1025)),
-         ((2, 3072, 4, 16, 700), (1, 256, 2, 16, 129))]
+# (B, L, H, D, keep), two calls in a row, the second smaller: a two-level
+# plan (8 x 1024, tiled LDS pass), then the single-pass column kernel; the
+# column kernel at 12 x 16 x 16, then the square single-level kernel; a
+# two-level plan in row layout (6 x 1024, CP2 = 16), then the generic
+# single-level kernel
+CASES = [((1, 8192, 4, 32, 1500), (1, 4096, 4, 32, 1025)),
+         ((2, 3072, 4, 16, 700), (1, 256, 2, 16, 129)),
+         ((1, 6144, 2, 16, 900), (1, 1536, 2, 16, 700))]
 
 
 def _pair(w, keep):
