@@ -226,6 +226,10 @@ def test_workspace_bytes():
     assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
     assert sm.spectre_mix_workspace_bytes(2, 8, 3072, 64, 1) == 4 * 2 * 3072 * 512
     assert sm.spectre_mix_workspace_bytes(5, 8, 4096, 64, 0) == 16 * 5 * 4096 * 512 + 4 * 8 * 4096
+    # the boundary: 4 x 64 = 256 items (one round) against 4 x 65 = 260 (H*D = 520: the
+    # four-step plan, row layout since CP2 = 260 is not a multiple of 32)
+    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 64, 0) == 4 * 4 * 4096 * 512
+    assert sm.spectre_mix_workspace_bytes(4, 8, 4096, 65, 0) == 12 * 4 * 4096 * 520 + 4 * 8 * 4096
     # L = 2048: single level, generic LDS kernel, y only, no gate table
     assert sm.spectre_mix_workspace_bytes(4, 8, 2048, 64, 0) == 4 * 4 * 2048 * 512
     # L = 256: single level, square kernel reading the gate itself (no table)
