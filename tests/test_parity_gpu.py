@@ -170,6 +170,32 @@ def test_column_kernel_shapes(B, L, H, D, dt, keep):
     check_full(w)
 
 
+def _column_sweep(n=10, seed=777):
+    """Seeded random shapes for the column kernel: L = 3072 or 4096, any even
+    H*D up to 512, B within one round (B * ceil(H*D/8) <= 256), both dtypes,
+    any keep_bins."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        L = int(rng.choice([3072, 4096]))
+        H, D = int(rng.integers(1, 9)), int(rng.integers(1, 65))
+        if (H * D) % 2:
+            continue
+        B = int(rng.integers(1, 5))
+        if B * ((H * D // 2 + 3) // 4) > 256:
+            continue
+        cases.append((B, L, H, D, int(rng.integers(0, 2)), int(rng.integers(0, L // 2 + 2))))
+    return cases
+
+
+@pytest.mark.parametrize("B,L,H,D,dt,keep", _column_sweep())
+def test_column_kernel_sweep(B, L, H, D, dt, keep):
+    import efficient_attention_fft_amd as sm
+    assert sm.spectre_mix_plan(L) == (sm.SPECTRE_OK, (1, 1, L))
+    w = workloads.custom(530 + L % 79, B=B, L=L, H=H, D=D, dtype=dt, keep_bins=keep, affine=True)
+    check_full(w)
+
+
 def test_both_plans_of_one_length_in_one_process():
     """L = 4096 in one round (column kernel), past it (four-step) and in one
     round again, in one process: each plan must get its own tables."""
