@@ -207,6 +207,20 @@ int cu_count(int dev, int* cus) {
   return SPECTRE_OK;
 }
 
+// Dynamic LDS above 64 KB needs the kernel's attribute raised, once per
+// (function, device); `done` holds one bit per device already set.
+int lds_attr(const void* fn, int bytes, uint64_t& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPECTRE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SPECTRE_EUNSUPPORTED;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done & bit) return SPECTRE_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return SPECTRE_EHIP;
+  done |= bit;
+  return SPECTRE_OK;
+}
+
 // ---------------------------------------------------------------- tracing
 //
 // Optional per-kernel HIP events: one before a traced call's first kernel,
@@ -620,13 +634,8 @@ int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
     const void* fn = uk == 5 ? reinterpret_cast<const void*>(&k_mid_dma<CG, 5>)
                    : uk == 9 ? reinterpret_cast<const void*>(&k_mid_dma<CG, 9>)
                              : reinterpret_cast<const void*>(&k_mid_dma<CG, 17>);
-    static bool dma_attr[3] = {false, false, false};  // guarded by g_mu
-    const int ai = uk == 5 ? 0 : uk == 9 ? 1 : 2;
-    if (!dma_attr[ai]) {
-      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        return SPECTRE_EHIP;
-      dma_attr[ai] = true;
-    }
+    static uint64_t dma_attr[3] = {0, 0, 0};  // guarded by g_mu
+    if (int rc = lds_attr(fn, 160 * 1024, dma_attr[uk == 5 ? 0 : uk == 9 ? 1 : 2])) return rc;
     MidParams q = p;
     q.gx = (int)grid.x;
     q.gy = (int)grid.y;
@@ -660,14 +669,10 @@ int launch_mid_sq_k(const MidParams& p, dim3 grid, hipStream_t st) {
     SPECTRE_LAUNCH_CHECK("B_mid_lds");
     return SPECTRE_OK;
   }
-  static bool attr_set[2] = {false, false};  // guarded by g_mu
+  static uint64_t attr_set[2] = {0, 0};  // guarded by g_mu
   const void* fn = gl ? reinterpret_cast<const void*>(&k_mid_sq<R, IN, true, CG>)
                       : reinterpret_cast<const void*>(&k_mid_sq<R, IN, false, CG>);
-  if (!attr_set[gl]) {
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return SPECTRE_EHIP;
-    attr_set[gl] = true;
-  }
+  if (int rc = lds_attr(fn, 160 * 1024, attr_set[gl])) return rc;
   if (gl)
     hipLaunchKernelGGL((k_mid_sq<R, IN, true, CG>), grid, dim3(R * ncols), lds, st, p);
   else
@@ -839,13 +844,10 @@ size_t local_bytes(const Shape& s, const Local* local) {
 template <int RA, int RB, int RC, int CPT, int IN>
 int launch_col_k(const ColParams& c, int64_t B, hipStream_t st) {
   using C = ColCfg<RA, RB, RC, CPT>;
-  static bool attr_set = false;  // guarded by g_mu
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_col<RA, RB, RC, CPT, IN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES) != hipSuccess)
-      return SPECTRE_EHIP;
-    attr_set = true;
-  }
+  static uint64_t attr_set = 0;  // guarded by g_mu
+  if (int rc = lds_attr(reinterpret_cast<const void*>(&k_col<RA, RB, RC, CPT, IN>), (int)C::LDS_BYTES,
+                        attr_set))
+    return rc;
   const int64_t items = (c.CP2 + CPT - 1) / CPT * B;
   if (items > INT32_MAX) return SPECTRE_EUNSUPPORTED;
   const dim3 grid((unsigned)items);
