@@ -1037,14 +1037,25 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
         __builtin_amdgcn_global_load_lds(g + q * 4096 + lane16, l + q * 4096, 16, 0, 2 /* nontemporal */);
     }
   };
+  // With a truncation bound (UK < 17) the tensor loop is unrolled: each
+  // tensor's product is then straight-line code and the loop's register
+  // copies go, but the registers only suffice when the next item's gate
+  // values are loaded during the last tensor, through 32-bit offsets from
+  // the head's table.  Without a bound the unrolled loop needs more than
+  // 256 VGPRs, so it stays rolled.
+  constexpr bool kUnrolled = UK < 17;
   auto gate_load = [&](int3 blk, int2 cols, float* gv) __attribute__((always_inline)) {
     const int hw = (2 * blk.y * 4) / p.D;  // the item's head
+    const float* gb = p.gtab + (int64_t)hw * p.ncol * N;
 #pragma unroll
     for (int r = 0; r < NGR; ++r) {
       const int e = min(tid + NT * r, NGL - 1);
       const int sl = e / ((H2 + 1) * R), u = (e / R) % (H2 + 1), kk = e % R;
       const int c = sl == 0 ? cols.x : cols.y;
-      gv[r] = p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u];
+      if constexpr (kUnrolled)
+        gv[r] = gb[(uint32_t)((c >= 0 ? c : 0) * N + kk + R * u)];
+      else
+        gv[r] = p.gtab[((int64_t)hw * p.ncol + (c >= 0 ? c : 0)) * N + kk + R * u];
     }
   };
 
@@ -1093,7 +1104,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     const bool special = a_zero && k1 == 0;
     const int colid1 = s1 == 0 ? cols.x : cols.y;  // every workgroup holds two columns
 
-#pragma unroll 1
+#pragma unroll (kUnrolled ? 3 : 1)
     for (int x = 0; x < 3; ++x) {
       int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
       asm volatile("" : "+v"(t1o));
@@ -1110,7 +1121,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
       // waits for it), then its gate values, both used at the end of the item
       if (x == 0) ncols_v = p.wgcols[nblk.x];
       if constexpr (!CG) {
-        if (x == 1) gate_load(nblk, ncols_v, gv);
+        if (x == (kUnrolled ? 2 : 1)) gate_load(nblk, ncols_v, gv);
       }
       __syncthreads();  // the blocks are read before the transpose overwrites them
       // ---- stage 1: DFT over i of x[t + R i], twiddle w_N^{t k}
