@@ -1044,6 +1044,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
   // the head's table.  Without a bound the unrolled loop needs more than
   // 256 VGPRs, so it stays rolled.
   constexpr bool kUnrolled = UK < 17;
+  constexpr int kTensorUnroll = kUnrolled ? 3 : 1;
   auto gate_load = [&](int3 blk, int2 cols, float* gv) __attribute__((always_inline)) {
     const int hw = (2 * blk.y * 4) / p.D;  // the item's head
     const float* gb = p.gtab + (int64_t)hw * p.ncol * N;
@@ -1104,7 +1105,7 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     const bool special = a_zero && k1 == 0;
     const int colid1 = s1 == 0 ? cols.x : cols.y;  // every workgroup holds two columns
 
-#pragma unroll (kUnrolled ? 3 : 1)
+#pragma unroll kTensorUnroll
     for (int x = 0; x < 3; ++x) {
       int t1o = t1;  // opaque: the 31 twiddle addresses are recomputed per tensor
       asm volatile("" : "+v"(t1o));
