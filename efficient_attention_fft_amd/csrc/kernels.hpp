@@ -987,7 +987,10 @@ __global__ __launch_bounds__(256, 2) void k_mid_sq(MidParams p) {
 //  - a workgroup takes several work items: w, w + gridDim.x, ... (with the
 //    grid a multiple of 8 an item's XCD is its index mod 8, as for one item
 //    per workgroup), and the next item's q copy runs under this item's last
-//    inverse DFT and its stores.
+//    inverse DFT and its stores;
+//  - the copies are issued at raised wave priority (s_setprio), so that the
+//    other workgroup's wave on the SIMD, busy with its transforms, does not
+//    hold them back.
 // The asynchronous copies write LDS, and the compiler knows that much: before
 // the first LDS read after a copy it waits for every outstanding vector
 // memory operation (vmcnt(0)), which at the top of an item also retires the
@@ -1137,7 +1140,12 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
       for (int t = 0; t < R; ++t) v[t] = lds[k1 * ROW + t * 8 + col2];
       if (x < 2) {
         __syncthreads();  // the transpose buffer is free: fetch the next tensor
+        // issued at raised priority: the SIMD's other wave (the other
+        // workgroup) is then in its arithmetic and would otherwise delay
+        // these issues, and with them the copy the next tensor waits for
+        __builtin_amdgcn_s_setprio(3);
         copy_block(p.in[x + 1], blk, cols);
+        __builtin_amdgcn_s_setprio(0);
       }
       dft<R, -1>(v);
       if (p.dc != nullptr && special)  // bin 0 of column (0, 0)
@@ -1250,7 +1258,9 @@ __global__ __launch_bounds__(256, 2) void k_mid_dma(MidParams p) {
     asm volatile("" : "+v"(ncols_v));
     const int2 ncols = make_int2(__builtin_amdgcn_readfirstlane(ncols_v.x), __builtin_amdgcn_readfirstlane(ncols_v.y));
     __syncthreads();  // the transpose buffer is free: fetch the next item's q
+    __builtin_amdgcn_s_setprio(3);
     if (more) copy_block(p.in[0], nblk, ncols);
+    __builtin_amdgcn_s_setprio(0);
     dft<R, +1>(v);
     // U in row layout: element i of this lane is token row m3 = t1 + R i
     const int cp1 = blk.y * 4 + j1;
@@ -1733,8 +1743,10 @@ __global__ __launch_bounds__(512, 4) void k_final_split(FinalParams p) {
   {
     const float2* u = p.U + ((b * R + h) * p.M + m) * p.CP2 + cp;
     const int64_t rs = 2 * p.M * p.CP2;  // rows 2a + h
+    __builtin_amdgcn_s_setprio(3);  // the loads ahead of other waves' arithmetic
 #pragma unroll
     for (int a = 0; a < R2; ++a) z[a] = load_nt(u + a * rs);
+    __builtin_amdgcn_s_setprio(0);
   }
   dft<R2, +1>(z);
   join_swap<R, +1>(z, h);
