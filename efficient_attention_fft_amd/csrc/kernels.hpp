@@ -1443,11 +1443,13 @@ void k_col(ColParams p) {
   float2 nxt[C::RA];
   auto load_rows = [&](const void* src) __attribute__((always_inline)) {
     const char* ub = static_cast<const char*>(src) + gbase * pair_bytes<IN>();
+    __builtin_amdgcn_s_setprio(3);  // ahead of other waves' transforms (about 1 us at 4096)
 #pragma unroll
     for (int j = 0; j < C::RA; ++j) {
       const float2 r = load_pair_c<IN>(ub + (size_t)j * C::TA * rowb, loff_a);
       nxt[j] = want_a ? r : make_float2(0.f, 0.f);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   load_rows(p.in[0]);
 
@@ -1528,8 +1530,10 @@ void k_col(ColParams p) {
   const bool addx = p.x != nullptr;
   if (addx) {
     const char* xb = static_cast<const char*>(p.x) + gbase * pair_bytes<IN>();
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int i = 0; i < RC; ++i) xr[i] = load_pair_c<IN>(xb + (size_t)i * C::TC * rowb, loff_c);
+    __builtin_amdgcn_s_setprio(0);
   }
   col_fft<C, +1>(v, col, t, cconj(wa), cconj(wb));
   if (t < C::TC && live) {
